@@ -1,0 +1,208 @@
+"""CPU oracle of one sparse-MoE SwiGLU layer forward pass (ctypes over oracle.c).
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+and its Python binding never import it and share no code with it.
+
+Parity pins of each function (what ties it to something other than itself)
+are in ``tests/test_oracle_*.py``:
+  route   -- exact rational logits on grid inputs, numpy stable argsort,
+             softmax-over-all-then-renormalise, sum-to-one, k=1, shift invariance
+  experts -- float64 dense evaluation of every expert on every token, a
+             textbook dense SwiGLU FFN at E=1, identical experts, k=E soft
+             mixture, relabelling, token independence, exact power-of-two scaling,
+             hand-computed closed-form fixtures under tests/golden/
+  align   -- Python ``sorted`` of (expert, assignment) pairs and the padding
+             invariants
+Absolute layer outputs at the named workloads have no printed values on the
+pages; beyond the pins above they are "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+_lock = threading.Lock()
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc -O2 -fopenmp (no BLAS, no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-fno-fast-math",
+           "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            lib.oracle_route.restype = ctypes.c_int
+            lib.oracle_route.argtypes = [_p, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p, _p]
+            lib.oracle_experts.restype = ctypes.c_int
+            lib.oracle_experts.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p,
+                                           _p, _i64, _p, _p]
+            lib.oracle_forward.restype = ctypes.c_int
+            lib.oracle_forward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i32,
+                                           _i32, _p, _p, _p, _p]
+            lib.oracle_align.restype = ctypes.c_int
+            lib.oracle_align.argtypes = [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
+                                         _i64, _p, _p]
+            lib.oracle_num_threads.restype = ctypes.c_int
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+            _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
+
+
+def _bf16_ptr(t):
+    """Pointer to a contiguous CPU bf16 tensor (or None). Keeps no copy."""
+    if t is None:
+        return None, None
+    if t.device.type != "cpu" or t.dtype != torch.bfloat16:
+        raise TypeError("oracle takes CPU bfloat16 tensors")
+    t = t.contiguous()
+    return t.data_ptr(), t
+
+
+def _f32_ptr(t):
+    if t is None:
+        return None, None
+    t = t.detach().to("cpu", torch.float32).contiguous()
+    return t.data_ptr(), t
+
+
+def route(x, w_g, router_bias, k: int):
+    """Router for every row of x.
+
+    Returns (ids int32 [T,k], p float64 [T,k], margin float64 [T], logits float32 [T,E]).
+    """
+    lib = _load()
+    T, D = x.shape
+    E = w_g.shape[0]
+    px, kx = _bf16_ptr(x)
+    pw, kw = _bf16_ptr(w_g)
+    pb, kb = _f32_ptr(router_bias)
+    logits = np.empty((T, E), np.float32)
+    ids = np.empty((T, k), np.int32)
+    p = np.empty((T, k), np.float64)
+    margin = np.empty((T,), np.float64)
+    rc = lib.oracle_route(px, pw, pb, T, D, E, k, logits.ctypes.data, ids.ctypes.data,
+                          p.ctypes.data, margin.ctypes.data)
+    if rc:
+        raise ValueError("oracle_route failed: %d" % rc)
+    return ids, p, margin, logits
+
+
+def experts(inp, ids, p, tokens=None, count_macs: bool = False):
+    """Expert outputs y [n, D] (float64) for ``tokens`` (default: all rows of x)
+    under the routing (ids [T,k] int, p [T,k] float)."""
+    lib = _load()
+    s = inp.shape
+    px, kx = _bf16_ptr(inp.x)
+    pgu, k1 = _bf16_ptr(inp.w_gate_up)
+    pdn, k2 = _bf16_ptr(inp.w_down)
+    psgu, k3 = _bf16_ptr(inp.ws_gate_up)
+    psdn, k4 = _bf16_ptr(inp.ws_down)
+    ids = np.ascontiguousarray(ids, np.int32)
+    p = np.ascontiguousarray(p, np.float64)
+    T = inp.x.shape[0]
+    if ids.shape != (T, s.k) or p.shape != (T, s.k):
+        raise ValueError("routing shape mismatch")
+    if tokens is None:
+        tok = None
+        n = T
+    else:
+        tok = np.ascontiguousarray(tokens, np.int64)
+        if tok.size and (tok.min() < 0 or tok.max() >= T):
+            raise ValueError("token index out of range")
+        n = tok.size
+    y = np.empty((n, s.D), np.float64)
+    macs = ctypes.c_int64(0)
+    rc = lib.oracle_experts(px, pgu, pdn, psgu, psdn, s.D, s.E, s.F, s.k, s.Fs, ids.ctypes.data,
+                            p.ctypes.data, None if tok is None else tok.ctypes.data, n,
+                            y.ctypes.data, ctypes.byref(macs))
+    if rc:
+        raise ValueError("oracle_experts failed: %d" % rc)
+    return (y, macs.value) if count_macs else y
+
+
+def forward(inp):
+    """Whole layer for every token: returns (y float64 [T,D], ids, p, margin)."""
+    lib = _load()
+    s = inp.shape
+    T = inp.x.shape[0]
+    px, kx = _bf16_ptr(inp.x)
+    pg, kg = _bf16_ptr(inp.w_g)
+    pb, kb = _f32_ptr(inp.router_bias)
+    pgu, k1 = _bf16_ptr(inp.w_gate_up)
+    pdn, k2 = _bf16_ptr(inp.w_down)
+    psgu, k3 = _bf16_ptr(inp.ws_gate_up)
+    psdn, k4 = _bf16_ptr(inp.ws_down)
+    ids = np.empty((T, s.k), np.int32)
+    p = np.empty((T, s.k), np.float64)
+    margin = np.empty((T,), np.float64)
+    y = np.empty((T, s.D), np.float64)
+    rc = lib.oracle_forward(px, pg, pb, pgu, pdn, psgu, psdn, T, s.D, s.E, s.F, s.k, s.Fs,
+                            ids.ctypes.data, p.ctypes.data, margin.ctypes.data, y.ctypes.data)
+    if rc:
+        raise ValueError("oracle_forward failed: %d" % rc)
+    return y, ids, p, margin
+
+
+def align(ids, E: int, block_m: int, shared: bool = False):
+    """Group assignments by expert (stable in assignment order) with BM-padded groups.
+
+    Returns a dict of int32 arrays: counts, offsets, padded, sorted_assign,
+    row_of, row_token (length padded[G]), tile_group (length n_tiles), n_tiles.
+    """
+    lib = _load()
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, k = ids.shape
+    G = E + (1 if shared else 0)
+    cap = T * k + G * (block_m - 1) + (T if shared else 0)
+    counts = np.zeros(G, np.int32)
+    offsets = np.zeros(G + 1, np.int32)
+    padded = np.zeros(G + 1, np.int32)
+    sorted_assign = np.zeros(T * k, np.int32)
+    row_of = np.zeros(T * k, np.int32)
+    row_token = np.zeros(max(cap, 1), np.int32)
+    tile_group = np.zeros(max(cap // block_m + 1, 1), np.int32)
+    n_tiles = ctypes.c_int32(0)
+    rc = lib.oracle_align(ids.ctypes.data, T, k, E, block_m, 1 if shared else 0,
+                          counts.ctypes.data, offsets.ctypes.data, padded.ctypes.data,
+                          sorted_assign.ctypes.data, row_of.ctypes.data, row_token.ctypes.data,
+                          cap, tile_group.ctypes.data, ctypes.byref(n_tiles))
+    if rc:
+        raise ValueError("oracle_align failed: %d" % rc)
+    nt = n_tiles.value
+    return dict(counts=counts, offsets=offsets, padded=padded, sorted_assign=sorted_assign,
+                row_of=row_of, row_token=row_token[:padded[G]].copy(),
+                tile_group=tile_group[:nt].copy(), n_tiles=nt)

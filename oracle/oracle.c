@@ -1,0 +1,289 @@
+/*
+ * CPU oracle for the forward pass of one sparse Mixture-of-Experts SwiGLU
+ * feed-forward layer.
+ *
+ * TEST INFRASTRUCTURE.  Only the test-suite, the package smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The GPU path never calls
+ * it, links it or shares any code with it.
+ *
+ * What it computes (sources are the pages' titles and sections):
+ *  - Router: "Mixture of experts: por que un modelo enorme apenas usa sus
+ *    parametros" (josueisai), section "El router: la pieza que de verdad
+ *    decide": a linear projection gives one score per expert, the k best are
+ *    kept, and a softmax normalises only among the chosen ones.  The glossary
+ *    "MoE (Mixture of Experts - Mezcla de Expertos)" (gotburnout), section 2
+ *    diagram, writes the same as p = Softmax(TopK(W_g x)).
+ *  - Experts: the glossary's section 3 pipeline, step 3: each chosen expert
+ *    is a SwiGLU FFN.  Step 4 / diagram row 4: y = sum_i p_i * Expert_i(x).
+ *  - Shared expert: glossary section 2, item 3 and diagram row 3: always
+ *    active; added with coefficient 1 (it takes no router weight).
+ *  - Packed layout: "Transformers v5 El Secreto Detras de los Modelos MoE Mas
+ *    Rapidos" (smart-guide), section "La Solucion: WeightConverter": experts
+ *    stacked on dim 0, the two input projections concatenated on dim 1, so one
+ *    expert's gate_up block is [2F, D], first-listed projection first.
+ *
+ * Readings taken where the pages leave a step open:
+ *  - The activated (SiLU) half is rows 0..F-1 of an expert's gate_up block;
+ *    rows F..2F-1 multiply it elementwise.
+ *  - The router's top-k decision is taken on fp32 logits (the precision the
+ *    router's logits are defined in); ties go to the lower expert index; the
+ *    chosen slots are ordered by descending logit.
+ *  - No residual, no normalisation, no capacity limit: every token is
+ *    computed by all of its k experts.
+ *
+ * Precision: bf16 inputs are widened exactly; every sum is accumulated in
+ * double, in ascending index order; exp is the C library's double exp.  The
+ * router logits are rounded once to fp32 before the selection.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static inline double bf(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* ------------------------------------------------------------------ router */
+
+/* Logits of one token: l[e] = fp32( sum_d x[d] * W_g[e,d] + b[e] ). */
+static void token_logits(const uint16_t* xt, const uint16_t* w_g, const float* bias,
+                         int32_t D, int32_t E, float* l) {
+  for (int32_t e = 0; e < E; ++e) {
+    const uint16_t* w = w_g + (int64_t)e * D;
+    double s = 0.0;
+    for (int32_t d = 0; d < D; ++d) s += bf(xt[d]) * bf(w[d]);
+    if (bias) s += (double)bias[e];
+    l[e] = (float)s;
+  }
+}
+
+/* Top-k by (logit descending, index ascending), then softmax over the chosen.
+ * margin = l_(k) - l_(k+1) with 1-based order statistics (+inf when k == E). */
+static void token_topk_softmax(const float* l, int32_t E, int32_t k, unsigned char* taken,
+                               int32_t* ids, double* p, double* margin) {
+  memset(taken, 0, (size_t)E);
+  for (int32_t j = 0; j < k; ++j) {
+    int32_t best = -1;
+    for (int32_t e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || l[e] > l[best]) best = e; /* strict: the lower index wins ties */
+    }
+    taken[best] = 1;
+    ids[j] = best;
+  }
+  if (margin) {
+    if (k == E) {
+      *margin = INFINITY;
+    } else {
+      int32_t next = -1;
+      for (int32_t e = 0; e < E; ++e)
+        if (!taken[e] && (next < 0 || l[e] > l[next])) next = e;
+      *margin = (double)l[ids[k - 1]] - (double)l[next];
+    }
+  }
+  double m = (double)l[ids[0]];
+  double s[256];
+  double tot = 0.0;
+  for (int32_t j = 0; j < k; ++j) {
+    s[j] = exp((double)l[ids[j]] - m);
+    tot += s[j];
+  }
+  for (int32_t j = 0; j < k; ++j) p[j] = s[j] / tot;
+}
+
+/*
+ * Route T tokens.
+ *   x [T,D] bf16, w_g [E,D] bf16, bias [E] fp32 or NULL
+ *   logits [T,E] fp32 out or NULL; ids [T,k] out; p [T,k] out; margin [T] out or NULL
+ * Returns 0, or -1 on an invalid size.
+ */
+int oracle_route(const uint16_t* x, const uint16_t* w_g, const float* bias, int64_t T, int32_t D,
+                 int32_t E, int32_t k, float* logits, int32_t* ids, double* p, double* margin) {
+  if (T < 0 || D <= 0 || E <= 0 || E > 256 || k <= 0 || k > E) return -1;
+  int err = 0;
+#pragma omp parallel
+  {
+    float* l = (float*)malloc(sizeof(float) * (size_t)E);
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    if (!l || !taken) {
+#pragma omp atomic write
+      err = -2;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t t = 0; t < T; ++t) {
+        token_logits(x + t * D, w_g, bias, D, E, l);
+        if (logits) memcpy(logits + t * E, l, sizeof(float) * (size_t)E);
+        token_topk_softmax(l, E, k, taken, ids + t * k, p + t * k, margin ? margin + t : NULL);
+      }
+    }
+    free(l);
+    free(taken);
+  }
+  return err;
+}
+
+/* ----------------------------------------------------------------- experts */
+
+/* yt[o] += coef * sum_f W_down[o,f] * h[f],  h[f] = SiLU(g_f) * u_f,
+ * g_f = W_gu[f,:] . x,  u_f = W_gu[F+f,:] . x,  SiLU(g) = g / (1 + exp(-g)). */
+static void swiglu_accumulate(const uint16_t* w_gu, const uint16_t* w_dn, int32_t F, int32_t D,
+                              const double* xd, double* h, double coef, double* yt, int64_t* macs) {
+  for (int32_t f = 0; f < F; ++f) {
+    const uint16_t* wg = w_gu + (int64_t)f * D;
+    const uint16_t* wu = w_gu + (int64_t)(F + f) * D;
+    double g = 0.0, u = 0.0;
+    for (int32_t d = 0; d < D; ++d) g += bf(wg[d]) * xd[d];
+    for (int32_t d = 0; d < D; ++d) u += bf(wu[d]) * xd[d];
+    *macs += 2 * (int64_t)D;
+    h[f] = g / (1.0 + exp(-g)) * u;
+  }
+  for (int32_t o = 0; o < D; ++o) {
+    const uint16_t* wd = w_dn + (int64_t)o * F;
+    double s = 0.0;
+    for (int32_t f = 0; f < F; ++f) s += bf(wd[f]) * h[f];
+    *macs += F;
+    yt[o] += coef * s;
+  }
+}
+
+/*
+ * Expert outputs for n_tokens tokens given their routing.
+ *   x [T,D] bf16 (rows picked by tokens[], or rows 0..n_tokens-1 when tokens is NULL)
+ *   w_gate_up [E,2F,D], w_down [E,D,F] bf16; ws_gate_up [2Fs,D], ws_down [D,Fs] bf16 or NULL
+ *   ids [*,k], p [*,k]: the routing rows of the same tokens (indexed by token id)
+ *   y [n_tokens, D] double out; macs: total multiply-adds performed (may be NULL)
+ * Slots are accumulated in order j = 0..k-1, the shared expert last.
+ */
+int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
+                   const uint16_t* ws_gate_up, const uint16_t* ws_down, int32_t D, int32_t E,
+                   int32_t F, int32_t k, int32_t Fs, const int32_t* ids, const double* p,
+                   const int64_t* tokens, int64_t n_tokens, double* y, int64_t* macs) {
+  if (D <= 0 || E <= 0 || F <= 0 || k <= 0 || k > E || Fs < 0 || n_tokens < 0) return -1;
+  if (Fs > 0 && (!ws_gate_up || !ws_down)) return -1;
+  int err = 0;
+  int64_t total = 0;
+  int32_t hmax = F > Fs ? F : Fs;
+#pragma omp parallel reduction(+ : total)
+  {
+    double* xd = (double*)malloc(sizeof(double) * (size_t)D);
+    double* h = (double*)malloc(sizeof(double) * (size_t)hmax);
+    if (!xd || !h) {
+#pragma omp atomic write
+      err = -2;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t i = 0; i < n_tokens; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        const uint16_t* xt = x + t * D;
+        double* yt = y + i * D;
+        for (int32_t d = 0; d < D; ++d) xd[d] = bf(xt[d]);
+        for (int32_t d = 0; d < D; ++d) yt[d] = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+          int32_t e = ids[t * k + j];
+          if (e < 0 || e >= E) continue; /* never produced by the router */
+          swiglu_accumulate(w_gate_up + (int64_t)e * 2 * F * D, w_down + (int64_t)e * D * F, F, D,
+                            xd, h, p[t * k + j], yt, &total);
+        }
+        if (Fs > 0) swiglu_accumulate(ws_gate_up, ws_down, Fs, D, xd, h, 1.0, yt, &total);
+      }
+    }
+    free(xd);
+    free(h);
+  }
+  if (macs) *macs = total;
+  return err;
+}
+
+/*
+ * Whole layer for T tokens: route every token, then run its experts.
+ * ids/p/margin outputs as in oracle_route; y [T,D] double.
+ */
+int oracle_forward(const uint16_t* x, const uint16_t* w_g, const float* bias,
+                   const uint16_t* w_gate_up, const uint16_t* w_down, const uint16_t* ws_gate_up,
+                   const uint16_t* ws_down, int64_t T, int32_t D, int32_t E, int32_t F, int32_t k,
+                   int32_t Fs, int32_t* ids, double* p, double* margin, double* y) {
+  int rc = oracle_route(x, w_g, bias, T, D, E, k, NULL, ids, p, margin);
+  if (rc) return rc;
+  return oracle_experts(x, w_gate_up, w_down, ws_gate_up, ws_down, D, E, F, k, Fs, ids, p, NULL, T,
+                        y, NULL);
+}
+
+/* ------------------------------------------------------------------- align */
+
+/*
+ * Group the T*k assignments a = t*k + j by expert, for a given routing.
+ * G = E groups (+1 shared group holding every token in order when shared != 0).
+ *   counts[g]        number of rows of group g
+ *   offsets[g]       exclusive prefix sum of counts            [G+1]
+ *   padded[g]        exclusive prefix sum of ceil(count/BM)*BM [G+1]
+ *   sorted_assign[i] the assignments in ascending (expert, a) order [T*k]
+ *   row_of[a]        padded row of assignment a                 [T*k]
+ *   row_token[r]     token of padded row r, -1 on padding rows  [padded[G]] (cap entries)
+ *   tile_group[i]    group of BM-row tile i                     [padded[G]/BM]
+ *   n_tiles          padded[G]/BM
+ * Returns 0, -1 on invalid sizes or ids, -3 if cap is too small.
+ */
+int oracle_align(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t BM, int32_t shared,
+                 int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
+                 int32_t* row_of, int32_t* row_token, int64_t cap, int32_t* tile_group,
+                 int32_t* n_tiles) {
+  if (T < 0 || k <= 0 || E <= 0 || BM <= 0) return -1;
+  int32_t G = E + (shared ? 1 : 0);
+  int64_t A = T * k;
+  for (int32_t g = 0; g < G; ++g) counts[g] = 0;
+  for (int64_t a = 0; a < A; ++a) {
+    if (ids[a] < 0 || ids[a] >= E) return -1;
+    counts[ids[a]]++;
+  }
+  if (shared) counts[E] = (int32_t)T;
+  offsets[0] = 0;
+  padded[0] = 0;
+  for (int32_t g = 0; g < G; ++g) {
+    offsets[g + 1] = offsets[g] + counts[g];
+    padded[g + 1] = padded[g] + (counts[g] + BM - 1) / BM * BM;
+  }
+  if ((int64_t)padded[G] > cap) return -3;
+  /* stable counting sort: scanning a upwards keeps ascending a inside each expert */
+  int32_t* cursor = (int32_t*)calloc((size_t)G, sizeof(int32_t));
+  if (!cursor) return -2;
+  for (int64_t r = 0; r < padded[G]; ++r) row_token[r] = -1;
+  for (int64_t a = 0; a < A; ++a) {
+    int32_t e = ids[a];
+    int32_t i = offsets[e] + cursor[e];
+    int32_t r = padded[e] + cursor[e];
+    cursor[e]++;
+    sorted_assign[i] = (int32_t)a;
+    row_of[a] = r;
+    row_token[r] = (int32_t)(a / k);
+  }
+  if (shared)
+    for (int64_t t = 0; t < T; ++t) row_token[padded[E] + t] = (int32_t)t;
+  free(cursor);
+  for (int32_t g = 0; g < G; ++g)
+    for (int32_t i = padded[g] / BM; i < padded[g + 1] / BM; ++i) tile_group[i] = g;
+  *n_tiles = padded[G] / BM;
+  return 0;
+}

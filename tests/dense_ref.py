@@ -1,0 +1,61 @@
+"""Dense float64 evaluation of the MoE layer, for tiny inputs only.
+
+An independent check of the oracle: it is vectorised instead of looping, runs
+every expert on every token (E times the needed work) and zeroes the
+unselected ones through a dense gate matrix, as the glossary "MoE (Mixture of
+Experts - Mezcla de Expertos)", section 3 step 2, describes the unselected
+scores being cancelled.  Library routines stand in for the hand-written loops:
+numpy matmul for every contraction, a stable numpy argsort for the top-k,
+scipy's softmax and expit for the normalisation and the SiLU.
+"""
+import numpy as np
+import scipy.special as sps
+import torch
+
+
+def f64(t):
+    return None if t is None else t.to(torch.float64).numpy()
+
+
+def dense_logits(inp):
+    X = f64(inp.x)
+    l = X @ f64(inp.w_g).T
+    if inp.router_bias is not None:
+        l = l + inp.router_bias.to(torch.float64).numpy()[None, :]
+    # the selection is defined on fp32 logits
+    return l.astype(np.float32).astype(np.float64)
+
+
+def dense_routing(inp):
+    l = dense_logits(inp)
+    k = inp.shape.k
+    ids = np.argsort(-l, axis=1, kind="stable")[:, :k]
+    chosen = np.take_along_axis(l, ids, axis=1)
+    p = sps.softmax(chosen, axis=1)
+    return ids, p, l
+
+
+def swiglu_ffn(X, w_gu, w_dn):
+    """Textbook SwiGLU FFN: W_down (SiLU(W_a x) * (W_b x)), W_a = first half."""
+    F = w_gu.shape[0] // 2
+    g = X @ w_gu[:F].T
+    u = X @ w_gu[F:].T
+    h = g * sps.expit(g) * u
+    return h @ w_dn.T
+
+
+def dense_forward(inp):
+    s = inp.shape
+    ids, p, _ = dense_routing(inp)
+    X = f64(inp.x)
+    T = X.shape[0]
+    G = np.zeros((T, s.E))
+    np.put_along_axis(G, ids, p, axis=1)
+    Wgu = f64(inp.w_gate_up)
+    Wd = f64(inp.w_down)
+    Y = np.zeros((T, s.D))
+    for e in range(s.E):
+        Y += G[:, e:e + 1] * swiglu_ffn(X, Wgu[e], Wd[e])
+    if s.Fs:
+        Y += swiglu_ffn(X, f64(inp.ws_gate_up), f64(inp.ws_down))
+    return Y, ids, p
