@@ -1,0 +1,207 @@
+"""Benchmark of one sparse-MoE SwiGLU layer forward pass on one MI355X.
+
+A step is one full ``moe_forward`` call (router, grouping, gate/up GEMM with
+SwiGLU, down GEMM, combine) over one batch of synthetic tokens already resident
+in HBM.  Default workload: the Mixtral-8x7B-shaped prefill layer
+(T=4096, D=4096, E=8, top-2, d_ff=14336).  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; % bf16 MFMA peak (prefill), % HBM BW (decode)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNELS = ("moe_router", "moe_align", "moe_gemm_gate_up", "moe_gemm_down", "moe_combine")
+LLC_BYTES = 256 << 20       # MI355X Infinity Cache
+
+
+def _log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def _traffic_from_profile(workload, kernel_src):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    PMC summary, or None when there is none or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_%s_pmc.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b:
+        return None
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def _cpu_baseline(inp, target_s):
+    """The CPU oracle (router + experts per token) on the first n tokens."""
+    import oracle
+    import workloads as W
+
+    s = inp.shape
+
+    def run(n):
+        sub = W.LayerInputs(s.with_T(n), inp.x[:n].contiguous(), inp.w_g, inp.w_gate_up, inp.w_down,
+                            inp.router_bias, inp.ws_gate_up, inp.ws_down)
+        t0 = time.perf_counter()
+        oracle.forward(sub)
+        return time.perf_counter() - t0
+
+    cores = oracle.num_threads()
+    n0 = max(1, min(s.T, cores))
+    t_cal = run(n0)
+    n = int(max(n0, min(s.T, n0 * target_s / max(t_cal, 1e-6))))
+    t = run(n) if n != n0 else t_cal
+    return {"value": n / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d of %d tokens of the %s workload, router + top-%d experts%s per token, "
+                      "%.1f s wall" % (n, s.T, "same", s.k, " + shared expert" if s.Fs else "", t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--T", type=int, default=None, help="token count override (decode sweeps)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from sparse_mixture_experts_prefix_amd import build as native
+
+    if not os.path.exists(native.LIB_PATH):
+        native.build()
+    import sparse_mixture_experts_prefix_amd as moe
+
+    moe.load_library()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+
+    wl = W.WORKLOADS[args.workload]
+    s = wl.shape if args.T is None else wl.shape.with_T(args.T)
+    _log("generating %s T=%d inputs" % (wl.name, s.T))
+    inp = W.make_inputs(s, seed=0)
+    g = inp.to(dev)
+    # Rotate over weight copies when one copy would sit in the Infinity Cache.
+    wbytes = inp.w_gate_up.numel() * 2 + inp.w_down.numel() * 2
+    n_copies = 1 if wbytes > 4 * LLC_BYTES else 4
+    sets = [g]
+    for _ in range(n_copies - 1):
+        sets.append(W.LayerInputs(s, g.x, g.w_g, g.w_gate_up.clone(), g.w_down.clone(), g.router_bias,
+                                  None if g.ws_gate_up is None else g.ws_gate_up.clone(),
+                                  None if g.ws_down is None else g.ws_down.clone()))
+    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias)
+    ws = moe.alloc_workspace(shape, dev)
+    y = torch.empty((s.T, s.D), dtype=torch.float32, device=dev)
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+
+    def step(i):
+        q = sets[i % len(sets)]
+        moe.moe_forward(q.x, q.w_g, q.w_gate_up, q.w_down, s.k, q.router_bias, q.ws_gate_up,
+                        q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    _log("timed %d steps: %.3f ms/step" % (args.steps, ms_per_step))
+
+    # Per-kernel durations from HIP events recorded on the launch stream.
+    ev = [moe.HipEvents(6) for _ in range(args.steps)]
+    for i in range(args.steps):
+        q = sets[i % len(sets)]
+        moe.moe_forward_timed(ev[i], q.x, q.w_g, q.w_gate_up, q.w_down, s.k, q.router_bias,
+                              q.ws_gate_up, q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws)
+    torch.cuda.synchronize()
+    per_kernel = {name: float(np.mean([e.elapsed_ms(j, j + 1) for e in ev]))
+                  for j, name in enumerate(KERNELS)}
+    for e in ev:
+        e.close()
+
+    loads = np.bincount(ids.cpu().numpy().ravel(), minlength=s.E)
+    touched = int((loads > 0).sum())
+    flops = W.algorithmic_flops(s)
+    nbytes = W.algorithmic_bytes(s, touched)
+    t_ideal = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+    layer_bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9) else "hbm"
+
+    gu_ms = per_kernel["moe_gemm_gate_up"]
+    kernel_src = os.path.join(ROOT, "sparse_mixture_experts_prefix_amd", "csrc", "gemm.hip")
+    traffic = _traffic_from_profile(wl.name, kernel_src)
+    if layer_bound == "mfma":
+        achieved = W.gate_up_flops(s) / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        # expert weights of the gate/up half actually touched + gathered x
+        gu_bytes = touched * 2 * s.F * s.D * 2 + 2 * s.Fs * s.D * 2 + s.T * s.D * 2
+        achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = "moe_gemm_gate_up"
+    roof["kernel_ms"] = round(gu_ms, 4)
+    roof["traffic"] = traffic
+
+    out = {
+        "metric": METRIC,
+        "value": round(s.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based normal draws: x ~ N(0,1), weights ~ N(0,0.02), bf16)",
+        "config": {"workload": wl.name, "T": s.T, "D": s.D, "E": s.E, "k": s.k, "d_ff": s.F,
+                   "shared_d_ff": s.Fs, "router_bias": bool(s.router_bias),
+                   "weight_copies_rotated": n_copies},
+        "roofline": roof,
+        "layer": {"bound": layer_bound, "algorithmic_tflop": round(flops / 1e12, 4),
+                  "algorithmic_gb": round(nbytes / 1e9, 4), "ideal_ms": round(t_ideal * 1e3, 4),
+                  "frac": round(t_ideal * 1e3 / ms_per_step, 4),
+                  "tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+                  "touched_experts": touched, "max_expert_rows": int(loads.max())},
+        "kernel_ms": {k_: round(v, 4) for k_, v in per_kernel.items()},
+    }
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
+        out["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"]["sample"] = out["cpu_baseline"]["sample"].replace("same", wl.name)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts SwiGLU
+ * feed-forward layer, forward pass.
+ *
+ * The layer (pages cited by title and section):
+ *  - Router: "Mixture of experts: por qué un modelo enorme apenas usa sus
+ *    parámetros", section "El router: la pieza que de verdad decide", and the
+ *    glossary "MoE (Mixture of Experts - Mezcla de Expertos)", section 2
+ *    diagram row 2: p = Softmax(TopK(W_g x)).  Each token keeps its k highest
+ *    router scores; the softmax runs over those k only.
+ *  - Experts: glossary section 3, step 3: every chosen expert is a SwiGLU FFN,
+ *    h = SiLU(W_a x) * (W_b x), out = W_down h.
+ *  - Combine: glossary section 3 step 4 and diagram row 4:
+ *    y = sum_i p_i * Expert_i(x).  The residual of that row is the caller's.
+ *  - Shared expert: glossary section 2, item 3: always active, weight 1.
+ *  - Dispatch/regroup: "Mixture of Experts optimiza Transformers y LLMs",
+ *    section "Ejecución eficiente: backends de expertos": tokens are sent to
+ *    the chosen experts' weights, grouped by expert id, and the weighted
+ *    results are returned in the original token order.
+ *  - Packed weights: "Transformers v5 El Secreto Detrás de los Modelos MoE
+ *    Más Rápidos", section "La Solución: WeightConverter": experts stacked on
+ *    dim 0 and the two input projections concatenated on dim 1.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are row-major and contiguous; "bf16" is IEEE bfloat16 stored as
+ *    16-bit words.  Device pointers are HIP device (or managed) memory on the
+ *    current device and must be 16-byte aligned.
+ *  - x         bf16 [T, D]
+ *  - w_g       bf16 [E, D]        router weight, one row per expert
+ *  - router_bias fp32 [E] or NULL added to the fp32 router logits before
+ *              the selection and the softmax
+ *  - w_gate_up bf16 [E, 2F, D]    rows 0..F-1 of expert e are the activated
+ *              (SiLU) projection, rows F..2F-1 the one it multiplies
+ *  - w_down    bf16 [E, D, F]
+ *  - ws_gate_up bf16 [2Fs, D], ws_down bf16 [D, Fs]: the shared expert, or
+ *              NULL when F_shared == 0
+ *  - y         fp32 [T, D] (written, never read)
+ *  - topk_ids  int32 [T, k], topk_w fp32 [T, k]: slot j is the j-th highest
+ *              logit (ties to the lower expert index); weights sum to 1.
+ *  - Sizes: 0 <= T, 1 <= k <= min(E, 8), 1 <= E <= 256, D and F (and Fs when
+ *    nonzero) positive multiples of 8, T*k + E*BM + T < 2^31.
+ *  - Ownership: the caller owns every buffer.  The library allocates no device
+ *    memory and keeps no state between calls except a cached device-property
+ *    lookup.  The workspace is caller-provided, sized by moe_workspace_size,
+ *    and its contents need not be initialised.
+ *  - Execution: all work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) with no host synchronisation.  Calls on different streams
+ *    are independent when each has its own workspace and outputs.
+ *  - Errors: arguments are checked on the host before anything is enqueued;
+ *    a non-zero return means nothing was launched, except MOE_ERR_HIP, which
+ *    reports a failed launch (earlier kernels of the same call may have been
+ *    enqueued).  Faults inside kernels surface at the caller's next
+ *    synchronisation.  Non-finite inputs are outside the contract.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, size out of range, k > E, D or F not a multiple of 8 */
+  MOE_ERR_UNSUPPORTED = -2, /* E > 256, k > 8, or sizes overflowing 32-bit row indices */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_ALIGNMENT = -4,   /* a pointer not 16-byte aligned */
+  MOE_ERR_HIP = -5          /* a HIP launch failed; moe_strerror gives HIP's text */
+};
+
+typedef struct moe_shape {
+  int32_t T;               /* tokens */
+  int32_t D;               /* model width */
+  int32_t E;               /* routed experts */
+  int32_t F;               /* routed expert hidden width (d_ff) */
+  int32_t k;               /* experts per token */
+  int32_t F_shared;        /* shared expert hidden width, 0 = none */
+  int32_t has_router_bias; /* nonzero: weights->router_bias is used */
+} moe_shape;
+
+typedef struct moe_weights {
+  const void* x;            /* bf16 [T, D] */
+  const void* w_g;          /* bf16 [E, D] */
+  const float* router_bias; /* fp32 [E], or NULL when has_router_bias == 0 */
+  const void* w_gate_up;    /* bf16 [E, 2F, D] */
+  const void* w_down;       /* bf16 [E, D, F] */
+  const void* ws_gate_up;   /* bf16 [2*F_shared, D] or NULL */
+  const void* ws_down;      /* bf16 [D, F_shared] or NULL */
+} moe_weights;
+
+/*
+ * Bytes of device workspace moe_forward / moe_forward_routed need for `shape`.
+ * Host only; touches no GPU.  Returns MOE_OK or MOE_ERR_INVALID_ARG /
+ * MOE_ERR_UNSUPPORTED for a shape the other calls would reject.
+ */
+int moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/*
+ * Row-tile height BM the grouped GEMMs use for `shape`: every expert's group
+ * of rows is padded to a multiple of it (see moe_align).  Host only.
+ * Returns BM > 0, or a negative error code.
+ */
+int moe_block_m(const moe_shape* shape);
+
+/*
+ * Whole layer: router -> expert grouping -> gate/up GEMM with SwiGLU ->
+ * down GEMM -> weighted combine (+ shared expert, weight 1).
+ *   y         fp32 [T, D] out
+ *   topk_ids  int32 [T, k] out, or NULL (then kept in the workspace)
+ *   topk_w    fp32 [T, k] out, or NULL
+ *   workspace device buffer of ws_bytes >= moe_workspace_size(shape)
+ * Deterministic: the same inputs give bitwise the same outputs.
+ */
+int moe_forward(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
+                float* topk_w, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Router only: fp32 logits x . W_g^T (+ bias), top-k, softmax over the k
+ * chosen (same definition as moe_forward's first step).
+ * Uses w->x, w->w_g, w->router_bias; writes topk_ids [T,k] and topk_w [T,k].
+ */
+int moe_route(const moe_shape* shape, const moe_weights* w, int32_t* topk_ids, float* topk_w,
+              void* stream);
+
+/*
+ * Expert grouping of a routing (dispatch step).  Assignment a = t*k + j.
+ * Groups g = 0..E-1 hold the assignments routed to expert g in ascending a;
+ * when shared_rows > 0 a last group g = E holds rows t = 0..shared_rows-1 in
+ * order (the shared expert).  Each group is padded to a multiple of block_m.
+ *   topk_ids       int32 [T*k] in, every id in [0, E)  (ids outside are skipped:
+ *                  they get row_of = -1 and no row)
+ *   counts         int32 [G]      rows of each group, G = E + (shared_rows > 0)
+ *   offsets        int32 [G+1]    exclusive prefix sum of counts
+ *   padded_offsets int32 [G+1]    exclusive prefix sum of ceil(count/block_m)*block_m
+ *   sorted_assign  int32 [T*k]    the assignments in (expert, a) order
+ *   row_of         int32 [T*k]    padded row of each assignment
+ *   row_token      int32 [T*k + G*(block_m-1) + shared_rows]  token of each
+ *                  padded row, -1 on padding rows (entries past the last
+ *                  padded row are left untouched)
+ *   tile_group     int32 [(T*k + G*(block_m-1) + shared_rows)/block_m + 1]
+ *                  group of each block_m-row tile
+ *   n_tiles        int32 [1]      number of tiles (padded_offsets[G] / block_m)
+ * All outputs are device buffers.  1 <= block_m <= 1024.
+ */
+int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+              int32_t shared_rows, int32_t* counts, int32_t* offsets, int32_t* padded_offsets,
+              int32_t* sorted_assign, int32_t* row_of, int32_t* row_token, int32_t* tile_group,
+              int32_t* n_tiles, void* stream);
+
+/*
+ * moe_forward with the routing given instead of computed (w->w_g and
+ * w->router_bias are not read): topk_ids int32 [T,k] with distinct ids per
+ * token in [0, E), topk_w fp32 [T,k].
+ */
+int moe_forward_routed(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
+                       const float* topk_w, float* y, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * moe_forward that also records a HIP event before its first kernel and after
+ * each of its five kernels, on `stream`, so a caller can time every step
+ * (router, align, gate/up GEMM, down GEMM, combine) with hipEventElapsedTime.
+ *   events  array of 6 hipEvent_t created by the caller (hipEventCreate);
+ *           events[0] precedes the router, events[i] follows kernel i.
+ * Same results and errors as moe_forward; events are not recorded when T == 0.
+ */
+int moe_forward_timed(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
+                      float* topk_w, void* workspace, size_t ws_bytes, void* stream,
+                      void* const* events);
+
+/* Static text for an error code (for MOE_ERR_HIP: the last HIP error seen by
+ * this thread).  Never NULL. */
+const char* moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

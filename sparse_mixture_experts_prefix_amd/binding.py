@@ -1,0 +1,313 @@
+"""ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Every step of the layer runs in the library's HIP kernels.  torch supplies
+device memory and the current stream; nothing here computes any part of the
+layer, and there is no fallback: if libmoe.so is missing, or a tensor is not
+on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_ALIGNMENT = -4
+MOE_ERR_HIP = -5
+
+EXPORTS = ("moe_workspace_size", "moe_block_m", "moe_forward", "moe_route", "moe_align",
+           "moe_forward_routed", "moe_forward_timed", "moe_strerror")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("libmoe error %d: %s" % (code, msg))
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("F", ctypes.c_int32), ("k", ctypes.c_int32), ("F_shared", ctypes.c_int32),
+                ("has_router_bias", ctypes.c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("w_g", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("ws_gate_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe.so once; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError("libmoe.so is not built (%s); run __graft_entry__.build()" % path)
+            lib = ctypes.CDLL(path)
+            P = ctypes.c_void_p
+            i32 = ctypes.c_int32
+            lib.moe_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]
+            lib.moe_block_m.argtypes = [ctypes.POINTER(Shape)]
+            lib.moe_forward.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P, P, P,
+                                        ctypes.c_size_t, P]
+            lib.moe_route.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P, P]
+            lib.moe_align.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+            lib.moe_forward_routed.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P,
+                                               P, P, ctypes.c_size_t, P]
+            lib.moe_strerror.argtypes = [ctypes.c_int]
+            lib.moe_strerror.restype = ctypes.c_char_p
+            for name in EXPORTS[:-1]:
+                getattr(lib, name).restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load_library().moe_strerror(int(code)).decode()
+
+
+def _check(rc: int) -> int:
+    if rc < 0:
+        raise MoEError(rc, strerror(rc))
+    return rc
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t, name, dtype, shape=None):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_shape(T, D, E, F, k, F_shared=0, has_router_bias=False) -> Shape:
+    return Shape(int(T), int(D), int(E), int(F), int(k), int(F_shared), 1 if has_router_bias else 0)
+
+
+def workspace_size(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def block_m(shape: Shape) -> int:
+    return _check(load_library().moe_block_m(ctypes.byref(shape)))
+
+
+def _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, has_bias):
+    T, D = x.shape
+    E, twoF, D2 = w_gate_up.shape
+    F = twoF // 2
+    Fs = 0 if ws_gate_up is None else ws_gate_up.shape[0] // 2
+    return make_shape(T, D, E, F, k, Fs, has_bias)
+
+
+def alloc_workspace(shape: Shape, device) -> torch.Tensor:
+    return torch.empty(max(workspace_size(shape), 1), dtype=torch.uint8, device=device)
+
+
+def _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down) -> Weights:
+    return Weights(_ptr(x), _ptr(w_g), _ptr(router_bias), _ptr(w_gate_up), _ptr(w_down),
+                   _ptr(ws_gate_up), _ptr(ws_down))
+
+
+def _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down):
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [T, D]")
+    T, D = x.shape
+    _dev(w_gate_up, "w_gate_up", torch.bfloat16)
+    if w_gate_up.dim() != 3 or w_gate_up.shape[2] != D or w_gate_up.shape[1] % 2:
+        raise ValueError("w_gate_up must be [E, 2F, D]")
+    E, twoF, _ = w_gate_up.shape
+    _dev(w_down, "w_down", torch.bfloat16, (E, D, twoF // 2))
+    if (ws_gate_up is None) != (ws_down is None):
+        raise ValueError("ws_gate_up and ws_down go together")
+    if ws_gate_up is not None:
+        _dev(ws_gate_up, "ws_gate_up", torch.bfloat16)
+        if ws_gate_up.dim() != 2 or ws_gate_up.shape[1] != D or ws_gate_up.shape[0] % 2:
+            raise ValueError("ws_gate_up must be [2Fs, D]")
+        _dev(ws_down, "ws_down", torch.bfloat16, (D, ws_gate_up.shape[0] // 2))
+    for t in (w_gate_up, w_down, ws_gate_up, ws_down):
+        if t is not None and t.device != x.device:
+            raise ValueError("all tensors must be on one device")
+    return T, D, E, twoF // 2
+
+
+def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None, ws_down=None, *,
+                y=None, topk_ids=None, topk_w=None, workspace=None):
+    """Whole MoE layer.  Returns y (fp32 [T, D]).
+
+    Optional preallocated outputs (y, topk_ids int32 [T,k], topk_w fp32 [T,k])
+    and workspace (uint8, >= workspace_size bytes) avoid any allocation here.
+    """
+    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    _dev(w_g, "w_g", torch.bfloat16, (E, D))
+    if router_bias is not None:
+        _dev(router_bias, "router_bias", torch.float32, (E,))
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, router_bias is not None)
+    if y is None:
+        y = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32, (T, D))
+    if topk_ids is not None:
+        _dev(topk_ids, "topk_ids", torch.int32, (T, k))
+    if topk_w is not None:
+        _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if workspace is None:
+        workspace = alloc_workspace(shape, x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
+    _check(load_library().moe_forward(ctypes.byref(shape), ctypes.byref(w), _ptr(y), _ptr(topk_ids),
+                                      _ptr(topk_w), _ptr(workspace), workspace.numel(),
+                                      _stream(x.device)))
+    return y
+
+
+def moe_route(x, w_g, k, router_bias=None, *, topk_ids=None, topk_w=None):
+    """Router only.  Returns (topk_ids int32 [T,k], topk_w fp32 [T,k])."""
+    _dev(x, "x", torch.bfloat16)
+    T, D = x.shape
+    _dev(w_g, "w_g", torch.bfloat16)
+    E = w_g.shape[0]
+    _dev(w_g, "w_g", torch.bfloat16, (E, D))
+    if router_bias is not None:
+        _dev(router_bias, "router_bias", torch.float32, (E,))
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _dev(topk_ids, "topk_ids", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    shape = make_shape(T, D, E, 8, k, 0, router_bias is not None)
+    w = Weights(_ptr(x), _ptr(w_g), _ptr(router_bias), None, None, None, None)
+    _check(load_library().moe_route(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids),
+                                    _ptr(topk_w), _stream(x.device)))
+    return topk_ids, topk_w
+
+
+def moe_align(topk_ids, E: int, block_m_: int, shared_rows: int = 0):
+    """Expert grouping of a routing (int32 [T, k] on the GPU).  Returns a dict of
+    int32 GPU tensors sized to their upper bounds plus ``n_tiles`` (1 element)."""
+    _dev(topk_ids, "topk_ids", torch.int32)
+    T, k = topk_ids.shape
+    G = E + (1 if shared_rows > 0 else 0)
+    cap = T * k + G * (block_m_ - 1) + shared_rows
+    dev = topk_ids.device
+
+    def z(n, fill=0):
+        return torch.full((max(n, 1),), fill, dtype=torch.int32, device=dev)
+
+    out = dict(counts=z(G), offsets=z(G + 1), padded=z(G + 1), sorted_assign=z(T * k),
+               row_of=z(T * k), row_token=z(cap, -7), tile_group=z(cap // block_m_ + 1, -7),
+               n_tiles=z(1))
+    _check(load_library().moe_align(
+        _ptr(topk_ids), T, k, E, block_m_, shared_rows, _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["padded"]), _ptr(out["sorted_assign"]), _ptr(out["row_of"]), _ptr(out["row_token"]),
+        _ptr(out["tile_group"]), _ptr(out["n_tiles"]), _stream(dev)))
+    return out
+
+
+def moe_forward_routed(x, w_gate_up, w_down, topk_ids, topk_w, ws_gate_up=None, ws_down=None, *,
+                       y=None, workspace=None):
+    """The layer under a given routing (topk_ids int32 [T,k], topk_w fp32 [T,k])."""
+    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    k = topk_ids.shape[1]
+    _dev(topk_ids, "topk_ids", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, False)
+    if y is None:
+        y = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32, (T, D))
+    if workspace is None:
+        workspace = alloc_workspace(shape, x.device)
+    w = _weights(x, None, None, w_gate_up, w_down, ws_gate_up, ws_down)
+    _check(load_library().moe_forward_routed(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids),
+                                             _ptr(topk_w), _ptr(y), _ptr(workspace),
+                                             workspace.numel(), _stream(x.device)))
+    return y
+
+
+# the C names, one to one
+moe_workspace_size = workspace_size
+moe_block_m = block_m
+moe_strerror = strerror
+
+
+# ------------------------------------------------------------------ timing
+class HipEvents:
+    """A few raw hipEvent_t handles from the HIP runtime already loaded in this
+    process (the one torch uses), for moe_forward_timed."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self._hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+            self.handles.append(h.value)
+        self.array = (ctypes.c_void_p * n)(*self.handles)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float(0.0)
+        self._hip.hipEventSynchronize(ctypes.c_void_p(self.handles[j]))
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.handles[i]),
+                                           ctypes.c_void_p(self.handles[j]))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(ctypes.c_void_p(h))
+        self.handles = []
+
+
+def moe_forward_timed(events: HipEvents, x, w_g, w_gate_up, w_down, k, router_bias=None,
+                      ws_gate_up=None, ws_down=None, *, y, topk_ids, topk_w, workspace):
+    """moe_forward recording events[0..5] around its five kernels (all buffers preallocated)."""
+    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, router_bias is not None)
+    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
+    lib = load_library()
+    lib.moe_forward_timed.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_forward_timed.restype = ctypes.c_int
+    _check(lib.moe_forward_timed(ctypes.byref(shape), ctypes.byref(w), _ptr(y), _ptr(topk_ids),
+                                 _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(x.device),
+                                 ctypes.cast(events.array, ctypes.c_void_p)))
+    return y

@@ -1,0 +1,117 @@
+// moe_align: group the T*k token-to-expert assignments by expert.
+//
+// Dispatch step of "Mixture of Experts optimiza Transformers y LLMs", section
+// "Ejecución eficiente: backends de expertos" (tokens sorted by expert id
+// before the grouped products) and of the glossary "MoE (Mixture of Experts -
+// Mezcla de Expertos)", section 3 step 3 (a token's vector is duplicated to
+// each chosen expert).
+//
+// One workgroup per group g (E routed experts, plus the shared-expert group).
+// Every workgroup builds the full expert histogram in LDS (integer counts, so
+// the atomics' order does not matter) and derives offsets and padded offsets;
+// workgroup g then walks the assignments in ascending order and compacts the
+// ones routed to g with a ballot/popcount rank, so the output is the stable
+// order by assignment index and bitwise reproducible.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__global__ __launch_bounds__(kThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int A, int k, int E, int BM, int shared_rows,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ padded,
+    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ tile_group,
+    int32_t* __restrict__ n_tiles) {
+  __shared__ int hist[258];
+  __shared__ int s_off[258];
+  __shared__ int s_pad[258];
+  __shared__ int wave_tot[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = E + (shared_rows > 0 ? 1 : 0);
+  const int g = blockIdx.x;
+
+  for (int i = tid; i < G; i += kThreads) hist[i] = (i == E) ? shared_rows : 0;
+  __syncthreads();
+  for (int a = tid; a < A; a += kThreads) {
+    const int e = ids[a];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, p = 0;
+    for (int i = 0; i < G; ++i) {
+      s_off[i] = o;
+      s_pad[i] = p;
+      o += hist[i];
+      p += (hist[i] + BM - 1) / BM * BM;
+    }
+    s_off[G] = o;
+    s_pad[G] = p;
+  }
+  __syncthreads();
+  if (g == 0) {
+    for (int i = tid; i < G; i += kThreads) counts[i] = hist[i];
+    for (int i = tid; i <= G; i += kThreads) {
+      offsets[i] = s_off[i];
+      padded[i] = s_pad[i];
+    }
+    if (tid == 0) n_tiles[0] = s_pad[G] / BM;
+    // assignments with an id outside [0, E) get no row
+    for (int a = tid; a < A; a += kThreads) {
+      const int e = ids[a];
+      if (e < 0 || e >= E) row_of[a] = -1;
+    }
+  }
+  const int cnt = hist[g], pbeg = s_pad[g], pend = s_pad[g + 1], obeg = s_off[g];
+
+  if (g < E) {
+    int running = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < A; base += kThreads) {
+      const int a = base + tid;
+      const bool pred = a < A && ids[a] == g;
+      const uint64_t m = __ballot(pred);
+      const int rank = __popcll(m & below);
+      if (lane == 0) wave_tot[wave] = __popcll(m);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = wave_tot[w];
+        before += (w < wave) ? c : 0;
+        total += c;
+      }
+      if (pred) {
+        const int pos = running + before + rank;
+        sorted_assign[obeg + pos] = a;
+        row_of[a] = pbeg + pos;
+        row_token[pbeg + pos] = a / k;
+      }
+      running += total;
+      __syncthreads();  // wave_tot is rewritten by the next chunk
+    }
+  } else {
+    for (int t = tid; t < shared_rows; t += kThreads) row_token[pbeg + t] = t;
+  }
+  for (int r = pbeg + cnt + tid; r < pend; r += kThreads) row_token[r] = -1;
+  for (int i = pbeg / BM + tid; i < pend / BM; i += kThreads) tile_group[i] = g;
+}
+
+}  // namespace
+
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int shared_rows,
+                        int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
+                        int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
+                        hipStream_t s) {
+  const int G = E + (shared_rows > 0 ? 1 : 0);
+  hipLaunchKernelGGL(align_kernel, dim3(G), dim3(kThreads), 0, s, ids, T * k, k, E, BM, shared_rows,
+                     counts, offsets, padded, sorted_assign, row_of, row_token, tile_group, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,43 @@
+// Kernel launchers (host functions defined next to their kernels).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router: logits = x W_g^T (+ bias) in fp32, top-k, softmax over the chosen.
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_g, const float* bias, int T, int D,
+                         int E, int k, int32_t* ids, float* wts, hipStream_t s);
+
+// Expert grouping of the assignments (see moe_align in moe.h).
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int shared_rows,
+                        int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
+                        int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
+                        hipStream_t s);
+
+struct GroupedGemm {
+  const uint16_t* A;          // gate/up: x [T, D] (rows gathered by row_token); down: H
+  const int32_t* row_token;   // gate/up only
+  int64_t lda;                // elements
+  const uint16_t* B_routed;   // w_gate_up [E, 2F, D] or w_down [E, D, F]
+  const uint16_t* B_shared;   // ws_gate_up [2Fs, D] or ws_down [D, Fs]; NULL without shared
+  int E;
+  int N_routed, N_shared;     // output columns (gate/up: F, Fs; down: D, D)
+  int K_routed, K_shared;     // reduction length (gate/up: D, D; down: F, Fs)
+  const int32_t* tile_group;  // group of each BM-row tile
+  const int32_t* n_tiles;     // device count of valid tiles
+  int64_t max_tiles;          // host upper bound of n_tiles
+  void* C;                    // gate/up: H bf16; down: Yp fp32
+  int64_t ldc;                // elements
+  int BM;
+};
+
+hipError_t launch_gemm_gate_up(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_gemm_down(const GroupedGemm& g, hipStream_t s);
+
+// y[t] = sum_j w[t,j] * Yp[row_of[t*k+j]] (+ Yp[shared_base + t]) in fixed order.
+hipError_t launch_combine(const float* Yp, const int32_t* row_of, const float* wts,
+                          const int32_t* padded, int T, int D, int k, int E, int has_shared,
+                          float* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,85 @@
+// Host-side argument checks and workspace layout (no HIP calls).
+#include "plan.hpp"
+
+namespace moe {
+
+namespace {
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+}  // namespace
+
+int check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->D <= 0 || s->E <= 0 || s->F <= 0 || s->k <= 0 || s->F_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->k > s->E) return MOE_ERR_INVALID_ARG;
+  if (s->D % 8 || s->F % 8 || s->F_shared % 8) return MOE_ERR_INVALID_ARG;
+  if (s->E > 256 || s->k > 8) return MOE_ERR_UNSUPPORTED;
+  // every padded row index and every x/y element offset per row must fit 32 bits
+  const int64_t bm = 256;  // largest tile height any plan uses
+  const int64_t rows = (int64_t)s->T * s->k + (int64_t)(s->E + 1) * bm + s->T;
+  if (rows >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int choose_block_m(const moe_shape* s) {
+  (void)s;
+  return 128;
+}
+
+int make_plan(const moe_shape* s, Plan* p) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  p->T = s->T;
+  p->D = s->D;
+  p->E = s->E;
+  p->F = s->F;
+  p->k = s->k;
+  p->Fs = s->F_shared;
+  p->G = s->E + (s->F_shared > 0 ? 1 : 0);
+  p->BM = choose_block_m(s);
+  p->A = p->T * p->k;
+  p->cap_rows = p->A + (int64_t)p->G * (p->BM - 1) + (p->Fs > 0 ? p->T : 0);
+  p->max_tiles = p->cap_rows / p->BM + 1;
+  p->ldh = p->F > p->Fs ? p->F : p->Fs;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = round_up(o + bytes);
+    return at;
+  };
+  p->off_ids = take(sizeof(int32_t) * p->A);
+  p->off_w = take(sizeof(float) * p->A);
+  p->off_counts = take(sizeof(int32_t) * (p->G + 1));
+  p->off_offsets = take(sizeof(int32_t) * (p->G + 1));
+  p->off_padded = take(sizeof(int32_t) * (p->G + 1));
+  p->off_ntiles = take(sizeof(int32_t));
+  p->off_sorted = take(sizeof(int32_t) * p->A);
+  p->off_rowof = take(sizeof(int32_t) * p->A);
+  p->off_rowtoken = take(sizeof(int32_t) * p->cap_rows);
+  p->off_tilegroup = take(sizeof(int32_t) * p->max_tiles);
+  p->off_h = take(sizeof(uint16_t) * (size_t)p->cap_rows * p->ldh);
+  p->off_yp = take(sizeof(float) * (size_t)p->cap_rows * p->D);
+  p->total = o;
+  return MOE_OK;
+}
+
+int check_weights(const moe_shape* s, const moe_weights* w, bool need_router) {
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (s->T > 0 && !w->x) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+  if (need_router) {
+    if (!w->w_g) return MOE_ERR_INVALID_ARG;
+    if (s->has_router_bias && !w->router_bias) return MOE_ERR_INVALID_ARG;
+  }
+  if (s->F_shared > 0 && (!w->ws_gate_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->x, w->w_gate_up, w->w_down, w->ws_gate_up, w->ws_down,
+                        need_router ? w->w_g : nullptr};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MOE_ERR_ALIGNMENT;
+  if (need_router && s->has_router_bias && (reinterpret_cast<uintptr_t>(w->router_bias) & 3u))
+    return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+}  // namespace moe

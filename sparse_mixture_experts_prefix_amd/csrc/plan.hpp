@@ -1,0 +1,40 @@
+// Host-side argument checks and workspace layout of the MoE layer call.
+// No HIP calls: this unit is plain C++ so its logic can be exercised on a
+// machine without a GPU.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Row-tile height of the grouped GEMMs and the per-call workspace layout.
+struct Plan {
+  int64_t T, D, E, F, k, Fs;
+  int G;              // groups: E routed (+1 shared)
+  int BM;             // row-tile height; every group is padded to a multiple of it
+  int64_t A;          // assignments T*k
+  int64_t cap_rows;   // upper bound of padded rows over all groups
+  int64_t max_tiles;  // upper bound of BM-row tiles
+  int64_t ldh;        // row stride (elements) of the hidden activations H: max(F, Fs)
+  // byte offsets inside the workspace
+  size_t off_ids, off_w, off_counts, off_offsets, off_padded, off_ntiles, off_sorted, off_rowof,
+      off_rowtoken, off_tilegroup, off_h, off_yp, total;
+};
+
+// Shape checks shared by every entry point (MOE_OK or an error code).
+int check_shape(const moe_shape* s);
+
+// Tile height for a shape (assumes check_shape passed).
+int choose_block_m(const moe_shape* s);
+
+// Fill `p` for a valid shape; returns check_shape's code.
+int make_plan(const moe_shape* s, Plan* p);
+
+// Pointer checks of moe_forward / moe_forward_routed (routed: ids/w given).
+int check_weights(const moe_shape* s, const moe_weights* w, bool need_router);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace moe

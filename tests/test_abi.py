@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every symbol moe.h
+declares, and its host-side checks return the documented codes before any
+launch (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("sparse_mixture_experts_prefix_amd")
+from sparse_mixture_experts_prefix_amd import binding as B  # noqa: E402
+from sparse_mixture_experts_prefix_amd import build as native  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(native.LIB_PATH):
+        native.build()
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_forward", "moe_route", "moe_align", "moe_forward_routed", "moe_workspace_size",
+              "moe_block_m", "moe_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(B.EXPORTS)
+
+
+def _shape(**kw):
+    d = dict(T=64, D=128, E=8, F=256, k=2, F_shared=0, has_router_bias=0)
+    d.update(kw)
+    return B.Shape(**d)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def _weights(**kw):
+    d = dict(x=FAKE, w_g=FAKE, router_bias=None, w_gate_up=FAKE, w_down=FAKE, ws_gate_up=None,
+             ws_down=None)
+    d.update(kw)
+    return B.Weights(**d)
+
+
+def _fwd(lib, shape, w, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.moe_forward(ctypes.byref(shape), ctypes.byref(w), y, None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), B.MOE_ERR_INVALID_ARG), (dict(k=9, E=16), B.MOE_ERR_UNSUPPORTED),
+    (dict(k=3, E=2), B.MOE_ERR_INVALID_ARG), (dict(E=257), B.MOE_ERR_UNSUPPORTED),
+    (dict(D=100), B.MOE_ERR_INVALID_ARG), (dict(F=12), B.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), B.MOE_ERR_INVALID_ARG), (dict(F_shared=4), B.MOE_ERR_INVALID_ARG),
+    (dict(T=1 << 30, k=8), B.MOE_ERR_UNSUPPORTED)])
+def test_shape_errors(lib, kw, code):
+    assert _fwd(lib, _shape(**kw), _weights()) == code
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(_shape(**kw)), ctypes.byref(n)) == code
+
+
+def test_pointer_errors(lib):
+    s = _shape()
+    assert _fwd(lib, s, _weights(x=None)) == B.MOE_ERR_INVALID_ARG
+    assert _fwd(lib, s, _weights(w_down=None)) == B.MOE_ERR_INVALID_ARG
+    assert _fwd(lib, s, _weights(), y=None) == B.MOE_ERR_INVALID_ARG
+    assert _fwd(lib, s, _weights(x=FAKE + 8)) == B.MOE_ERR_ALIGNMENT
+    assert _fwd(lib, s, _weights(), y=FAKE + 4) == B.MOE_ERR_ALIGNMENT
+    assert _fwd(lib, _shape(has_router_bias=1), _weights()) == B.MOE_ERR_INVALID_ARG
+    assert _fwd(lib, _shape(F_shared=64), _weights()) == B.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_too_small(lib):
+    s = _shape()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    assert _fwd(lib, s, _weights(), ws_bytes=n.value - 1) == B.MOE_ERR_WORKSPACE
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    # T = 0 returns before any launch, even with no x or y
+    assert _fwd(lib, _shape(T=0), _weights(x=None), y=None, ws=None) == 0
+
+
+def test_workspace_and_block_m(lib):
+    s = _shape(T=4096, D=4096, E=8, F=14336, k=2)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == 0
+    bm = lib.moe_block_m(ctypes.byref(s))
+    assert bm in (16, 32, 64, 128, 256)
+    rows = 4096 * 2 + 8 * (bm - 1)
+    # at least H (bf16) and Yp (fp32) for every padded row
+    assert n.value >= rows * (14336 * 2 + 4096 * 4)
+    assert n.value < 2 * rows * (14336 * 2 + 4096 * 4)
+
+
+def test_align_argument_errors(lib):
+    P = FAKE
+    assert lib.moe_align(P, 10, 2, 8, 0, 0, P, P, P, P, P, P, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_align(P, 10, 9, 16, 16, 0, P, P, P, P, P, P, P, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_align(P, 10, 2, 8, 16, 0, None, P, P, P, P, P, P, P, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5, 99):
+        assert isinstance(B.strerror(code), str) and B.strerror(code)
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moe.moe_forward(x, x, x.view(1, 4, 8), x.view(1, 8, 4), 1)

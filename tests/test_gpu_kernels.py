@@ -1,0 +1,229 @@
+"""GPU parity of each kernel and of the layer, at sizes the oracle finishes in seconds.
+
+Every call goes through the C ABI (libmoe.so) via the ctypes binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import align_equal, check_routing, reference_y, sample_tokens, y_error
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("sparse_mixture_experts_prefix_amd")
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    moe.load_library()  # raises loudly when libmoe.so is missing
+
+
+def _gpu(inp):
+    return inp.to(DEV)
+
+
+def _forward(inp, **kw):
+    g = _gpu(inp)
+    s = inp.shape
+    T = inp.x.shape[0]
+    ids = torch.empty((T, s.k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, s.k), dtype=torch.float32, device=DEV)
+    y = moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias, g.ws_gate_up,
+                        g.ws_down, topk_ids=ids, topk_w=w, **kw)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _layer_parity(inp, tokens=None):
+    s = inp.shape
+    y, ids_g, w_g = _forward(inp)
+    ids_or, p_or, margin, logits = oracle.route(inp.x, inp.w_g, inp.router_bias, s.k)
+    flipped = check_routing(ids_g, w_g, ids_or, p_or, margin, logits, s.k)
+    T = inp.x.shape[0]
+    tok = np.arange(T) if tokens is None else tokens
+    y_ref = reference_y(inp, ids_or, p_or, ids_g, w_g, flipped, tok)
+    rel, err, rms = y_error(y[tok], y_ref)
+    print("T=%d D=%d E=%d k=%d F=%d Fs=%d: max|err|/RMS=%.4g flips=%d" % (
+        T, s.D, s.E, s.k, s.F, s.Fs, rel, len(flipped)))
+    assert rel <= 2e-2
+    return y, ids_g, w_g
+
+
+# --------------------------------------------------------------------- router
+@pytest.mark.parametrize("T,D,E,k,bias", [
+    (64, 128, 8, 2, False), (300, 2880, 32, 4, False), (97, 7168, 256, 8, False),
+    (1, 64, 3, 3, False), (50, 4096, 8, 2, True), (33, 136, 17, 5, False)])
+def test_router_parity(T, D, E, k, bias):
+    s = W.Shape(T=T, D=D, E=E, k=k, F=8, router_bias=bias)
+    inp = W.make_inputs(s, seed=T + D)
+    g = _gpu(inp)
+    ids, w = moe.moe_route(g.x, g.w_g, k, g.router_bias)
+    torch.cuda.synchronize()
+    ids_or, p_or, margin, logits = oracle.route(inp.x, inp.w_g, inp.router_bias, k)
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_or, p_or, margin, logits, k)
+
+
+def test_router_exact_ties_on_grid_inputs():
+    """Exact fp32 ties (grid inputs): the GPU must take the lower index, like the oracle."""
+    s = W.Shape(T=500, D=64, E=16, k=4, F=8)
+    inp = W.make_grid_inputs(s, seed=7)
+    g = _gpu(inp)
+    ids, w = moe.moe_route(g.x, g.w_g, s.k)
+    torch.cuda.synchronize()
+    ids_or, p_or, margin, logits = oracle.route(inp.x, inp.w_g, None, s.k)
+    assert np.any(margin == 0)
+    assert np.array_equal(ids.cpu().numpy(), ids_or)  # logits are exact, so order is too
+
+
+def test_router_batch_invariance():
+    s = W.Shape(T=64, D=2880, E=32, k=4, F=8)
+    inp = W.make_inputs(s, seed=3)
+    g = _gpu(inp)
+    ids, w = moe.moe_route(g.x, g.w_g, s.k)
+    for t in (0, 15, 16, 63):
+        i1, w1 = moe.moe_route(g.x[t:t + 1].contiguous(), g.w_g, s.k)
+        assert torch.equal(i1[0], ids[t]) and torch.equal(w1[0], w[t])
+
+
+# ---------------------------------------------------------------------- align
+@pytest.mark.parametrize("T,k,E,shared", [(64, 2, 8, 0), (1000, 4, 32, 0), (513, 8, 256, 513),
+                                          (1, 4, 32, 0), (4096, 2, 8, 4096), (3, 1, 1, 0)])
+def test_align_parity_random_ids(T, k, E, shared):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    shape = moe.make_shape(T, 64, E, 64, k, 64 if shared else 0)
+    bm = moe.moe_block_m(shape)
+    out = moe.moe_align(torch.from_numpy(ids).to(DEV), E, bm, shared)
+    torch.cuda.synchronize()
+    ref = oracle.align(ids, E, bm, shared=bool(shared))
+    align_equal({k_: v.cpu().numpy() for k_, v in out.items()}, ref)
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
+def test_align_parity_block_sizes_and_skew(bm):
+    T, k, E = 777, 2, 8
+    rng = np.random.default_rng(bm)
+    # Zipf-like loads with two empty experts
+    p = np.array([0.5, 0.3, 0.1, 0.05, 0.03, 0.02, 0.0, 0.0])
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    out = moe.moe_align(torch.from_numpy(ids).to(DEV), E, bm, 0)
+    ref = oracle.align(ids, E, bm)
+    align_equal({k_: v.cpu().numpy() for k_, v in out.items()}, ref)
+
+
+def test_align_all_to_one_expert():
+    T, k, E = 300, 2, 8
+    ids = np.tile(np.array([[6, 1]], np.int32), (T, 1))
+    out = moe.moe_align(torch.from_numpy(ids).to(DEV), E, 128, 0)
+    align_equal({k_: v.cpu().numpy() for k_, v in out.items()}, oracle.align(ids, E, 128))
+
+
+# ------------------------------------------------------------- routed layer
+@pytest.mark.parametrize("T,D,E,k,F,Fs", [(200, 256, 8, 2, 384, 0), (1, 128, 4, 2, 64, 0),
+                                          (300, 192, 16, 4, 136, 64)])
+def test_forward_routed_parity(T, D, E, k, F, Fs):
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs)
+    inp = W.make_inputs(s, seed=T)
+    ids_or, p_or, _, _ = oracle.route(inp.x, inp.w_g, None, k)
+    g = _gpu(inp)
+    y = moe.moe_forward_routed(g.x, g.w_gate_up, g.w_down, torch.from_numpy(ids_or).to(DEV),
+                               torch.from_numpy(p_or.astype(np.float32)).to(DEV), g.ws_gate_up,
+                               g.ws_down)
+    torch.cuda.synchronize()
+    y_ref = oracle.experts(inp, ids_or, p_or.astype(np.float32).astype(np.float64))
+    rel, _, _ = y_error(y.cpu().numpy(), y_ref)
+    assert rel <= 2e-2
+
+
+# --------------------------------------------------------------- whole layer
+LAYER_CASES = [
+    # several tiles per expert and a ragged last tile in M, N and K
+    (2048, 256, 8, 2, 512, 0, False),
+    (1500, 320, 8, 2, 200, 0, False),
+    (333, 2880, 32, 4, 2880, 0, False),
+    (700, 512, 64, 8, 256, 256, False),
+    (1024, 1024, 8, 2, 1024, 0, True),
+    (5, 128, 8, 2, 256, 0, False),
+    (64, 128, 8, 2, 256, 0, False),
+]
+
+
+@pytest.mark.parametrize("T,D,E,k,F,Fs,bias", LAYER_CASES)
+def test_layer_parity(T, D, E, k, F, Fs, bias):
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, router_bias=bias)
+    _layer_parity(W.make_inputs(s, seed=T + E))
+
+
+def test_layer_E1_k1_dense_ffn():
+    s = W.Shape(T=100, D=256, E=1, k=1, F=512)
+    y, ids, w = _layer_parity(W.make_inputs(s, seed=1))
+    assert np.all(ids == 0) and np.all(w == 1.0)
+
+
+def test_layer_k_equals_E():
+    s = W.Shape(T=100, D=128, E=4, k=4, F=128)
+    _layer_parity(W.make_inputs(s, seed=2))
+
+
+def test_layer_all_tokens_to_one_expert_and_empty_experts():
+    """A +100 bias on one expert sends every token there first; others stay empty."""
+    s = W.Shape(T=400, D=256, E=8, k=1, F=256, router_bias=True)
+    inp = W.make_inputs(s, seed=4)
+    inp.router_bias = torch.tensor([-100, -100, -100, 100, -100, -100, -100, -100], dtype=torch.float32)
+    y, ids, w = _layer_parity(inp)
+    assert np.all(ids == 3)
+
+
+def test_layer_zero_tokens():
+    s = W.Shape(T=0, D=128, E=8, k=2, F=256)
+    inp = W.make_inputs(s, seed=0)
+    y, ids, w = _forward(inp)
+    assert y.shape == (0, 128)
+
+
+def test_layer_deterministic_and_scaling():
+    s = W.Shape(T=777, D=512, E=16, k=4, F=384, Fs=128)
+    inp = W.make_inputs(s, seed=9)
+    y1, i1, w1 = _forward(inp)
+    y2, i2, w2 = _forward(inp)
+    assert np.array_equal(y1, y2) and np.array_equal(i1, i2) and np.array_equal(w1, w2)
+    inp2 = W.LayerInputs(s, inp.x, inp.w_g, inp.w_gate_up, (inp.w_down * 2).contiguous(), None,
+                         inp.ws_gate_up, (inp.ws_down * 2).contiguous())
+    y3, _, _ = _forward(inp2)
+    assert np.array_equal(y3, 2 * y1)  # power-of-two scaling commutes with every rounding
+
+
+def test_layer_poisoned_workspace_and_guards():
+    """A NaN-filled workspace must not leak into y (padding rows are never read),
+    and bytes around y stay untouched."""
+    s = W.Shape(T=300, D=256, E=8, k=2, F=320, Fs=64)
+    inp = W.make_inputs(s, seed=10)
+    g = _gpu(inp)
+    shape = moe.make_shape(300, 256, 8, 320, 2, 64)
+    ws = moe.alloc_workspace(shape, DEV)
+    ws.view(torch.uint8).fill_(0xFF)  # every float in it is NaN
+    y_ref = moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, 2, None, g.ws_gate_up, g.ws_down)
+    guard = torch.full((300 * 256 + 2 * 64,), 12345.0, dtype=torch.float32, device=DEV)
+    y = guard[64:64 + 300 * 256].view(300, 256)
+    moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, 2, None, g.ws_gate_up, g.ws_down, y=y,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.all(guard[:64] == 12345.0) and torch.all(guard[-64:] == 12345.0)
+
+
+def test_errors_are_raised_before_launch():
+    s = W.Shape(T=16, D=128, E=8, k=2, F=256)
+    g = _gpu(W.make_inputs(s, seed=0))
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, 2, workspace=small)
+    assert ei.value.code == moe.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, 9)
+    assert ei.value.code in (moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED)
