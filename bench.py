@@ -77,6 +77,9 @@ def main():
     ap.add_argument("--T", type=int, default=None, help="token count override (decode sweeps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="run one plain device copy of this many GiB first (a known-size kernel "
+                         "for calibrating rocprofv3 byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -117,6 +120,16 @@ def main():
     y = torch.empty((s.T, s.D), dtype=torch.float32, device=dev)
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
     wts = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        _log("copy calibration: %d bytes read, %d bytes written" % (n, n))
 
     def step(i):
         q = sets[i % len(sets)]

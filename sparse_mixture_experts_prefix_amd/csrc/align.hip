@@ -21,7 +21,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
-__global__ __launch_bounds__(kThreads) void align_kernel(
+__global__ __launch_bounds__(kThreads) void moe_align_kernel(
     const int32_t* __restrict__ ids, int A, int k, int E, int BM, int shared_rows,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ padded,
     int32_t* __restrict__ sorted_assign, int32_t* __restrict__ row_of,
@@ -109,7 +109,7 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int sha
                         int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
                         hipStream_t s) {
   const int G = E + (shared_rows > 0 ? 1 : 0);
-  hipLaunchKernelGGL(align_kernel, dim3(G), dim3(kThreads), 0, s, ids, T * k, k, E, BM, shared_rows,
+  hipLaunchKernelGGL(moe_align_kernel, dim3(G), dim3(kThreads), 0, s, ids, T * k, k, E, BM, shared_rows,
                      counts, offsets, padded, sorted_assign, row_of, row_token, tile_group, n_tiles);
   return hipGetLastError();
 }

@@ -67,7 +67,10 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   gu.C = H;
   gu.ldc = P.ldh;
   gu.BM = P.BM;
-  e = launch_gemm_gate_up(gu, s);
+  gu.group_count = counts;
+  gu.group_padded = padded;
+  gu.a_bytes = P.T * P.D * 2;
+  e = P.BM == 256 ? launch_gemm_gate_up_prefill(gu, s) : launch_gemm_gate_up(gu, s);
   if (e == hipSuccess) e = mk.mark(3, s);
   if (e != hipSuccess) return hip_fail(e);
 
@@ -83,7 +86,8 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   dn.K_shared = (int)P.Fs;
   dn.C = Yp;
   dn.ldc = P.D;
-  e = launch_gemm_down(dn, s);
+  dn.a_bytes = P.cap_rows * P.ldh * 2;
+  e = P.BM == 256 ? launch_gemm_down_prefill(dn, s) : launch_gemm_down(dn, s);
   if (e == hipSuccess) e = mk.mark(4, s);
   if (e != hipSuccess) return hip_fail(e);
 

@@ -18,7 +18,7 @@ namespace {
 
 constexpr int kMaxK = 8;
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Yp,
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ Yp,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ wts,
                                                       const int32_t* __restrict__ padded, int T,
@@ -55,7 +55,7 @@ hipError_t launch_combine(const float* Yp, const int32_t* row_of, const float* w
                           const int32_t* padded, int T, int D, int k, int E, int has_shared,
                           float* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, s, Yp, row_of, wts, padded, T, D, k, E,
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, s, Yp, row_of, wts, padded, T, D, k, E,
                      has_shared, y);
   return hipGetLastError();
 }

@@ -26,7 +26,7 @@ constexpr int kBK = 64;
 constexpr int kLds = kBK + 8;  // padded LDS row (bf16): 144 B keeps 16-lane b128 reads conflict-free
 
 template <bool GATE_UP, int BM, int BN>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GroupedGemm p) {
+__device__ __forceinline__ void grouped_gemm_tile(const GroupedGemm& p) {
   constexpr int WM = BM / 2;            // rows per wave
   constexpr int MT = WM / 32;           // 32-row MFMA tiles per wave
   constexpr int NT = BN / 64;           // 32-col MFMA tiles per wave (gate/up: half gate, half up)
@@ -181,6 +181,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GroupedGemm p) {
   }
 }
 
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void moe_gemm_gate_up_kernel(GroupedGemm p) {
+  grouped_gemm_tile<true, BM, BN>(p);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void moe_gemm_down_kernel(GroupedGemm p) {
+  grouped_gemm_tile<false, BM, BN>(p);
+}
+
 template <bool GATE_UP, int BM, int BN>
 hipError_t launch_tiles(const GroupedGemm& g, hipStream_t s) {
   const int nmax = GATE_UP ? (g.N_routed > g.N_shared ? g.N_routed : g.N_shared)
@@ -189,8 +199,10 @@ hipError_t launch_tiles(const GroupedGemm& g, hipStream_t s) {
   const int64_t n_tiles_n = (nmax + NB - 1) / NB;
   const int64_t blocks = g.max_tiles * n_tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP, BM, BN>), dim3((unsigned)blocks), dim3(256), 0,
-                     s, g);
+  if (GATE_UP)
+    hipLaunchKernelGGL((moe_gemm_gate_up_kernel<BM, BN>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((moe_gemm_down_kernel<BM, BN>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

@@ -1,0 +1,254 @@
+// Prefill-sized grouped GEMMs (many rows per expert): 256 x 256 x 64 tiles.
+//
+// Same operation as the generic kernels in gemm.hip (SwiGLU expert FFN of the
+// glossary "MoE (Mixture of Experts - Mezcla de Expertos)", section 3 step 3;
+// packed [E, 2F, D] gate/up tensor of "Transformers v5 El Secreto Detrás de
+// los Modelos MoE Más Rápidos", section "La Solución: WeightConverter"), laid
+// out for CDNA4:
+//  - 4 wavefronts, each owning a 128 x 128 output block as 4 x 4 MFMA
+//    32x32x16 tiles (256 fp32 accumulators per lane), so every 16-byte LDS
+//    read feeds four MFMAs.
+//  - Operands go HBM/L2 -> LDS with buffer_load ... lds (no registers, no
+//    ds_write), double-buffered: the loads of stage s+1 fly while stage s is
+//    multiplied.  Out-of-range buffer offsets read as zero, which handles
+//    padding rows, gathered rows of -1 and N/K tails with no branches.
+//  - LDS rows are 128 B (64 bf16 of K); the eight 16-byte chunks of row r are
+//    stored XOR-swizzled by (r & 7) ^ ((r >> 3) & 1), which keeps both 8- and
+//    16-lane phases of the b128 operand reads on distinct banks.
+//  - Tiles are ordered in super-tiles of 4 m-tiles x 8 n-tiles and the block
+//    index is remapped so that each XCD (the hardware deals workgroups to the
+//    8 XCDs round-robin) walks a contiguous run of super-tiles: the 32
+//    workgroups an XCD runs together share their A and B tiles in its L2.
+//  - MFMA work of 32-row sub-tiles that hold only padding rows is skipped.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kStageBytes = (BM + BN) * BK * 2;  // 64 KB: A then B
+constexpr int kLdsBytes = 2 * kStageBytes;       // double buffer
+constexpr int MS = 4, NS = 8;                    // super-tile: MS m-tiles x NS n-tiles
+constexpr uint32_t kOob = 0x80000000u;           // buffer offset that reads as zero
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword3 0x00020000: raw (untyped) 32-bit data, the gfx9 default for buffer ops
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// First LDS row of B sub-tile j of wave column wn.
+template <bool GATE_UP>
+__device__ __forceinline__ int b_row_of(int wn, int j) {
+  if (GATE_UP) return (j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
+  return wn * 128 + j * 32;
+}
+
+// Main loop over K: stage s is multiplied from LDS buffer s&1 while the loads
+// of stage s+1 fill the other buffer.  ACT = active 32-row A sub-tiles.
+template <bool GATE_UP, int ACT, class Issue>
+__device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, int lane,
+                                       Issue& issue, f32x16 (&acc)[4][4]) {
+  const int lr = lane & 31, kh = lane >> 5;
+  int rd[4];  // LDS byte offset of this lane's chunk inside a 32-row block, per k-substep
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) rd[ks] = (lr * 8 + ((2 * ks + kh) ^ swz(lr))) * 16;
+  const int nk = (K + BK - 1) / BK;
+  issue(0, 0);
+  for (int s = 0; s < nk; ++s) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage s landed
+    __syncthreads();                     // ... and everyone's; stage s-1 reads are done
+    if (s + 1 < nk) issue((s + 1) * BK, (s + 1) & 1);
+    const char* sa = lds + (s & 1) * kStageBytes;
+    const char* sb = sa + BM * BK * 2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < ACT; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + rd[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + b_row_of<GATE_UP>(wn, j) * 128 + rd[ks]);
+#pragma unroll
+      for (int i = 0; i < ACT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  }
+}
+
+template <bool GATE_UP>
+__device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
+  // ---------------------------------------------------------------- schedule
+  const int64_t nt_n = p.n_tiles_n;
+  const int64_t m_blocks = (p.max_tiles + MS - 1) / MS;
+  const int64_t P = gridDim.x;  // multiple of 8
+  const int64_t L = (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8;
+  const int64_t S = L / (MS * NS), w = L % (MS * NS);
+  const int64_t m_tile = (S % m_blocks) * MS + w % MS;
+  const int64_t n_tile = (S / m_blocks) * NS + w / MS;
+  if (m_tile >= p.n_tiles[0] || n_tile >= nt_n) return;
+  const int g = p.tile_group[m_tile];
+  const bool shared = g >= p.E;
+  const int N = shared ? p.N_shared : p.N_routed;
+  const int K = shared ? p.K_shared : p.K_routed;
+  constexpr int NB = GATE_UP ? BN / 2 : BN;
+  const int n0 = (int)n_tile * NB;
+  if (n0 >= N) return;
+  const int64_t row0 = m_tile * BM;
+  const int valid_rows = min(BM, (int)(p.group_count[g] - (row0 - p.group_padded[g])));
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ------------------------------------------------------ operand sources
+  // Wave `wave`, load j (0..7) writes LDS rows (wave*8 + j)*8 .. +7 of a
+  // region; lane i of it carries row +i/8 and K-chunk (i%8) ^ swz(row).
+  const __amdgpu_buffer_rsrc_t rsA =
+      GATE_UP ? make_rsrc(p.A, (uint32_t)p.a_bytes)
+              : make_rsrc(p.A + row0 * p.lda, (uint32_t)(BM * p.lda * 2));
+  const bf16_t* Bg = shared ? p.B_shared
+                            : p.B_routed + (int64_t)g * (GATE_UP ? 2 : 1) * (int64_t)N * K;
+  const __amdgpu_buffer_rsrc_t rsB =
+      make_rsrc(Bg, (uint32_t)((int64_t)(GATE_UP ? 2 : 1) * N * K * 2));
+  uint32_t offA[8], offB[8];
+  const int sub = lane >> 3;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (wave * 8 + j) * 8 + sub;  // 0..255
+    const int kc = (lane & 7) ^ swz(r);
+    const uint32_t kb = kc * 16;
+    if (GATE_UP) {
+      const int t = r < valid_rows ? p.row_token[row0 + r] : -1;
+      offA[j] = t >= 0 ? (uint32_t)t * (uint32_t)(p.lda * 2) + kb : kOob;
+      const int half = r >> 7, f = n0 + (r & 127);
+      offB[j] = f < N ? (uint32_t)(half * N + f) * (uint32_t)(K * 2) + kb : kOob;
+    } else {
+      offA[j] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + kb : kOob;
+      const int n = n0 + r;
+      offB[j] = n < N ? (uint32_t)n * (uint32_t)(K * 2) + kb : kOob;
+    }
+  }
+  const int kcl = (lane & 7);  // chunk position within the 8 of a row, before the swizzle
+
+  auto issue = [&](int k0, int stage) {
+    char* base = lds + stage * kStageBytes;
+    // K tail: chunks at or past K read as zero (wave-uniform branch, last stage only)
+    const bool tail = k0 + BK > K;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t oa = offA[j], ob = offB[j];
+      if (tail) {
+        const int r = (wave * 8 + j) * 8 + sub;
+        const int kc = kcl ^ swz(r);
+        if (k0 + kc * 8 >= K) oa = ob = kOob;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(base + (wave * 8 + j) * 1024), 16,
+                                               oa, k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsB, (lds_void*)(base + BM * BK * 2 + (wave * 8 + j) * 1024), 16, ob, k0 * 2, 0, 0);
+    }
+  };
+
+  // active 32-row sub-tiles of this wave (uniform): the K loop is compiled
+  // once per count so no MFMA sits under a branch
+  const int act = min(4, max(0, (valid_rows - wm * 128 + 31) / 32));
+  const int lr = lane & 31, kh = lane >> 5;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  switch (act) {
+    case 4: k_loop<GATE_UP, 4>(lds, K, wm, wn, lane, issue, acc); break;
+    case 3: k_loop<GATE_UP, 3>(lds, K, wm, wn, lane, issue, acc); break;
+    case 2: k_loop<GATE_UP, 2>(lds, K, wm, wn, lane, issue, acc); break;
+    case 1: k_loop<GATE_UP, 1>(lds, K, wm, wn, lane, issue, acc); break;
+    default: k_loop<GATE_UP, 0>(lds, K, wm, wn, lane, issue, acc); break;
+  }
+  auto a_row = [&](int i) { return wm * 128 + i * 32; };
+
+  // -------------------------------------------------------------- epilogue
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= act) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
+      const int64_t grow = row0 + row;
+      if (GATE_UP) {
+        bf16_t* H = reinterpret_cast<bf16_t*>(p.C);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = n0 + wn * 64 + j * 32 + lr;
+          if (f < N) H[grow * p.ldc + f] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + 2][r]);
+        }
+      } else {
+        float* Y = reinterpret_cast<float*>(p.C);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * 128 + j * 32 + lr;
+          if (n < N) Y[grow * p.ldc + n] = acc[i][j][r];
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void moe_gemm_gate_up_prefill_kernel(GroupedGemm p) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  prefill_tile<true>(p, lds);
+}
+
+__global__ __launch_bounds__(256) void moe_gemm_down_prefill_kernel(GroupedGemm p) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  prefill_tile<false>(p, lds);
+}
+
+hipError_t launch(bool gate_up, GroupedGemm g, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
+  const int NB = gate_up ? BN / 2 : BN;
+  g.n_tiles_n = (nmax + NB - 1) / NB;
+  const int64_t m_blocks = (g.max_tiles + MS - 1) / MS;
+  const int64_t n_blocks = (g.n_tiles_n + NS - 1) / NS;
+  const int64_t blocks = m_blocks * n_blocks * MS * NS;  // a multiple of 8
+  if (blocks == 0) return hipSuccess;
+  if (gate_up)
+    hipLaunchKernelGGL(moe_gemm_gate_up_prefill_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes,
+                       s, g);
+  else
+    hipLaunchKernelGGL(moe_gemm_down_prefill_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes, s,
+                       g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_gate_up_prefill(const GroupedGemm& g, hipStream_t s) {
+  return launch(true, g, s);
+}
+
+hipError_t launch_gemm_down_prefill(const GroupedGemm& g, hipStream_t s) {
+  return launch(false, g, s);
+}
+
+}  // namespace moe

@@ -30,10 +30,18 @@ struct GroupedGemm {
   void* C;                    // gate/up: H bf16; down: Yp fp32
   int64_t ldc;                // elements
   int BM;
+  const int32_t* group_count;   // rows of each group
+  const int32_t* group_padded;  // first padded row of each group
+  int64_t a_bytes;              // bytes addressable through A (gate/up: all of x)
+  int64_t n_tiles_n;            // set by the launcher
 };
 
+// Generic tiles (any BM the plan picks below the prefill size).
 hipError_t launch_gemm_gate_up(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_gemm_down(const GroupedGemm& g, hipStream_t s);
+// 256 x 256 x 64 tiles for BM = 256 (prefill-sized groups).
+hipError_t launch_gemm_gate_up_prefill(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_gemm_down_prefill(const GroupedGemm& g, hipStream_t s);
 
 // y[t] = sum_j w[t,j] * Yp[row_of[t*k+j]] (+ Yp[shared_base + t]) in fixed order.
 hipError_t launch_combine(const float* Yp, const int32_t* row_of, const float* wts,

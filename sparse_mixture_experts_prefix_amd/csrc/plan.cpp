@@ -19,12 +19,17 @@ int check_shape(const moe_shape* s) {
   const int64_t bm = 256;  // largest tile height any plan uses
   const int64_t rows = (int64_t)s->T * s->k + (int64_t)(s->E + 1) * bm + s->T;
   if (rows >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  // operands are addressed through 32-bit buffer offsets below 2^31 bytes
+  const int64_t lim = int64_t(1) << 31;
+  if ((int64_t)s->T * s->D * 2 >= lim) return MOE_ERR_UNSUPPORTED;
+  const int64_t fmax = s->F > s->F_shared ? s->F : s->F_shared;
+  if ((int64_t)fmax * s->D * 4 >= lim) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 int choose_block_m(const moe_shape* s) {
   (void)s;
-  return 128;
+  return 256;
 }
 
 int make_plan(const moe_shape* s, Plan* p) {

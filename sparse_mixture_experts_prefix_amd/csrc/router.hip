@@ -26,7 +26,7 @@ __device__ __forceinline__ bool better(float v, int i, float w, int j) {
 }
 
 template <int NCT>  // 16-expert column tiles; E <= 16 * NCT
-__global__ __launch_bounds__(256) void router_kernel(const bf16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void moe_router_kernel(const bf16_t* __restrict__ x,
                                                      const bf16_t* __restrict__ wg,
                                                      const float* __restrict__ bias, int T, int D,
                                                      int E, int k, int32_t* __restrict__ ids,
@@ -141,7 +141,7 @@ template <int NCT>
 hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias, int T, int D,
                       int E, int k, int32_t* ids, float* wts, hipStream_t s) {
   const int blocks = (T + kTok - 1) / kTok;
-  hipLaunchKernelGGL(router_kernel<NCT>, dim3(blocks), dim3(256), 0, s, x, w_g, bias, T, D, E, k,
+  hipLaunchKernelGGL(moe_router_kernel<NCT>, dim3(blocks), dim3(256), 0, s, x, w_g, bias, T, D, E, k,
                      ids, wts);
   return hipGetLastError();
 }
