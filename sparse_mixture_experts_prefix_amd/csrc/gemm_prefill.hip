@@ -49,8 +49,12 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
   return wn * 128 + j * 32;
 }
 
-// Main loop over K: stage s is multiplied from LDS buffer s&1 while the loads
-// of stage s+1 fill the other buffer.  ACT = active 32-row A sub-tiles.
+// Main loop over K.  LDS holds two stages; registers hold two sets of operand
+// fragments.  While the MFMAs of k-substep ks run, the fragments of ks+1 are
+// being read; the one barrier per stage sits before the last substep, after
+// its fragments are in registers, so the first reads of the next stage and
+// the loads of the stage after it overlap the last 16 MFMAs.
+// ACT = active 32-row A sub-tiles of this wave.
 template <bool GATE_UP, int ACT, class Issue>
 __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, int lane,
                                        Issue& issue, f32x16 (&acc)[4][4]) {
@@ -59,26 +63,40 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) rd[ks] = (lr * 8 + ((2 * ks + kh) ^ swz(lr))) * 16;
   const int nk = (K + BK - 1) / BK;
-  issue(0, 0);
-  for (int s = 0; s < nk; ++s) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of stage s landed
-    __syncthreads();                     // ... and everyone's; stage s-1 reads are done
-    if (s + 1 < nk) issue((s + 1) * BK, (s + 1) & 1);
-    const char* sa = lds + (s & 1) * kStageBytes;
+
+  bf16x8 fa[2][4], fb[2][4];
+  auto read = [&](int stage, int ks, int slot) {
+    const char* sa = lds + (stage & 1) * kStageBytes;
     const char* sb = sa + BM * BK * 2;
 #pragma unroll
+    for (int i = 0; i < ACT; ++i)
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + rd[ks]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + b_row_of<GATE_UP>(wn, j) * 128 + rd[ks]);
+  };
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (nk > 1) issue(BK, 1);
+  read(0, 0, 0);
+  for (int s = 0; s < nk; ++s) {
+#pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[4], bfr[4];
+      const int cur = ks & 1;
+      if (ks < 3) {
+        read(s, ks + 1, cur ^ 1);
+      } else if (s + 1 < nk) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage s+1 landed (this wave)
+        __syncthreads();                     // all waves: s+1 landed, stage s fully read
+        read(s + 1, 0, 0);
+        if (s + 2 < nk) issue((s + 2) * BK, s & 1);
+      }
 #pragma unroll
       for (int i = 0; i < ACT; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + rd[ks]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + b_row_of<GATE_UP>(wn, j) * 128 + rd[ks]);
-#pragma unroll
-      for (int i = 0; i < ACT; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[cur][i], fb[cur][j], acc[i][j]);
     }
   }
 }
