@@ -9,16 +9,16 @@
 //    32x32x16 tiles (256 fp32 accumulators per lane), so every 16-byte LDS
 //    read feeds four MFMAs.
 //  - Operands go HBM/L2 -> LDS with buffer_load ... lds (no registers, no
-//    ds_write), double-buffered: the loads of stage s+1 fly while stage s is
-//    multiplied.  Out-of-range buffer offsets read as zero, which handles
+//    ds_write), double-buffered, and a wave's loads of a stage are spread
+//    over three MFMA substeps (see k_loop).  Out-of-range buffer offsets read as zero, which handles
 //    padding rows, gathered rows of -1 and N/K tails with no branches.
 //  - LDS rows are 128 B (64 bf16 of K); the eight 16-byte chunks of row r are
 //    stored XOR-swizzled by (r & 7) ^ ((r >> 3) & 1), which keeps both 8- and
 //    16-lane phases of the b128 operand reads on distinct banks.
-//  - Tiles are ordered in super-tiles of 4 m-tiles x 8 n-tiles and the block
-//    index is remapped so that each XCD (the hardware deals workgroups to the
-//    8 XCDs round-robin) walks a contiguous run of super-tiles: the 32
-//    workgroups an XCD runs together share their A and B tiles in its L2.
+//  - The valid tiles are split into 8 equal runs, one per XCD (the hardware
+//    deals workgroups to the 8 XCDs round-robin), each walked in blocks of
+//    4 m-tiles x 8 n-tiles, so the workgroups an XCD runs together share
+//    their A and B tiles in its L2 and no XCD gets more tiles than another.
 //  - MFMA work of 32-row sub-tiles that hold only padding rows is skipped.
 #include "device.hpp"
 #include "launch.hpp"
@@ -50,10 +50,12 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 }
 
 // Main loop over K.  LDS holds two stages; registers hold two sets of operand
-// fragments.  While the MFMAs of k-substep ks run, the fragments of ks+1 are
-// being read; the one barrier per stage sits before the last substep, after
-// its fragments are in registers, so the first reads of the next stage and
-// the loads of the stage after it overlap the last 16 MFMAs.
+// fragments (the reads of k-substep ks+1 fly while the 16 MFMAs of ks run).
+// The address unit is the scarce resource (one 1-KB load every ~20 cycles per
+// CU), so the 16 loads a wave issues per stage are spread over three
+// substeps instead of one burst: loads of stage s+1 go out in three groups,
+// right after barrier s-1 (during substep 3 of stage s-1) and during substeps
+// 0 and 1 of stage s; the barrier before substep 3 of stage s needs them all.
 // ACT = active 32-row A sub-tiles of this wave.
 template <bool GATE_UP, int ACT, class Issue>
 __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, int lane,
@@ -75,43 +77,71 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
     for (int j = 0; j < 4; ++j)
       fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + b_row_of<GATE_UP>(wn, j) * 128 + rd[ks]);
   };
+  auto mma = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < ACT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
+  };
 
-  issue(0, 0);
+  issue(0, 0, 0, 8);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (nk > 1) issue(BK, 1);
+  if (nk > 1) issue(1, 1, 0, 3);
   read(0, 0, 0);
-  for (int s = 0; s < nk; ++s) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int cur = ks & 1;
-      if (ks < 3) {
-        read(s, ks + 1, cur ^ 1);
-      } else if (s + 1 < nk) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage s+1 landed (this wave)
-        __syncthreads();                     // all waves: s+1 landed, stage s fully read
-        read(s + 1, 0, 0);
-        if (s + 2 < nk) issue((s + 2) * BK, s & 1);
-      }
-#pragma unroll
-      for (int i = 0; i < ACT; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[cur][i], fb[cur][j], acc[i][j]);
-    }
+  for (int s = 0; s + 1 < nk; ++s) {
+    const int nxt = s + 2 < nk ? s + 2 : nk - 1;  // past the end: a harmless reload
+    read(s, 1, 1);
+    issue(s + 1, (s + 1) & 1, 3, 6);
+    mma(0);
+    read(s, 2, 0);
+    issue(s + 1, (s + 1) & 1, 6, 8);
+    mma(1);
+    read(s, 3, 1);
+    mma(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage s+1 landed (this wave)
+    __syncthreads();                     // all waves: s+1 landed, stage s fully read
+    read(s + 1, 0, 0);
+    issue(nxt, s & 1, 0, 3);
+    mma(1);
   }
+  // last stage: no loads, no barrier
+  read(nk - 1, 1, 1);
+  mma(0);
+  read(nk - 1, 2, 0);
+  mma(1);
+  read(nk - 1, 3, 1);
+  mma(0);
+  mma(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be writing LDS at exit
 }
 
 template <bool GATE_UP>
 __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   // ---------------------------------------------------------------- schedule
+  // The V = m_tiles x n_tiles valid tiles (m_tiles is known on the device
+  // only) are cut into 8 equal runs, one per XCD: the hardware deals
+  // workgroup b to XCD b % 8, so XCD x executes run x in order.  Inside a run,
+  // tiles go in columns of NS n-tiles, and in each column in blocks of MS
+  // m-tiles x NS n-tiles, so the workgroups an XCD runs together share A and
+  // B tiles in its L2.
   const int64_t nt_n = p.n_tiles_n;
-  const int64_t m_blocks = (p.max_tiles + MS - 1) / MS;
-  const int64_t P = gridDim.x;  // multiple of 8
-  const int64_t L = (blockIdx.x % 8) * (P / 8) + blockIdx.x / 8;
-  const int64_t S = L / (MS * NS), w = L % (MS * NS);
-  const int64_t m_tile = (S % m_blocks) * MS + w % MS;
-  const int64_t n_tile = (S / m_blocks) * NS + w / MS;
-  if (m_tile >= p.n_tiles[0] || n_tile >= nt_n) return;
+  const int64_t mt = p.n_tiles[0];
+  const int64_t V = mt * nt_n;
+  const int64_t run = (V + 7) / 8;
+  const int64_t jb = blockIdx.x / 8;
+  if (jb >= run) return;
+  const int64_t L = (blockIdx.x % 8) * run + jb;
+  if (L >= V) return;
+  const int64_t colsz = mt * NS;
+  const int64_t sn = L / colsz;
+  const int64_t cw = min((int64_t)NS, nt_n - sn * NS);  // n-tiles in this column
+  const int64_t rem = L - sn * colsz;
+  const int64_t mb = rem / (MS * cw);
+  const int64_t mh = min((int64_t)MS, mt - mb * MS);      // m-tiles in this block
+  const int64_t inner = rem - mb * MS * cw;
+  const int64_t m_tile = mb * MS + inner % mh;
+  const int64_t n_tile = sn * NS + inner / mh;
   const int g = p.tile_group[m_tile];
   const bool shared = g >= p.E;
   const int N = shared ? p.N_shared : p.N_routed;
@@ -122,7 +152,8 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int64_t row0 = m_tile * BM;
   const int valid_rows = min(BM, (int)(p.group_count[g] - (row0 - p.group_padded[g])));
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // ------------------------------------------------------ operand sources
@@ -155,12 +186,15 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   }
   const int kcl = (lane & 7);  // chunk position within the 8 of a row, before the swizzle
 
-  auto issue = [&](int k0, int stage) {
-    char* base = lds + stage * kStageBytes;
-    // K tail: chunks at or past K read as zero (wave-uniform branch, last stage only)
+  // loads j in [j0, j1) of K-stage `stage` into LDS buffer `buf`; chunks at or
+  // past K (only in the last stage when K % 64 != 0) read as zero
+  auto issue = [&](int stage, int buf, int j0, int j1) {
+    const int k0 = stage * BK;
+    char* base = lds + buf * kStageBytes;
     const bool tail = k0 + BK > K;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      if (j < j0 || j >= j1) continue;
       uint32_t oa = offA[j], ob = offB[j];
       if (tail) {
         const int r = (wave * 8 + j) * 8 + sub;
@@ -246,9 +280,8 @@ hipError_t launch(bool gate_up, GroupedGemm g, hipStream_t s) {
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
   const int NB = gate_up ? BN / 2 : BN;
   g.n_tiles_n = (nmax + NB - 1) / NB;
-  const int64_t m_blocks = (g.max_tiles + MS - 1) / MS;
-  const int64_t n_blocks = (g.n_tiles_n + NS - 1) / NS;
-  const int64_t blocks = m_blocks * n_blocks * MS * NS;  // a multiple of 8
+  // enough workgroups for every XCD's run (see prefill_tile)
+  const int64_t blocks = (g.max_tiles * g.n_tiles_n + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
   if (gate_up)
     hipLaunchKernelGGL(moe_gemm_gate_up_prefill_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes,
