@@ -89,14 +89,30 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
   __syncthreads();
   if (nk > 1) issue(1, 1, 0, 3);
   read(0, 0, 0);
+  // Instruction order of one substep: the fragment reads of the next substep
+  // first, then one load per two MFMAs, so no wave stalls on a full address
+  // FIFO while its MFMA pipe idles.
+  auto pattern = [&](int nvmem) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads first
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      if (q < nvmem) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);     // the rest
+  };
   for (int s = 0; s + 1 < nk; ++s) {
     const int nxt = s + 2 < nk ? s + 2 : nk - 1;  // past the end: a harmless reload
     read(s, 1, 1);
     issue(s + 1, (s + 1) & 1, 3, 6);
     mma(0);
+    pattern(6);
     read(s, 2, 0);
     issue(s + 1, (s + 1) & 1, 6, 8);
     mma(1);
+    pattern(4);
     read(s, 3, 1);
     mma(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage s+1 landed (this wave)
@@ -104,6 +120,7 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
     read(s + 1, 0, 0);
     issue(nxt, s & 1, 0, 3);
     mma(1);
+    pattern(6);
   }
   // last stage: no loads, no barrier
   read(nk - 1, 1, 1);
