@@ -14,8 +14,8 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "align.hip", "gemm.hip", "gemm_prefill.hip", "combine.hip", "api.cpp",
-           "plan.cpp"]
+SOURCES = ["router.hip", "align.hip", "gemm_prefill.hip", "gemm_decode.hip", "combine.hip",
+           "api.cpp", "plan.cpp"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

@@ -70,7 +70,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   gu.group_count = counts;
   gu.group_padded = padded;
   gu.a_bytes = P.T * P.D * 2;
-  e = P.BM == 256 ? launch_gemm_gate_up_prefill(gu, s) : launch_gemm_gate_up(gu, s);
+  e = P.BM == 256 ? launch_gemm_gate_up_prefill(gu, s) : launch_gemm_gate_up_decode(gu, s);
   if (e == hipSuccess) e = mk.mark(3, s);
   if (e != hipSuccess) return hip_fail(e);
 
@@ -87,7 +87,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   dn.C = Yp;
   dn.ldc = P.D;
   dn.a_bytes = P.cap_rows * P.ldh * 2;
-  e = P.BM == 256 ? launch_gemm_down_prefill(dn, s) : launch_gemm_down(dn, s);
+  e = P.BM == 256 ? launch_gemm_down_prefill(dn, s) : launch_gemm_down_decode(dn, s);
   if (e == hipSuccess) e = mk.mark(4, s);
   if (e != hipSuccess) return hip_fail(e);
 

@@ -1,6 +1,6 @@
 // Prefill-sized grouped GEMMs (many rows per expert): 256 x 256 x 64 tiles.
 //
-// Same operation as the generic kernels in gemm.hip (SwiGLU expert FFN of the
+// Same operation as the decode kernels in gemm_decode.hip (SwiGLU expert FFN of the
 // glossary "MoE (Mixture of Experts - Mezcla de Expertos)", section 3 step 3;
 // packed [E, 2F, D] gate/up tensor of "Transformers v5 El Secreto Detrás de
 // los Modelos MoE Más Rápidos", section "La Solución: WeightConverter"), laid

@@ -36,12 +36,12 @@ struct GroupedGemm {
   int64_t n_tiles_n;            // set by the launcher
 };
 
-// Generic tiles (any BM the plan picks below the prefill size).
-hipError_t launch_gemm_gate_up(const GroupedGemm& g, hipStream_t s);
-hipError_t launch_gemm_down(const GroupedGemm& g, hipStream_t s);
 // 256 x 256 x 64 tiles for BM = 256 (prefill-sized groups).
 hipError_t launch_gemm_gate_up_prefill(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_gemm_down_prefill(const GroupedGemm& g, hipStream_t s);
+// Weight-streaming tiles for BM = 16 or 32 (decode-sized groups).
+hipError_t launch_gemm_gate_up_decode(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_gemm_down_decode(const GroupedGemm& g, hipStream_t s);
 
 // y[t] = sum_j w[t,j] * Yp[row_of[t*k+j]] (+ Yp[shared_base + t]) in fixed order.
 hipError_t launch_combine(const float* Yp, const int32_t* row_of, const float* wts,

@@ -27,8 +27,13 @@ int check_shape(const moe_shape* s) {
   return MOE_OK;
 }
 
+// Rows per expert decide the kernel family: a few rows per expert stream the
+// weights (16- or 32-row tiles), many rows per expert are MFMA-bound
+// (256-row tiles).
 int choose_block_m(const moe_shape* s) {
-  (void)s;
+  const int64_t rows = (int64_t)s->T * s->k;
+  if (rows <= (int64_t)20 * s->E) return 16;
+  if (rows <= (int64_t)48 * s->E) return 32;
   return 256;
 }
 
