@@ -77,6 +77,8 @@ def main():
     ap.add_argument("--T", type=int, default=None, help="token count override (decode sweeps)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph (removes host launch gaps)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="run one plain device copy of this many GiB first (a known-size kernel "
                          "for calibrating rocprofv3 byte counters)")
@@ -136,12 +138,28 @@ def main():
         moe.moe_forward(q.x, q.w_g, q.w_gate_up, q.w_down, s.k, q.router_bias, q.ws_gate_up,
                         q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws)
 
+    run = step
+    if args.graph:
+        for i in range(2 * len(sets)):  # compile-time state (kernel attributes) before capture
+            step(i)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(len(sets)):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(i)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+
+        def run(i):
+            graphs[i % len(graphs)].replay()
+
     for i in range(args.warmup):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
@@ -167,7 +185,9 @@ def main():
     layer_bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9) else "hbm"
 
     gu_ms = per_kernel["moe_gemm_gate_up"]
-    kernel_src = os.path.join(ROOT, "sparse_mixture_experts_prefix_amd", "csrc", "gemm.hip")
+    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias)
+    gemm_file = "gemm_prefill.hip" if moe.moe_block_m(shape) == 256 else "gemm_decode.hip"
+    kernel_src = os.path.join(ROOT, "sparse_mixture_experts_prefix_amd", "csrc", gemm_file)
     traffic = _traffic_from_profile(wl.name, kernel_src)
     if layer_bound == "mfma":
         achieved = W.gate_up_flops(s) / (gu_ms * 1e-3) / 1e12
@@ -198,7 +218,7 @@ def main():
         "data": "synthetic (seeded counter-based normal draws: x ~ N(0,1), weights ~ N(0,0.02), bf16)",
         "config": {"workload": wl.name, "T": s.T, "D": s.D, "E": s.E, "k": s.k, "d_ff": s.F,
                    "shared_d_ff": s.Fs, "router_bias": bool(s.router_bias),
-                   "weight_copies_rotated": n_copies},
+                   "weight_copies_rotated": n_copies, "hip_graph": bool(args.graph)},
         "roofline": roof,
         "layer": {"bound": layer_bound, "algorithmic_tflop": round(flops / 1e12, 4),
                   "algorithmic_gb": round(nbytes / 1e9, 4), "ideal_ms": round(t_ideal * 1e3, 4),

@@ -26,7 +26,6 @@ namespace moe {
 namespace {
 
 constexpr uint32_t kOob = 0x80000000u;
-constexpr int kWaves = 4;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -37,11 +36,11 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
 }
 
-template <bool GATE_UP, int MT, int NG>
+template <bool GATE_UP, int MT, int NG, int kWaves, int kUnroll>
 __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
   constexpr int BMD = 16 * MT;
   constexpr int NOUT = GATE_UP ? NG / 2 * 16 : NG * 16;  // output columns per tile
-  __shared__ f32x4 red[kWaves - 1][MT][NG][64];
+  __shared__ f32x4 red[kWaves > 1 ? kWaves - 1 : 1][MT][NG][64];
 
   const int64_t bid = blockIdx.x;
   const int64_t n_tile = bid % p.n_tiles_n;
@@ -101,7 +100,7 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
 #pragma unroll
     for (int j = 0; j < NG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- K loop: 64-wide chunks q = wave, wave + 4, ...; two chunks per trip
+  // ---- K loop: 64-wide chunks q = wave, wave + kWaves, ...; kUnroll chunks per trip
   const int nq = (K + 63) / 64;
   auto load_chunk = [&](int q, u32x4 (&a)[MT][2], u32x4 (&b)[NG][2]) {
     const int k0 = q * 64;
@@ -130,33 +129,36 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
           acc[i][j] = mfma16(as_bf16x8(a[i][h]), as_bf16x8(b[j][h]), acc[i][j]);
   };
   int q = wave;
-  for (; q + kWaves < nq; q += 2 * kWaves) {
-    u32x4 a0[MT][2], b0[NG][2], a1[MT][2], b1[NG][2];
-    load_chunk(q, a0, b0);
-    load_chunk(q + kWaves, a1, b1);
-    mma_chunk(a0, b0);
-    mma_chunk(a1, b1);
+  for (; q + (kUnroll - 1) * kWaves < nq; q += kUnroll * kWaves) {
+    u32x4 a[kUnroll][MT][2], b[kUnroll][NG][2];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) load_chunk(q + u * kWaves, a[u], b[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) mma_chunk(a[u], b[u]);
   }
-  if (q < nq) {
+  for (; q < nq; q += kWaves) {
     u32x4 a0[MT][2], b0[NG][2];
     load_chunk(q, a0, b0);
     mma_chunk(a0, b0);
   }
 
-  // ---- fixed-order reduction over the 4 waves: ((w0 + w1) + w2) + w3
-  if (wave > 0) {
+  // ---- fixed-order reduction over the waves: (((w0 + w1) + w2) + ...)
+  if (kWaves > 1) {
+    if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < NG; ++j) red[wave - 1][i][j][lane] = acc[i][j];
+        for (int j = 0; j < NG; ++j) red[wave - 1][i][j][lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < kWaves - 1; ++w)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NG; ++j) acc[i][j] += red[w][i][j][lane];
   }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NG; ++j)
-      acc[i][j] = ((acc[i][j] + red[0][i][j][lane]) + red[1][i][j][lane]) + red[2][i][j][lane];
 
   // ---- epilogue: lane (c, gq) holds rows 4*gq + r, column c of each 16x16 tile
 #pragma unroll
@@ -183,28 +185,34 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
   }
 }
 
+// 16-row column groups per tile (gate/up: half gate, half up), waves splitting
+// K, and 64-wide K-chunks whose loads are in flight together per wave.
+// Measured on the gpt-oss-shaped decode layer: 32-64 output columns, 4 waves.
+constexpr int kNgGateUp = 4, kNgDown = 4, kKw = 4, kUnr = 2;
+
 template <int MT>
-__global__ __launch_bounds__(256) void moe_gemm_gate_up_decode_kernel(GroupedGemm p) {
-  decode_tile<true, MT, 4>(p);
+__global__ __launch_bounds__(kKw * 64) void moe_gemm_gate_up_decode_kernel(GroupedGemm p) {
+  decode_tile<true, MT, kNgGateUp, kKw, kUnr>(p);
 }
 
 template <int MT>
-__global__ __launch_bounds__(256) void moe_gemm_down_decode_kernel(GroupedGemm p) {
-  decode_tile<false, MT, 4>(p);
+__global__ __launch_bounds__(kKw * 64) void moe_gemm_down_decode_kernel(GroupedGemm p) {
+  decode_tile<false, MT, kNgDown, kKw, kUnr>(p);
 }
 
 template <int MT>
 hipError_t launch_mt(bool gate_up, GroupedGemm g, hipStream_t s) {
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
-  const int nout = gate_up ? 32 : 64;
+  const int nout = gate_up ? kNgGateUp / 2 * 16 : kNgDown * 16;
   g.n_tiles_n = (nmax + nout - 1) / nout;
   const int64_t blocks = g.max_tiles * g.n_tiles_n;
   if (blocks == 0) return hipSuccess;
   if (gate_up)
-    hipLaunchKernelGGL(moe_gemm_gate_up_decode_kernel<MT>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       g);
+    hipLaunchKernelGGL(moe_gemm_gate_up_decode_kernel<MT>, dim3((unsigned)blocks), dim3(kKw * 64), 0,
+                       s, g);
   else
-    hipLaunchKernelGGL(moe_gemm_down_decode_kernel<MT>, dim3((unsigned)blocks), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(moe_gemm_down_decode_kernel<MT>, dim3((unsigned)blocks), dim3(kKw * 64), 0, s,
+                       g);
   return hipGetLastError();
 }
 
