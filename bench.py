@@ -29,18 +29,25 @@ def _log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def _traffic_from_profile(workload, kernel_src):
+def _kernel_sources_sha(gemm_file):
+    """sha256 over the sources that make up the gate/up kernel."""
+    h = hashlib.sha256()
+    for f in (gemm_file, "device.hpp", "launch.hpp"):
+        h.update(open(os.path.join(ROOT, "sparse_mixture_experts_prefix_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def _traffic_from_profile(workload, T, sha):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
     PMC summary, or None when there is none or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", "gemm_gate_up_%s_pmc.md" % workload)
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_%s_T%d_pmc.md" % (workload, T))
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_sha or not m_b:
         return None
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
     return float(m_b.group(1)) if sha == m_sha.group(1) else None
 
 
@@ -187,8 +194,7 @@ def main():
     gu_ms = per_kernel["moe_gemm_gate_up"]
     shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias)
     gemm_file = "gemm_prefill.hip" if moe.moe_block_m(shape) == 256 else "gemm_decode.hip"
-    kernel_src = os.path.join(ROOT, "sparse_mixture_experts_prefix_amd", "csrc", gemm_file)
-    traffic = _traffic_from_profile(wl.name, kernel_src)
+    traffic = _traffic_from_profile(wl.name, s.T, _kernel_sources_sha(gemm_file))
     if layer_bound == "mfma":
         achieved = W.gate_up_flops(s) / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

@@ -56,6 +56,8 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 // substeps instead of one burst: loads of stage s+1 go out in three groups,
 // right after barrier s-1 (during substep 3 of stage s-1) and during substeps
 // 0 and 1 of stage s; the barrier before substep 3 of stage s needs them all.
+// The weight rows go out in the first groups: their misses travel to HBM and
+// need the longest time in flight.
 // ACT = active 32-row A sub-tiles of this wave.
 template <bool GATE_UP, int ACT, class Issue>
 __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, int lane,
@@ -84,10 +86,10 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
   };
 
-  issue(0, 0, 0, 8);
+  issue(0, 0, 0, 16);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (nk > 1) issue(1, 1, 0, 3);
+  if (nk > 1) issue(1, 1, 0, 6);
   read(0, 0, 0);
   // Instruction order of one substep: the fragment reads of the next substep
   // first, then one load per two MFMAs, so no wave stalls on a full address
@@ -106,11 +108,11 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
   for (int s = 0; s + 1 < nk; ++s) {
     const int nxt = s + 2 < nk ? s + 2 : nk - 1;  // past the end: a harmless reload
     read(s, 1, 1);
-    issue(s + 1, (s + 1) & 1, 3, 6);
+    issue(s + 1, (s + 1) & 1, 6, 12);
     mma(0);
     pattern(6);
     read(s, 2, 0);
-    issue(s + 1, (s + 1) & 1, 6, 8);
+    issue(s + 1, (s + 1) & 1, 12, 16);
     mma(1);
     pattern(4);
     read(s, 3, 1);
@@ -118,7 +120,7 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage s+1 landed (this wave)
     __syncthreads();                     // all waves: s+1 landed, stage s fully read
     read(s + 1, 0, 0);
-    issue(nxt, s & 1, 0, 3);
+    issue(nxt, s & 1, 0, 6);
     mma(1);
     pattern(6);
   }
@@ -203,25 +205,27 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   }
   const int kcl = (lane & 7);  // chunk position within the 8 of a row, before the swizzle
 
-  // loads j in [j0, j1) of K-stage `stage` into LDS buffer `buf`; chunks at or
-  // past K (only in the last stage when K % 64 != 0) read as zero
-  auto issue = [&](int stage, int buf, int j0, int j1) {
+  // loads q in [q0, q1) of K-stage `stage` into LDS buffer `buf`: q 0..7 are
+  // B rows (expert weights, mostly HBM misses, so they go out first), q 8..15
+  // A rows (activations, mostly cache hits).  Chunks at or past K (only in the
+  // last stage when K % 64 != 0) read as zero.
+  auto issue = [&](int stage, int buf, int q0, int q1) {
     const int k0 = stage * BK;
     char* base = lds + buf * kStageBytes;
     const bool tail = k0 + BK > K;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < j0 || j >= j1) continue;
-      uint32_t oa = offA[j], ob = offB[j];
+    for (int q = 0; q < 16; ++q) {
+      if (q < q0 || q >= q1) continue;
+      const bool isB = q < 8;
+      const int j = q & 7;
+      uint32_t o = isB ? offB[j] : offA[j];
       if (tail) {
         const int r = (wave * 8 + j) * 8 + sub;
         const int kc = kcl ^ swz(r);
-        if (k0 + kc * 8 >= K) oa = ob = kOob;
+        if (k0 + kc * 8 >= K) o = kOob;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(base + (wave * 8 + j) * 1024), 16,
-                                               oa, k0 * 2, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsB, (lds_void*)(base + BM * BK * 2 + (wave * 8 + j) * 1024), 16, ob, k0 * 2, 0, 0);
+      char* dst = base + (isB ? BM * BK * 2 : 0) + (wave * 8 + j) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA, (lds_void*)dst, 16, o, k0 * 2, 0, 0);
     }
   };
 
