@@ -21,6 +21,27 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
+// Compute units of the current device, capped at the split workspace size:
+// the prefill GEMMs balance their last round of tiles over this many
+// workgroups (one resident per CU).
+hipError_t split_ctas(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static int cached[64] = {0};
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) {
+    *out = cached[dev];
+    return hipSuccess;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int n = cus < moe::kSplitCtas ? cus : moe::kSplitCtas;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  *out = n;
+  return hipSuccess;
+}
+
 // Records events[i] on the stream when timing is requested.
 struct Marks {
   void* const* ev;
@@ -44,6 +65,12 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   uint16_t* H = at<uint16_t>(ws, P.off_h);
   float* Yp = at<float>(ws, P.off_yp);
   const int shared_rows = P.Fs > 0 ? (int)P.T : 0;
+  const bool prefill = P.BM == 256;
+  int ctas = 0;
+  if (prefill) {
+    hipError_t e0 = split_ctas(&ctas);
+    if (e0 != hipSuccess) return hip_fail(e0);
+  }
 
   hipError_t e = launch_align(ids, (int)P.T, (int)P.k, (int)P.E, P.BM, shared_rows, counts, offsets,
                               padded, sorted, row_of, row_token, tile_group, n_tiles, s);
@@ -64,12 +91,15 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   gu.tile_group = tile_group;
   gu.n_tiles = n_tiles;
   gu.max_tiles = P.max_tiles;
+  gu.min_tiles = (P.A + P.BM - 1) / P.BM + (P.Fs > 0 ? (P.T + P.BM - 1) / P.BM : 0);
   gu.C = H;
   gu.ldc = P.ldh;
   gu.BM = P.BM;
   gu.group_count = counts;
   gu.group_padded = padded;
   gu.a_bytes = P.T * P.D * 2;
+  gu.ctas = ctas;
+  gu.partial = prefill ? at<float>(ws, P.off_partial) : nullptr;
   e = P.BM == 256 ? launch_gemm_gate_up_prefill(gu, s) : launch_gemm_gate_up_decode(gu, s);
   if (e == hipSuccess) e = mk.mark(3, s);
   if (e != hipSuccess) return hip_fail(e);

@@ -30,6 +30,9 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kStageBytes = (BM + BN) * BK * 2;  // 64 KB: A then B
 constexpr int kLdsBytes = 2 * kStageBytes;       // double buffer
 constexpr int MS = 4, NS = 8;                    // super-tile: MS m-tiles x NS n-tiles
+constexpr int kMaxSplit = 8;                     // pieces per tile of the last round
+constexpr int kMinPieceStages = 4;               // K-stages per piece, at least
+constexpr int kSplitRounds = 4;                  // cut only when V < kSplitRounds * ctas
 constexpr uint32_t kOob = 0x80000000u;           // buffer offset that reads as zero
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -59,18 +62,18 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 // The weight rows go out in the first groups: their misses travel to HBM and
 // need the longest time in flight.
 // ACT = active 32-row A sub-tiles of this wave.
+// Stages s0 .. s0+n-1 (n >= 1); local stage i sits in LDS buffer i & 1.
 template <bool GATE_UP, int ACT, class Issue>
-__device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, int lane,
+__device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, int lane,
                                        Issue& issue, f32x16 (&acc)[4][4]) {
   const int lr = lane & 31, kh = lane >> 5;
   int rd[4];  // LDS byte offset of this lane's chunk inside a 32-row block, per k-substep
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) rd[ks] = (lr * 8 + ((2 * ks + kh) ^ swz(lr))) * 16;
-  const int nk = (K + BK - 1) / BK;
 
   bf16x8 fa[2][4], fb[2][4];
-  auto read = [&](int stage, int ks, int slot) {
-    const char* sa = lds + (stage & 1) * kStageBytes;
+  auto read = [&](int ls, int ks, int slot) {
+    const char* sa = lds + (ls & 1) * kStageBytes;
     const char* sb = sa + BM * BK * 2;
 #pragma unroll
     for (int i = 0; i < ACT; ++i)
@@ -86,10 +89,10 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
   };
 
-  issue(0, 0, 0, 16);
+  issue(s0, 0, 0, 16);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (nk > 1) issue(1, 1, 0, 6);
+  if (n > 1) issue(s0 + 1, 1, 0, 6);
   read(0, 0, 0);
   // Instruction order of one substep: the fragment reads of the next substep
   // first, then one load per two MFMAs, so no wave stalls on a full address
@@ -105,53 +108,74 @@ __device__ __forceinline__ void k_loop(const char* lds, int K, int wm, int wn, i
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);     // the rest
   };
-  for (int s = 0; s + 1 < nk; ++s) {
-    const int nxt = s + 2 < nk ? s + 2 : nk - 1;  // past the end: a harmless reload
-    read(s, 1, 1);
-    issue(s + 1, (s + 1) & 1, 6, 12);
+  for (int i = 0; i + 1 < n; ++i) {
+    const int nxt = i + 2 < n ? i + 2 : n - 1;  // past the end: a harmless reload
+    read(i, 1, 1);
+    issue(s0 + i + 1, (i + 1) & 1, 6, 12);
     mma(0);
     pattern(6);
-    read(s, 2, 0);
-    issue(s + 1, (s + 1) & 1, 12, 16);
+    read(i, 2, 0);
+    issue(s0 + i + 1, (i + 1) & 1, 12, 16);
     mma(1);
     pattern(4);
-    read(s, 3, 1);
+    read(i, 3, 1);
     mma(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage s+1 landed (this wave)
-    __syncthreads();                     // all waves: s+1 landed, stage s fully read
-    read(s + 1, 0, 0);
-    issue(nxt, s & 1, 0, 6);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage i+1 landed (this wave)
+    __syncthreads();                     // all waves: i+1 landed, stage i fully read
+    read(i + 1, 0, 0);
+    issue(s0 + nxt, i & 1, 0, 6);
     mma(1);
     pattern(6);
   }
   // last stage: no loads, no barrier
-  read(nk - 1, 1, 1);
+  read(n - 1, 1, 1);
   mma(0);
-  read(nk - 1, 2, 0);
+  read(n - 1, 2, 0);
   mma(1);
-  read(nk - 1, 3, 1);
+  read(n - 1, 3, 1);
   mma(0);
   mma(1);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be writing LDS at exit
 }
 
-template <bool GATE_UP>
-__device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
-  // ---------------------------------------------------------------- schedule
-  // The V = m_tiles x n_tiles valid tiles (m_tiles is known on the device
-  // only) are cut into 8 equal runs, one per XCD: the hardware deals
-  // workgroup b to XCD b % 8, so XCD x executes run x in order.  Inside a run,
-  // tiles go in columns of NS n-tiles, and in each column in blocks of MS
-  // m-tiles x NS n-tiles, so the workgroups an XCD runs together share A and
-  // B tiles in its L2.
-  const int64_t nt_n = p.n_tiles_n;
-  const int64_t mt = p.n_tiles[0];
-  const int64_t V = mt * nt_n;
-  const int64_t run = (V + 7) / 8;
-  const int64_t jb = blockIdx.x / 8;
-  if (jb >= run) return;
-  const int64_t L = (blockIdx.x % 8) * run + jb;
-  if (L >= V) return;
+// ------------------------------------------------------------------ schedule
+// V = m_tiles x n_tiles valid tiles (m_tiles is known on the device only).
+// When V is not a multiple of the `ctas` workgroups that run at once, the
+// last, partial round is balanced: its R tiles are each cut into S pieces
+// along K (R*S <= ctas).  Each piece stores its fp32 partial tile, and a
+// second kernel adds the S partials in K order and runs the epilogue.  Only
+// for a few rounds of tiles: with many rounds the hardware's dispatch of
+// tiles to CUs as they free up already evens out the end, and the partial
+// tiles would cost more than they save.
+struct Split {
+  int64_t V, R, n_dp;  // valid tiles, tiles cut in pieces (the last R), tiles run whole
+  int S;               // pieces per cut tile (1: no cut)
+};
+
+__device__ __forceinline__ Split split_of(const GroupedGemm& p) {
+  Split sp;
+  sp.V = (int64_t)p.n_tiles[0] * p.n_tiles_n;
+  sp.R = 0;
+  sp.S = 1;
+  if (p.ctas > 0 && sp.V % p.ctas && sp.V < (int64_t)kSplitRounds * p.ctas) {
+    const int64_t R = sp.V % p.ctas;
+    const int kmin = p.B_shared && p.K_shared < p.K_routed ? p.K_shared : p.K_routed;
+    const int64_t by_k = ((kmin + BK - 1) / BK) / kMinPieceStages;
+    const int64_t S = min(min((int64_t)kMaxSplit, p.ctas / R), by_k);
+    if (S >= 2) {
+      sp.R = R;
+      sp.S = (int)S;
+    }
+  }
+  sp.n_dp = sp.V - sp.R;
+  return sp;
+}
+
+// Logical tile L -> (m_tile, n_tile): columns of NS n-tiles, and in each
+// column blocks of MS m-tiles x NS n-tiles, so consecutive tiles share their
+// A and B tiles.
+__device__ __forceinline__ void tile_coords(int64_t L, int64_t mt, int64_t nt_n, int64_t& m_tile,
+                                            int64_t& n_tile) {
   const int64_t colsz = mt * NS;
   const int64_t sn = L / colsz;
   const int64_t cw = min((int64_t)NS, nt_n - sn * NS);  // n-tiles in this column
@@ -159,8 +183,35 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int64_t mb = rem / (MS * cw);
   const int64_t mh = min((int64_t)MS, mt - mb * MS);      // m-tiles in this block
   const int64_t inner = rem - mb * MS * cw;
-  const int64_t m_tile = mb * MS + inner % mh;
-  const int64_t n_tile = sn * NS + inner / mh;
+  m_tile = mb * MS + inner % mh;
+  n_tile = sn * NS + inner / mh;
+}
+
+template <bool GATE_UP>
+__device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
+  // The V - R whole tiles are cut into 8 equal runs, one per XCD: the
+  // hardware deals workgroup b to XCD b % 8, so XCD x executes run x in
+  // order and the workgroups an XCD runs together share A and B tiles in its
+  // L2.  The R*S pieces come after all of them.
+  const Split sp = split_of(p);
+  const int64_t run = (sp.n_dp + 7) / 8;
+  const int64_t b = blockIdx.x;
+  int64_t L;
+  int part = 0, piece_tile = 0;
+  if (b < 8 * run) {
+    L = (b % 8) * run + b / 8;
+    if (L >= sp.n_dp) return;
+  } else {
+    const int64_t q = b - 8 * run;
+    if (q >= sp.R * sp.S) return;
+    piece_tile = (int)(q % sp.R);
+    part = (int)(q / sp.R);
+    L = sp.n_dp + piece_tile;
+  }
+  const bool piece = L >= sp.n_dp;
+  const int S = sp.S;
+  int64_t m_tile, n_tile;
+  tile_coords(L, p.n_tiles[0], p.n_tiles_n, m_tile, n_tile);
   const int g = p.tile_group[m_tile];
   const bool shared = g >= p.E;
   const int N = shared ? p.N_shared : p.N_routed;
@@ -241,14 +292,41 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  const int nk = (K + BK - 1) / BK;
+  const int s0 = piece ? (int)((int64_t)part * nk / S) : 0;
+  const int s1 = piece ? (int)((int64_t)(part + 1) * nk / S) : nk;
   switch (act) {
-    case 4: k_loop<GATE_UP, 4>(lds, K, wm, wn, lane, issue, acc); break;
-    case 3: k_loop<GATE_UP, 3>(lds, K, wm, wn, lane, issue, acc); break;
-    case 2: k_loop<GATE_UP, 2>(lds, K, wm, wn, lane, issue, acc); break;
-    case 1: k_loop<GATE_UP, 1>(lds, K, wm, wn, lane, issue, acc); break;
-    default: k_loop<GATE_UP, 0>(lds, K, wm, wn, lane, issue, acc); break;
+    case 4: k_loop<GATE_UP, 4>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
+    case 3: k_loop<GATE_UP, 3>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
+    case 2: k_loop<GATE_UP, 2>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
+    case 1: k_loop<GATE_UP, 1>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
+    default: k_loop<GATE_UP, 0>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
   }
   auto a_row = [&](int i) { return wm * 128 + i * 32; };
+
+  // ------------------------------------------------ pieces of a split tile
+  if (piece) {  // row-major fp32 partial tile, columns in LDS B-row order
+    // one per-lane base offset; every store adds a compile-time byte offset,
+    // so the 256 stores need no address registers
+    const __amdgpu_buffer_rsrc_t rsP = make_rsrc(
+        p.partial + (int64_t)(piece_tile * S + part) * (BM * BN), BM * BN * 4);
+    const uint32_t vbase = (uint32_t)(((a_row(0) + 4 * kh) * BN + b_row_of<GATE_UP>(wn, 0) + lr) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= act) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int off = ((i * 32 + 8 * (r >> 2) + (r & 3)) * BN +
+                           (b_row_of<GATE_UP>(0, j) - b_row_of<GATE_UP>(0, 0))) * 4;
+          const float v = acc[i][j][r];  // a scalar first: bit_cast of a vector element
+                                         // reinterprets the vector's first lane
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsP, vbase, off, 0);
+        }
+    }
+    return;
+  }
 
   // -------------------------------------------------------------- epilogue
 #pragma unroll
@@ -287,6 +365,70 @@ __global__ __launch_bounds__(256) void moe_gemm_down_prefill_kernel(GroupedGemm 
   prefill_tile<false>(p, lds);
 }
 
+// Finishes the cut tiles of the last round: block b owns rows
+// 16*(b % 16) .. +15 of cut tile b / 16, adds the S partials of each output
+// in K order (piece 0 first) and runs the GEMM's epilogue on the valid rows
+// (gate/up: SwiGLU into H; down: rows of Yp).  All S loads of an output are
+// issued before the sum, so the kernel streams instead of waiting on each.
+constexpr int kFixRows = 16;
+constexpr int kFixBlocksPerTile = BM / kFixRows;
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p) {
+  const Split sp = split_of(p);
+  const int64_t t = blockIdx.x / kFixBlocksPerTile;
+  if (t >= sp.R) return;
+  int64_t m_tile, n_tile;
+  tile_coords(sp.n_dp + t, p.n_tiles[0], p.n_tiles_n, m_tile, n_tile);
+  const int g = p.tile_group[m_tile];
+  const int N = g >= p.E ? p.N_shared : p.N_routed;
+  constexpr int NB = GATE_UP ? BN / 2 : BN;  // output columns of a tile
+  const int n0 = (int)n_tile * NB;
+  if (n0 >= N) return;
+  const int64_t row0 = m_tile * BM;
+  const int valid_rows = min(BM, (int)(p.group_count[g] - (row0 - p.group_padded[g])));
+  const int r0 = (blockIdx.x % kFixBlocksPerTile) * kFixRows;
+  const int r1 = min(r0 + kFixRows, valid_rows);
+  const float* P = p.partial + t * sp.S * (BM * BN);
+  constexpr int Q = NB / 4;  // float4 outputs per row
+  // sum of the S partials of the float4 at (row, col), in piece order
+  auto sum4 = [&](int row, int col) {
+    float4 v[kMaxSplit];
+#pragma unroll
+    for (int q = 0; q < kMaxSplit; ++q)
+      if (q < sp.S) v[q] = *reinterpret_cast<const float4*>(P + (int64_t)q * (BM * BN) + row * BN + col);
+    float4 a = v[0];
+#pragma unroll
+    for (int q = 1; q < kMaxSplit; ++q)
+      if (q < sp.S) {
+        a.x += v[q].x;
+        a.y += v[q].y;
+        a.z += v[q].z;
+        a.w += v[q].w;
+      }
+    return a;
+  };
+  for (int e = threadIdx.x; e < (r1 - r0) * Q; e += blockDim.x) {
+    const int row = r0 + e / Q, c = (e % Q) * 4;
+    if (GATE_UP) {
+      // LDS B-row order of a gate/up tile: gate columns 0..127, up columns 128..255
+      const float4 gt = sum4(row, c), up = sum4(row, BN / 2 + c);
+      const float h[4] = {silu(gt.x) * up.x, silu(gt.y) * up.y, silu(gt.z) * up.z, silu(gt.w) * up.w};
+      bf16_t* H = reinterpret_cast<bf16_t*>(p.C) + (row0 + row) * p.ldc + n0 + c;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (n0 + c + u < N) H[u] = f32_to_bf16(h[u]);
+    } else {
+      const float4 v = sum4(row, c);
+      float* Y = reinterpret_cast<float*>(p.C) + (row0 + row) * p.ldc + n0 + c;
+      const float y[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (n0 + c + u < N) Y[u] = y[u];
+    }
+  }
+}
+
 hipError_t launch(bool gate_up, GroupedGemm g, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
@@ -301,8 +443,17 @@ hipError_t launch(bool gate_up, GroupedGemm g, hipStream_t s) {
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
   const int NB = gate_up ? BN / 2 : BN;
   g.n_tiles_n = (nmax + NB - 1) / NB;
-  // enough workgroups for every XCD's run (see prefill_tile)
-  const int64_t blocks = (g.max_tiles * g.n_tiles_n + 7) / 8 * 8;
+  // No split (and no second kernel) when the device could never choose one:
+  // too many tiles for any routing, or K too short to cut.  With ids outside
+  // [0, E) the bound may overstate the tiles; that only forgoes the split.
+  {
+    const int kmin = g.B_shared && g.K_shared < g.K_routed ? g.K_shared : g.K_routed;
+    const bool short_k = ((kmin + BK - 1) / BK) / kMinPieceStages < 2;
+    if (short_k || g.min_tiles * g.n_tiles_n >= (int64_t)kSplitRounds * g.ctas) g.ctas = 0;
+  }
+  // enough workgroups for every XCD's run plus the pieces of a split last
+  // round (at most ctas of them; see prefill_tile)
+  const int64_t blocks = (g.max_tiles * g.n_tiles_n + 7) / 8 * 8 + (g.ctas > 0 ? g.ctas : 0);
   if (blocks == 0) return hipSuccess;
   if (gate_up)
     hipLaunchKernelGGL(moe_gemm_gate_up_prefill_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes,
@@ -310,6 +461,13 @@ hipError_t launch(bool gate_up, GroupedGemm g, hipStream_t s) {
   else
     hipLaunchKernelGGL(moe_gemm_down_prefill_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes, s,
                        g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.ctas <= 0) return e;
+  const unsigned fix_blocks = (unsigned)g.ctas * kFixBlocksPerTile;
+  if (gate_up)
+    hipLaunchKernelGGL(moe_gemm_split_fixup_kernel<true>, dim3(fix_blocks), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL(moe_gemm_split_fixup_kernel<false>, dim3(fix_blocks), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ struct GroupedGemm {
   const int32_t* tile_group;  // group of each BM-row tile
   const int32_t* n_tiles;     // device count of valid tiles
   int64_t max_tiles;          // host upper bound of n_tiles
+  int64_t min_tiles;          // host lower bound of n_tiles when every id is valid
   void* C;                    // gate/up: H bf16; down: Yp fp32
   int64_t ldc;                // elements
   int BM;
@@ -34,9 +35,14 @@ struct GroupedGemm {
   const int32_t* group_padded;  // first padded row of each group
   int64_t a_bytes;              // bytes addressable through A (gate/up: all of x)
   int64_t n_tiles_n;            // set by the launcher
+  // Prefill only: workgroups that run at once (0: never split a tile over K)
+  // and room for that many fp32 partial tiles of BM x BN (row-major)
+  int ctas;
+  float* partial;
 };
 
-// 256 x 256 x 64 tiles for BM = 256 (prefill-sized groups).
+// 256 x 256 x 64 tiles for BM = 256 (prefill-sized groups); each launches
+// the GEMM and, when ctas > 0, the kernel that finishes split tiles.
 hipError_t launch_gemm_gate_up_prefill(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_gemm_down_prefill(const GroupedGemm& g, hipStream_t s);
 // Weight-streaming tiles for BM = 16 or 32 (decode-sized groups).

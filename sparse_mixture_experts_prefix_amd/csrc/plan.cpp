@@ -70,6 +70,8 @@ int make_plan(const moe_shape* s, Plan* p) {
   p->off_tilegroup = take(sizeof(int32_t) * p->max_tiles);
   p->off_h = take(sizeof(uint16_t) * (size_t)p->cap_rows * p->ldh);
   p->off_yp = take(sizeof(float) * (size_t)p->cap_rows * p->D);
+  const bool split = p->BM == 256;  // only the 256-row kernels split tiles over K
+  p->off_partial = take(split ? sizeof(float) * kSplitCtas * kPartialTileFloats : 0);
   p->total = o;
   return MOE_OK;
 }

@@ -9,6 +9,11 @@
 
 namespace moe {
 
+// Workgroups the prefill GEMMs balance their last round over (one per CU,
+// at most this many), and so the number of partial tiles the workspace holds.
+constexpr int kSplitCtas = 256;
+constexpr int64_t kPartialTileFloats = 256 * 256;
+
 // Row-tile height of the grouped GEMMs and the per-call workspace layout.
 struct Plan {
   int64_t T, D, E, F, k, Fs;
@@ -20,7 +25,7 @@ struct Plan {
   int64_t ldh;        // row stride (elements) of the hidden activations H: max(F, Fs)
   // byte offsets inside the workspace
   size_t off_ids, off_w, off_counts, off_offsets, off_padded, off_ntiles, off_sorted, off_rowof,
-      off_rowtoken, off_tilegroup, off_h, off_yp, total;
+      off_rowtoken, off_tilegroup, off_h, off_yp, off_partial, total;
 };
 
 // Shape checks shared by every entry point (MOE_OK or an error code).

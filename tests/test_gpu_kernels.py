@@ -159,6 +159,51 @@ def test_layer_parity(T, D, E, k, F, Fs, bias):
     _layer_parity(W.make_inputs(s, seed=T + E))
 
 
+def _split(V, ctas, kmin):
+    """(R, S) of the prefill GEMMs' last-round split: R tiles cut in S pieces."""
+    if V % ctas == 0 or V >= 4 * ctas:
+        return 0, 1
+    R = V % ctas
+    S = min(8, ctas // R, ((kmin + 63) // 64) // 4)
+    return (R, S) if S >= 2 else (0, 1)
+
+
+@pytest.mark.parametrize("T,D,E,k,F,Fs", [
+    (512, 512, 8, 2, 512, 0),      # both GEMMs split (S = 2 at even expert loads)
+    (2048, 512, 8, 2, 2048, 0),    # down split up to eight ways
+    (1024, 512, 8, 2, 1024, 512),  # shared expert with a shorter K in the down GEMM
+    (600, 1024, 4, 1, 4096, 0),    # few tiles, long K
+])
+def test_layer_split_last_round(T, D, E, k, F, Fs):
+    """Tiles of a partial last round are cut along K, and the last piece to
+    arrive sums the partials: parity, bitwise repeatability, and that the
+    split really ran for these shapes."""
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs)
+    inp = W.make_inputs(s, seed=T + F)
+    shape = moe.make_shape(T, D, E, F, k, Fs)
+    assert moe.moe_block_m(shape) == 256
+    y1, ids, _ = _layer_parity(inp)
+    # again with a workspace full of 0xFF bytes: the arrival counters start at -1
+    # unless the call clears them, and the partial tiles hold NaNs
+    g = _gpu(inp)
+    ws = moe.alloc_workspace(shape, DEV)
+    ws.view(torch.uint8).fill_(0xFF)
+    y2 = moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, k, None, g.ws_gate_up, g.ws_down,
+                         workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1, y2.cpu().numpy())
+    counts = np.bincount(ids.ravel(), minlength=E)
+    mt = int(sum((c + 255) // 256 for c in counts)) + ((T + 255) // 256 if Fs else 0)
+    ctas = min(256, torch.cuda.get_device_properties(0).multi_processor_count)
+    fmax = max(F, Fs)
+    _, s_gu = _split(mt * ((fmax + 127) // 128), ctas, D)
+    _, s_dn = _split(mt * ((D + 255) // 256), ctas, min(F, Fs) if Fs else F)
+    if (T, F) == (2048, 2048) or (T, F) == (600, 4096):
+        assert s_dn >= 2  # the down GEMM is the one cut for these shapes
+    print("m-tiles %d: gate/up S=%d, down S=%d" % (mt, s_gu, s_dn))
+    assert max(s_gu, s_dn) >= 2
+
+
 def test_layer_E1_k1_dense_ffn():
     s = W.Shape(T=100, D=256, E=1, k=1, F=512)
     y, ids, w = _layer_parity(W.make_inputs(s, seed=1))
