@@ -9,9 +9,10 @@
 //    32x32x16 tiles (256 fp32 accumulators per lane), so every 16-byte LDS
 //    read feeds four MFMAs.
 //  - Operands go HBM/L2 -> LDS with buffer_load ... lds (no registers, no
-//    ds_write), double-buffered, and a wave's loads of a stage are spread
-//    over three MFMA substeps (see k_loop).  Out-of-range buffer offsets read as zero, which handles
-//    padding rows, gathered rows of -1 and N/K tails with no branches.
+//    ds_write); A is double- and B triple-buffered, and a wave's loads of a
+//    stage are spread evenly over the MFMA substeps (see k_loop).
+//    Out-of-range buffer offsets read as zero, which handles padding rows,
+//    gathered rows of -1 and N/K tails with no branches.
 //  - LDS rows are 128 B (64 bf16 of K); the eight 16-byte chunks of row r are
 //    stored XOR-swizzled by (r & 7) ^ ((r >> 3) & 1), which keeps both 8- and
 //    16-lane phases of the b128 operand reads on distinct banks.
@@ -20,6 +21,7 @@
 //    4 m-tiles x 8 n-tiles, so the workgroups an XCD runs together share
 //    their A and B tiles in its L2 and no XCD gets more tiles than another.
 //  - MFMA work of 32-row sub-tiles that hold only padding rows is skipped.
+//  - A short, partial last round of tiles is cut along K (see split_of).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -27,8 +29,9 @@ namespace moe {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kStageBytes = (BM + BN) * BK * 2;  // 64 KB: A then B
-constexpr int kLdsBytes = 2 * kStageBytes;       // double buffer
+constexpr int kABytes = BM * BK * 2;             // 32 KB: one K-stage of A
+constexpr int kBBytes = BN * BK * 2;             // 32 KB: one K-stage of B
+constexpr int kLdsBytes = 2 * kABytes + 3 * kBBytes;  // A double-, B triple-buffered: 160 KB
 constexpr int MS = 4, NS = 8;                    // super-tile: MS m-tiles x NS n-tiles
 constexpr int kMaxSplit = 8;                     // pieces per tile of the last round
 constexpr int kMinPieceStages = 4;               // K-stages per piece, at least
@@ -52,29 +55,34 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
   return wn * 128 + j * 32;
 }
 
-// Main loop over K.  LDS holds two stages; registers hold two sets of operand
-// fragments (the reads of k-substep ks+1 fly while the 16 MFMAs of ks run).
-// The address unit is the scarce resource (one 1-KB load every ~20 cycles per
-// CU), so the 16 loads a wave issues per stage are spread over three
-// substeps instead of one burst: loads of stage s+1 go out in three groups,
-// right after barrier s-1 (during substep 3 of stage s-1) and during substeps
-// 0 and 1 of stage s; the barrier before substep 3 of stage s needs them all.
-// The weight rows go out in the first groups: their misses travel to HBM and
-// need the longest time in flight.
-// ACT = active 32-row A sub-tiles of this wave.
-// Stages s0 .. s0+n-1 (n >= 1); local stage i sits in LDS buffer i & 1.
-template <bool GATE_UP, int ACT, class Issue>
+// Main loop over K.  LDS holds two K-stages of A and three of B (all 160 KB);
+// registers hold two sets of operand fragments (the reads of k-substep ks+1
+// fly while the 16 MFMAs of ks run).  Per stage a wave issues 16 loads, one
+// per four MFMAs, four in each substep, since the CU's address unit (about
+// one 1-KB load per ~20 cycles) stalls the in-order issue when loads come in
+// bursts:
+//  - after barrier i (stage i fully read) and in substep 0 of stage i+1: the
+//    A rows of stage i+2 (activations, mostly cache hits), into the A buffer
+//    stage i used;
+//  - in substeps 1 and 2 of stage i+1: the B rows of stage i+3 (expert
+//    weights, whose misses go to HBM), into the B buffer stage i used, a
+//    whole stage ahead of their use.
+// The barrier before substep 3 of stage i+1 waits for A(i+2) and B(i+2)
+// only (vmcnt(8): the eight B(i+3) loads issued after them may still fly).
+// Stages s0 .. s0+n-1 (n >= 1); ACT = active 32-row A sub-tiles of this wave.
+template <bool GATE_UP, int ACT, class IssueA, class IssueB>
 __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, int lane,
-                                       Issue& issue, f32x16 (&acc)[4][4]) {
+                                       IssueA& issue_a, IssueB& issue_b, f32x16 (&acc)[4][4]) {
   const int lr = lane & 31, kh = lane >> 5;
   int rd[4];  // LDS byte offset of this lane's chunk inside a 32-row block, per k-substep
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) rd[ks] = (lr * 8 + ((2 * ks + kh) ^ swz(lr))) * 16;
 
   bf16x8 fa[2][4], fb[2][4];
-  auto read = [&](int ls, int ks, int slot) {
-    const char* sa = lds + (ls & 1) * kStageBytes;
-    const char* sb = sa + BM * BK * 2;
+  // fragments of k-substep ks of local stage ls (B buffer bb) into register set `slot`
+  auto read = [&](int ls, int bb, int ks, int slot) {
+    const char* sa = lds + (ls & 1) * kABytes;
+    const char* sb = lds + 2 * kABytes + bb * kBBytes;
 #pragma unroll
     for (int i = 0; i < ACT; ++i)
       fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + rd[ks]);
@@ -88,51 +96,57 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
   };
+  // instruction order of one substep: the 8 fragment reads of the next
+  // substep first, then one load per four MFMAs
+  auto pattern = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // fragment reads
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+    }
+  };
 
-  issue(s0, 0, 0, 16);
+  issue_b(s0, 0, 0, 8);
+  issue_a(s0, 0, 0, 8);
+  if (n > 1) issue_b(s0 + 1, 1, 0, 8);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (n > 1) issue(s0 + 1, 1, 0, 6);
-  read(0, 0, 0);
-  // Instruction order of one substep: the fragment reads of the next substep
-  // first, then one load per two MFMAs, so no wave stalls on a full address
-  // FIFO while its MFMA pipe idles.
-  auto pattern = [&](int nvmem) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads first
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      if (q < nvmem) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);     // the rest
-  };
+  if (n > 1) issue_a(s0 + 1, 1, 0, 4);
+  read(0, 0, 0, 0);
+  int bcur = 0, b2 = 2;  // B buffers of stages i and i+2
   for (int i = 0; i + 1 < n; ++i) {
-    const int nxt = i + 2 < n ? i + 2 : n - 1;  // past the end: a harmless reload
-    read(i, 1, 1);
-    issue(s0 + i + 1, (i + 1) & 1, 6, 12);
+    const int a2 = i + 2 < n ? i + 2 : n - 1;  // past the end: harmless reloads
+    read(i, bcur, 1, 1);
+    issue_a(s0 + i + 1, (i + 1) & 1, 4, 8);
     mma(0);
-    pattern(6);
-    read(i, 2, 0);
-    issue(s0 + i + 1, (i + 1) & 1, 12, 16);
+    pattern();
+    read(i, bcur, 2, 0);
+    issue_b(s0 + a2, b2, 0, 4);
     mma(1);
-    pattern(4);
-    read(i, 3, 1);
+    pattern();
+    read(i, bcur, 3, 1);
+    issue_b(s0 + a2, b2, 4, 8);
     mma(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): stage i+1 landed (this wave)
-    __syncthreads();                     // all waves: i+1 landed, stage i fully read
-    read(i + 1, 0, 0);
-    issue(s0 + nxt, i & 1, 0, 6);
+    pattern();
+    // vmcnt(8): A(i+1) and B(i+1) landed, B(i+2) may still fly; lgkmcnt(0):
+    // this wave's reads of stage i are done.  A plain s_barrier, since the
+    // fence of __syncthreads would wait for every load.
+    __builtin_amdgcn_s_waitcnt(0x0078);
+    __builtin_amdgcn_s_barrier();
+    bcur = bcur == 2 ? 0 : bcur + 1;
+    b2 = b2 == 2 ? 0 : b2 + 1;
+    read(i + 1, bcur, 0, 0);
+    issue_a(s0 + a2, i & 1, 0, 4);
     mma(1);
-    pattern(6);
+    pattern();
   }
   // last stage: no loads, no barrier
-  read(n - 1, 1, 1);
+  read(n - 1, bcur, 1, 1);
   mma(0);
-  read(n - 1, 2, 0);
+  read(n - 1, bcur, 2, 0);
   mma(1);
-  read(n - 1, 3, 1);
+  read(n - 1, bcur, 3, 1);
   mma(0);
   mma(1);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be writing LDS at exit
@@ -256,29 +270,29 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   }
   const int kcl = (lane & 7);  // chunk position within the 8 of a row, before the swizzle
 
-  // loads q in [q0, q1) of K-stage `stage` into LDS buffer `buf`: q 0..7 are
-  // B rows (expert weights, mostly HBM misses, so they go out first), q 8..15
-  // A rows (activations, mostly cache hits).  Chunks at or past K (only in the
-  // last stage when K % 64 != 0) read as zero.
-  auto issue = [&](int stage, int buf, int q0, int q1) {
+  // loads j in [j0, j1) of the A (or B) rows of K-stage `stage` into A (or B)
+  // buffer `buf`; chunks at or past K (only in the last stage when
+  // K % 64 != 0) read as zero
+  auto issue = [&](bool isB, int stage, int buf, int j0, int j1) {
     const int k0 = stage * BK;
-    char* base = lds + buf * kStageBytes;
+    char* base = isB ? lds + 2 * kABytes + buf * kBBytes : lds + buf * kABytes;
     const bool tail = k0 + BK > K;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if (q < q0 || q >= q1) continue;
-      const bool isB = q < 8;
-      const int j = q & 7;
+    for (int j = 0; j < 8; ++j) {
+      if (j < j0 || j >= j1) continue;
       uint32_t o = isB ? offB[j] : offA[j];
       if (tail) {
         const int r = (wave * 8 + j) * 8 + sub;
         const int kc = kcl ^ swz(r);
         if (k0 + kc * 8 >= K) o = kOob;
       }
-      char* dst = base + (isB ? BM * BK * 2 : 0) + (wave * 8 + j) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA, (lds_void*)dst, 16, o, k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA,
+                                               (lds_void*)(base + (wave * 8 + j) * 1024), 16, o,
+                                               k0 * 2, 0, 0);
     }
   };
+  auto issue_a = [&](int stage, int buf, int j0, int j1) { issue(false, stage, buf, j0, j1); };
+  auto issue_b = [&](int stage, int buf, int j0, int j1) { issue(true, stage, buf, j0, j1); };
 
   // active 32-row sub-tiles of this wave (uniform): the K loop is compiled
   // once per count so no MFMA sits under a branch
@@ -296,11 +310,11 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int s0 = piece ? (int)((int64_t)part * nk / S) : 0;
   const int s1 = piece ? (int)((int64_t)(part + 1) * nk / S) : nk;
   switch (act) {
-    case 4: k_loop<GATE_UP, 4>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
-    case 3: k_loop<GATE_UP, 3>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
-    case 2: k_loop<GATE_UP, 2>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
-    case 1: k_loop<GATE_UP, 1>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
-    default: k_loop<GATE_UP, 0>(lds, s0, s1 - s0, wm, wn, lane, issue, acc); break;
+    case 4: k_loop<GATE_UP, 4>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 3: k_loop<GATE_UP, 3>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 2: k_loop<GATE_UP, 2>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 1: k_loop<GATE_UP, 1>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    default: k_loop<GATE_UP, 0>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
   }
   auto a_row = [&](int i) { return wm * 128 + i * 32; };
 
