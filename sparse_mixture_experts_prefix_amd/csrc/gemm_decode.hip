@@ -18,7 +18,10 @@
 //    full 128-byte line.  Weights go straight from HBM to registers (each
 //    byte is used once); loads of two chunks are in flight per wave.
 //  - Out-of-range buffer offsets read as zero: padding rows, rows past the
-//    group's count and K tails need no branches.
+//    group's count and K tails need no branches.  Weight rows of tiles that
+//    lie wholly in bounds are read with plain global loads instead (faster).
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -100,47 +103,65 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
 #pragma unroll
     for (int j = 0; j < NG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- K loop: 64-wide chunks q = wave, wave + kWaves, ...; kUnroll chunks per trip
+  // ---- K loop: 64-wide chunks q = wave, wave + kWaves, ...; kUnroll chunks per trip.
+  // A tile whose weight rows and K range are all in bounds (the usual case)
+  // reads the weights with plain global loads, which stream faster than
+  // bounds-checked buffer loads; a ragged tile uses the buffer loads, whose
+  // out-of-range offsets read as zero.
   const int nq = (K + 63) / 64;
-  auto load_chunk = [&](int q, u32x4 (&a)[MT][2], u32x4 (&b)[NG][2]) {
-    const int k0 = q * 64;
-    // K tail (K % 64 != 0): a lane's 32 bytes are all in or all out when K % 16 == 0;
-    // otherwise its two 16-byte halves are checked separately
-    const int kk = k0 + gq * 16;
-    const bool in0 = kk < K, in1 = kk + 8 < K;
+  const char* Bbytes = reinterpret_cast<const char*>(Bg);
+  auto run = [&](auto exact_tag) {
+    constexpr bool kExact = decltype(exact_tag)::value;
+    auto load_chunk = [&](int q, u32x4 (&a)[MT][2], u32x4 (&b)[NG][2]) {
+      const int k0 = q * 64;
+      // K tail (K % 64 != 0): a lane's 32 bytes are all in or all out when K % 16 == 0;
+      // otherwise its two 16-byte halves are checked separately
+      const int kk = k0 + gq * 16;
+      const bool in0 = kk < K, in1 = kk + 8 < K;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      a[i][0] = bload(rsA, in0 ? offA[i] : kOob, k0 * 2);
-      a[i][1] = bload(rsA, in1 ? offA[i] + 16 : kOob, k0 * 2);
+      for (int i = 0; i < MT; ++i) {
+        a[i][0] = bload(rsA, in0 ? offA[i] : kOob, k0 * 2);
+        a[i][1] = bload(rsA, in1 ? offA[i] + 16 : kOob, k0 * 2);
+      }
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        if constexpr (kExact) {
+          const char* pb = Bbytes + offB[j] + k0 * 2;
+          b[j][0] = *reinterpret_cast<const u32x4*>(pb);
+          b[j][1] = *reinterpret_cast<const u32x4*>(pb + 16);
+        } else {
+          b[j][0] = bload(rsB, in0 ? offB[j] : kOob, k0 * 2);
+          b[j][1] = bload(rsB, in1 ? offB[j] + 16 : kOob, k0 * 2);
+        }
+      }
+    };
+    auto mma_chunk = [&](const u32x4 (&a)[MT][2], const u32x4 (&b)[NG][2]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NG; ++j)
+            acc[i][j] = mfma16(as_bf16x8(a[i][h]), as_bf16x8(b[j][h]), acc[i][j]);
+    };
+    int q = wave;
+    for (; q + (kUnroll - 1) * kWaves < nq; q += kUnroll * kWaves) {
+      u32x4 a[kUnroll][MT][2], b[kUnroll][NG][2];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) load_chunk(q + u * kWaves, a[u], b[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) mma_chunk(a[u], b[u]);
     }
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      b[j][0] = bload(rsB, in0 ? offB[j] : kOob, k0 * 2);
-      b[j][1] = bload(rsB, in1 ? offB[j] + 16 : kOob, k0 * 2);
+    for (; q < nq; q += kWaves) {
+      u32x4 a0[MT][2], b0[NG][2];
+      load_chunk(q, a0, b0);
+      mma_chunk(a0, b0);
     }
   };
-  auto mma_chunk = [&](const u32x4 (&a)[MT][2], const u32x4 (&b)[NG][2]) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NG; ++j)
-          acc[i][j] = mfma16(as_bf16x8(a[i][h]), as_bf16x8(b[j][h]), acc[i][j]);
-  };
-  int q = wave;
-  for (; q + (kUnroll - 1) * kWaves < nq; q += kUnroll * kWaves) {
-    u32x4 a[kUnroll][MT][2], b[kUnroll][NG][2];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) load_chunk(q + u * kWaves, a[u], b[u]);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) mma_chunk(a[u], b[u]);
-  }
-  for (; q < nq; q += kWaves) {
-    u32x4 a0[MT][2], b0[NG][2];
-    load_chunk(q, a0, b0);
-    mma_chunk(a0, b0);
-  }
+  if (K % 64 == 0 && n0 + NOUT <= N)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // ---- fixed-order reduction over the waves: (((w0 + w1) + w2) + ...)
   if (kWaves > 1) {
