@@ -11,7 +11,8 @@
 //  - A workgroup owns one m-tile (16*MT rows of one expert) and 16*NG weight
 //    rows (gate/up: NG/2 groups of gate rows with the matching up rows);
 //    its 4 waves split K and their partial sums are added in LDS in a fixed
-//    order (deterministic).
+//    order (deterministic).  All loads of a trip are issued before its
+//    MFMAs (a scheduling barrier), so each wave keeps two chunks in flight.
 //  - MFMA 16x16x32 bf16.  The K order inside a 64-wide chunk is permuted the
 //    same way for A and B: lane (col c, group g) holds bytes [32g, 32g+32) of
 //    its row for two consecutive MFMAs, so the four lanes of a row read one
@@ -149,12 +150,16 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
       u32x4 a[kUnroll][MT][2], b[kUnroll][NG][2];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) load_chunk(q + u * kWaves, a[u], b[u]);
+      // every load of the trip goes out before the first MFMA; left alone,
+      // the compiler sinks loads to their uses and keeps only ~6 in flight
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) mma_chunk(a[u], b[u]);
     }
     for (; q < nq; q += kWaves) {
       u32x4 a0[MT][2], b0[NG][2];
       load_chunk(q, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
       mma_chunk(a0, b0);
     }
   };

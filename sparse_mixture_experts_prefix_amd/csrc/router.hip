@@ -43,7 +43,9 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
   constexpr int EP = 16 * NCT;
   constexpr int kWaves = waves_for<NCT>();
   constexpr int kLevels = kWaves == 16 ? 4 : 3;
-  constexpr int UNR = NCT <= 4 ? 2 : 1;  // chunks whose loads are in flight together
+  // chunks whose loads are in flight together (the same chunk order per wave
+  // for every UNR, so the sums do not depend on it)
+  constexpr int UNR = NCT <= 2 ? 6 : (NCT <= 4 ? 3 : 1);
   extern __shared__ float part[];        // [kWaves/2][kTok][EP + 1]: partials, then logits
   auto slot = [&](int s, int row, int col) -> float& {
     return part[(s * kTok + row) * (EP + 1) + col];
@@ -76,6 +78,7 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
           bv[u][c] = (e < E && kin) ? ld16(wg + (int64_t)e * D + kk) : u32x4{0u, 0u, 0u, 0u};
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // all loads of the trip before the MFMAs
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
 #pragma unroll
