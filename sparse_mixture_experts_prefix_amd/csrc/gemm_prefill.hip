@@ -343,6 +343,41 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   }
 
   // -------------------------------------------------------------- epilogue
+  if (GATE_UP) {
+    // SwiGLU in registers; the 256 x 128 fp32 result goes through the (now
+    // idle) LDS so that each lane writes 16 bytes of H at a time, and padding
+    // rows are not written.  Rows are padded to 136 floats so the two row
+    // groups of a 64-lane write land on different banks.
+    constexpr int kHs = BN / 2 + 8;
+    float* hs = reinterpret_cast<float*>(lds);
+    __syncthreads();  // every wave is done reading the K stages
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= act) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          hs[row * kHs + wn * 64 + j * 32 + lr] = silu(acc[i][j][r]) * acc[i][j + 2][r];
+      }
+    }
+    __syncthreads();
+    bf16_t* H = reinterpret_cast<bf16_t*>(p.C);
+    const int ncol = min(BN / 2, N - n0);  // a multiple of 8 (N % 8 == 0)
+    for (int e = tid; e < valid_rows * (BN / 16); e += 256) {
+      const int row = e / (BN / 16), c8 = (e % (BN / 16)) * 8;
+      if (c8 >= ncol) continue;
+      const float4 v0 = *reinterpret_cast<const float4*>(hs + row * kHs + c8);
+      const float4 v1 = *reinterpret_cast<const float4*>(hs + row * kHs + c8 + 4);
+      auto pack = [](float a, float b) {
+        return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+      };
+      const u32x4 w = {pack(v0.x, v0.y), pack(v0.z, v0.w), pack(v1.x, v1.y), pack(v1.z, v1.w)};
+      st16(H + (row0 + row) * p.ldc + n0 + c8, w);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i >= act) continue;
@@ -350,20 +385,11 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     for (int r = 0; r < 16; ++r) {
       const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
       const int64_t grow = row0 + row;
-      if (GATE_UP) {
-        bf16_t* H = reinterpret_cast<bf16_t*>(p.C);
+      float* Y = reinterpret_cast<float*>(p.C);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int f = n0 + wn * 64 + j * 32 + lr;
-          if (f < N) H[grow * p.ldc + f] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + 2][r]);
-        }
-      } else {
-        float* Y = reinterpret_cast<float*>(p.C);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 128 + j * 32 + lr;
-          if (n < N) Y[grow * p.ldc + n] = acc[i][j][r];
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 128 + j * 32 + lr;
+        if (n < N) Y[grow * p.ldc + n] = acc[i][j][r];
       }
     }
   }
