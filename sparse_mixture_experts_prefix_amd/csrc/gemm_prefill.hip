@@ -57,10 +57,9 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 
 // Main loop over K.  LDS holds two K-stages of A and three of B (all 160 KB);
 // registers hold two sets of operand fragments (the reads of k-substep ks+1
-// fly while the 16 MFMAs of ks run).  Per stage a wave issues 16 loads, one
-// per four MFMAs, four in each substep, since the CU's address unit (about
-// one 1-KB load per ~20 cycles) stalls the in-order issue when loads come in
-// bursts:
+// fly while the 16 MFMAs of ks run).  Per stage a wave issues 16 loads, four
+// in each substep, since the CU's address unit (about one 1-KB load per ~20
+// cycles) stalls the in-order issue when loads come in bursts:
 //  - after barrier i (stage i fully read) and in substep 0 of stage i+1: the
 //    A rows of stage i+2 (activations, mostly cache hits), into the A buffer
 //    stage i used;
@@ -96,15 +95,25 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
   };
-  // instruction order of one substep: the 8 fragment reads of the next
-  // substep first, then one load per four MFMAs
+  // instruction order of one substep (16 MFMAs): one MFMA, then the 8
+  // fragment reads of the next substep each behind one MFMA (a burst of reads
+  // queues behind the other waves' reads and the loads' LDS writes), then the
+  // four loads, one per two MFMAs.  Measured 3-4% faster than reads first.
   auto pattern = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one fragment read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // one load
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
 
   issue_b(s0, 0, 0, 8);
