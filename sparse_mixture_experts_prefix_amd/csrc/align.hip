@@ -14,6 +14,7 @@
 // order by assignment index and bitwise reproducible.
 #include "device.hpp"
 #include "launch.hpp"
+#include "topk.hpp"  // ranks_before
 
 namespace moe {
 namespace {
@@ -26,8 +27,9 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ padded,
     int32_t* __restrict__ sorted_assign, int32_t* __restrict__ row_of,
     int32_t* __restrict__ row_token, int32_t* __restrict__ tile_group,
-    int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ n_tiles, RouteFinish fin) {
   __shared__ int hist[258];
+  __shared__ int s_ids[kSmallRouteT * 8];
   __shared__ int s_off[258];
   __shared__ int s_pad[258];
   __shared__ int wave_tot[kWaves];
@@ -35,10 +37,64 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
   const int G = E + (shared_rows > 0 ? 1 : 0);
   const int g = blockIdx.x;
 
+  if (fin.partial) {
+    // Few tokens: finish the routing here.  Every workgroup adds the partial
+    // logits of all T <= kSmallRouteT tokens (part order, then the bias),
+    // picks each token's top-k (E <= kSmallRouteE) and keeps the ids in LDS;
+    // workgroup 0 also stores ids and weights.
+    extern __shared__ float lg[];  // [T][E + 1]
+    const int T = A / k;
+    for (int idx = tid; idx < T * E; idx += kThreads) {
+      const int t = idx / E, e = idx - t * E;
+      const float* src = fin.partial + (int64_t)t * E + e;
+      const int64_t stride = (int64_t)T * E;
+      float v = 0.f;
+      for (int q0 = 0; q0 < fin.P; q0 += 16) {
+        float pv[16];  // every load of the group in flight before the in-order sum
+#pragma unroll
+        for (int q = 0; q < 16; ++q) pv[q] = q0 + q < fin.P ? src[(q0 + q) * stride] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (q0 + q < fin.P) v = (q0 + q == 0) ? pv[q] : v + pv[q];
+      }
+      if (fin.bias) v += fin.bias[e];
+      lg[t * (E + 1) + e] = v;
+    }
+    __syncthreads();
+    // slot of every (token, expert): the number of the token's logits that
+    // rank before it (value descending, ties to the lower index); one thread
+    // per pair, so all tokens are ranked at once
+    for (int idx = tid; idx < T * E; idx += kThreads) {
+      const int t = idx / E, e = idx - t * E;
+      const float* row = lg + t * (E + 1);
+      const float v = row[e];
+      int rank = 0;
+      for (int j = 0; j < E; ++j) rank += ranks_before(row[j], j, v, e) ? 1 : 0;
+      if (rank < k) s_ids[t * k + rank] = e;
+    }
+    __syncthreads();
+    if (g == 0) {  // softmax over the chosen, adding exp(l - l_max) in slot order
+      for (int idx = tid; idx < T * k; idx += kThreads) {
+        const int t = idx / k, q = idx - t * k;
+        const float* row = lg + t * (E + 1);
+        const float vmax = row[s_ids[t * k]];
+        float tot = 0.f, mine = 0.f;
+        for (int j = 0; j < k; ++j) {
+          const float ex = expf(row[s_ids[t * k + j]] - vmax);
+          tot += ex;
+          if (j == q) mine = ex;
+        }
+        fin.ids[idx] = s_ids[idx];
+        fin.wts[idx] = mine / tot;
+      }
+    }
+  }
+  auto id_of = [&](int a) { return fin.partial ? s_ids[a] : ids[a]; };
+
   for (int i = tid; i < G; i += kThreads) hist[i] = (i == E) ? shared_rows : 0;
   __syncthreads();
   for (int a = tid; a < A; a += kThreads) {
-    const int e = ids[a];
+    const int e = id_of(a);
     if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
   }
   __syncthreads();
@@ -63,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
     if (tid == 0) n_tiles[0] = s_pad[G] / BM;
     // assignments with an id outside [0, E) get no row
     for (int a = tid; a < A; a += kThreads) {
-      const int e = ids[a];
+      const int e = id_of(a);
       if (e < 0 || e >= E) row_of[a] = -1;
     }
   }
@@ -74,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int base = 0; base < A; base += kThreads) {
       const int a = base + tid;
-      const bool pred = a < A && ids[a] == g;
+      const bool pred = a < A && id_of(a) == g;
       const uint64_t m = __ballot(pred);
       const int rank = __popcll(m & below);
       if (lane == 0) wave_tot[wave] = __popcll(m);
@@ -107,10 +163,26 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int shared_rows,
                         int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
                         int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
-                        hipStream_t s) {
+                        const RouteFinish* fin, hipStream_t s) {
   const int G = E + (shared_rows > 0 ? 1 : 0);
-  hipLaunchKernelGGL(moe_align_kernel, dim3(G), dim3(kThreads), 0, s, ids, T * k, k, E, BM, shared_rows,
-                     counts, offsets, padded, sorted_assign, row_of, row_token, tile_group, n_tiles);
+  RouteFinish f{};
+  size_t lds = 0;
+  if (fin) {
+    if (T > kSmallRouteT || k > 8 || E > kSmallRouteE) return hipErrorInvalidValue;
+    f = *fin;
+    lds = sizeof(float) * (size_t)T * (E + 1);
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)moe_align_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)(sizeof(float) * kSmallRouteT * (kSmallRouteE + 1)));
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  }
+  hipLaunchKernelGGL(moe_align_kernel, dim3(G), dim3(kThreads), lds, s, ids, T * k, k, E, BM,
+                     shared_rows, counts, offsets, padded, sorted_assign, row_of, row_token,
+                     tile_group, n_tiles, f);
   return hipGetLastError();
 }
 

@@ -52,7 +52,8 @@ struct Marks {
 
 // Everything after routing: align -> gate/up -> down -> combine.
 int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, const float* wts,
-                float* y, void* ws, hipStream_t s, Marks mk = Marks{nullptr}) {
+                float* y, void* ws, hipStream_t s, Marks mk = Marks{nullptr},
+                const moe::RouteFinish* fin = nullptr) {
   using namespace moe;
   int32_t* counts = at<int32_t>(ws, P.off_counts);
   int32_t* offsets = at<int32_t>(ws, P.off_offsets);
@@ -73,7 +74,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   }
 
   hipError_t e = launch_align(ids, (int)P.T, (int)P.k, (int)P.E, P.BM, shared_rows, counts, offsets,
-                              padded, sorted, row_of, row_token, tile_group, n_tiles, s);
+                              padded, sorted, row_of, row_token, tile_group, n_tiles, fin, s);
   if (e == hipSuccess) e = mk.mark(2, s);
   if (e != hipSuccess) return hip_fail(e);
 
@@ -168,11 +169,23 @@ static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, 
   const Marks mk{events};
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(workspace, P.off_ids);
   float* wts = topk_w ? topk_w : at<float>(workspace, P.off_w);
+  const float* bias = shape->has_router_bias ? w->router_bias : nullptr;
   hipError_t e = mk.mark(0, s);
+  if (P.T <= moe::kSmallRouteT && P.E <= moe::kSmallRouteE) {
+    // few tokens: partial logits over many workgroups, routing finished in align
+    float* rpart = at<float>(workspace, P.off_rpart);
+    if (e == hipSuccess)
+      e = moe::launch_router_partial(static_cast<const uint16_t*>(w->x),
+                                     static_cast<const uint16_t*>(w->w_g), (int)P.T, (int)P.D,
+                                     (int)P.E, rpart, s);
+    if (e == hipSuccess) e = mk.mark(1, s);
+    if (e != hipSuccess) return hip_fail(e);
+    const moe::RouteFinish fin{rpart, moe::router_parts(P.D), bias, ids, wts};
+    return run_experts(P, w, ids, wts, y, workspace, s, mk, &fin);
+  }
   if (e == hipSuccess)
     e = moe::launch_router(static_cast<const uint16_t*>(w->x), static_cast<const uint16_t*>(w->w_g),
-                           shape->has_router_bias ? w->router_bias : nullptr, (int)P.T, (int)P.D,
-                           (int)P.E, (int)P.k, ids, wts, s);
+                           bias, (int)P.T, (int)P.D, (int)P.E, (int)P.k, ids, wts, s);
   if (e == hipSuccess) e = mk.mark(1, s);
   if (e != hipSuccess) return hip_fail(e);
   return run_experts(P, w, ids, wts, y, workspace, s, mk);
@@ -224,7 +237,7 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t 
   if (T > 0 && (!topk_ids || !sorted_assign || !row_of)) return MOE_ERR_INVALID_ARG;
   hipError_t e = moe::launch_align(topk_ids, T, k, E, block_m, shared_rows, counts, offsets,
                                    padded_offsets, sorted_assign, row_of, row_token, tile_group,
-                                   n_tiles, static_cast<hipStream_t>(stream));
+                                   n_tiles, nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return MOE_OK;
 }

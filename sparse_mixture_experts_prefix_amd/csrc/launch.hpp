@@ -3,17 +3,35 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.hpp"
+
 namespace moe {
 
 // Router: logits = x W_g^T (+ bias) in fp32, top-k, softmax over the chosen.
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_g, const float* bias, int T, int D,
                          int E, int k, int32_t* ids, float* wts, hipStream_t s);
 
+// Few tokens: the router's K range is split over router_parts(D) workgroups
+// per 16 tokens, which write partial logits [P][T][E] (fp32); the align
+// kernel adds them (part order), adds the bias and picks top-k.
+hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w_g, int T, int D, int E,
+                                 float* partial, hipStream_t s);
+
+// Routing finished inside the align kernel (NULL: the ids are given).
+struct RouteFinish {
+  const float* partial;  // [P][T][E]
+  int P;
+  const float* bias;     // fp32 [E] or NULL
+  int32_t* ids;          // top-k ids out [T, k]
+  float* wts;            // top-k weights out [T, k]
+};
+
 // Expert grouping of the assignments (see moe_align in moe.h).
+// With fin != NULL the ids come from fin (T <= kSmallRouteT) and `ids` is unused.
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int shared_rows,
                         int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
                         int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
-                        hipStream_t s);
+                        const RouteFinish* fin, hipStream_t s);
 
 struct GroupedGemm {
   const uint16_t* A;          // gate/up: x [T, D] (rows gathered by row_token); down: H

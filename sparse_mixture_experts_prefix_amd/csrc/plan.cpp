@@ -72,6 +72,10 @@ int make_plan(const moe_shape* s, Plan* p) {
   p->off_yp = take(sizeof(float) * (size_t)p->cap_rows * p->D);
   const bool split = p->BM == 256;  // only the 256-row kernels split tiles over K
   p->off_partial = take(split ? sizeof(float) * kSplitCtas * kPartialTileFloats : 0);
+  // partial router logits of the few-token path
+  p->off_rpart = take(p->T <= kSmallRouteT && p->E <= kSmallRouteE
+                          ? sizeof(float) * router_parts(p->D) * p->T * p->E
+                          : 0);
   p->total = o;
   return MOE_OK;
 }

@@ -9,6 +9,14 @@
 
 namespace moe {
 
+// Few tokens (T <= kSmallRouteT, E <= kSmallRouteE): the router's K range is split over
+// router_parts(D) workgroups per 16 tokens (kRouterPartChunks 64-wide chunks
+// each), and the align kernel finishes the routing.
+constexpr int kSmallRouteT = 64;
+constexpr int kSmallRouteE = 64;
+constexpr int kRouterPartChunks = 8;
+inline int router_parts(int64_t D) { return (int)(((D + 63) / 64 + kRouterPartChunks - 1) / kRouterPartChunks); }
+
 // Workgroups the prefill GEMMs balance their last round over (one per CU,
 // at most this many), and so the number of partial tiles the workspace holds.
 constexpr int kSplitCtas = 256;
@@ -25,7 +33,7 @@ struct Plan {
   int64_t ldh;        // row stride (elements) of the hidden activations H: max(F, Fs)
   // byte offsets inside the workspace
   size_t off_ids, off_w, off_counts, off_offsets, off_padded, off_ntiles, off_sorted, off_rowof,
-      off_rowtoken, off_tilegroup, off_h, off_yp, off_partial, total;
+      off_rowtoken, off_tilegroup, off_h, off_yp, off_partial, off_rpart, total;
 };
 
 // Shape checks shared by every entry point (MOE_OK or an error code).

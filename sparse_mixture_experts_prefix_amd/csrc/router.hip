@@ -7,15 +7,17 @@
 // Experts - Mezcla de Expertos)", section 2 diagram row 2, p = Softmax(TopK(W_g x)).
 //
 // One workgroup of 16 wavefronts (8 when E > 128) owns 16 tokens.  Logits are an MFMA
-// 16x16x32 bf16 contraction with fp32 accumulation: wave w takes the 32-wide
+// 16x16x32 bf16 contraction with fp32 accumulation: wave w takes the 64-wide
 // slices w, w+16, w+32, ... of D (w, w+8, ... with 8 waves), and the partial
-// sums are added by a fixed tree in LDS, so a token's logits are bitwise the same for any
-// T (one configuration for every batch size; 16 waves keep enough loads in
-// flight when T is a handful of tokens).  Each wave then ranks tokens: the
-// E <= 256 logits sit 4 per lane, and k rounds of a wave-wide
-// (value desc, index asc) arg-max pick the experts.
+// sums are added in LDS in wave order, so a token's logits are bitwise the
+// same for any T (one configuration for every batch size; 16 waves keep
+// enough loads in flight when T is a handful of tokens).  Each wave then
+// ranks tokens in (value desc, index asc) order: with E <= 64 every lane
+// counts the logits that beat its own; with more experts, 4 logits per lane
+// and k rounds of a wave-wide arg-max pick them.
 #include "device.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace moe {
 namespace {
@@ -28,11 +30,6 @@ constexpr int kTok = 16;  // tokens per workgroup
 template <int NCT>
 constexpr int waves_for() { return NCT > 8 ? 8 : 16; }
 
-// (v, i) beats (w, j) when v > w, or v == w and i < j.
-__device__ __forceinline__ bool better(float v, int i, float w, int j) {
-  return v > w || (v == w && i < j);
-}
-
 template <int NCT>  // 16-expert column tiles; E <= 16 * NCT
 __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wg,
@@ -42,11 +39,10 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
                                                           float* __restrict__ wts) {
   constexpr int EP = 16 * NCT;
   constexpr int kWaves = waves_for<NCT>();
-  constexpr int kLevels = kWaves == 16 ? 4 : 3;
-  // chunks whose loads are in flight together (the same chunk order per wave
-  // for every UNR, so the sums do not depend on it)
-  constexpr int UNR = NCT <= 2 ? 6 : (NCT <= 4 ? 3 : 1);
-  extern __shared__ float part[];        // [kWaves/2][kTok][EP + 1]: partials, then logits
+  // 64-wide K chunks whose loads are in flight together (the same chunk order
+  // per wave for every UNR, so the sums do not depend on it)
+  constexpr int UNR = NCT <= 2 ? 3 : (NCT <= 4 ? 2 : 1);
+  extern __shared__ float part[];        // [kWaves][kTok][EP + 1]: partials, then logits
   auto slot = [&](int s, int row, int col) -> float& {
     return part[(s * kTok + row) * (EP + 1) + col];
   };
@@ -58,64 +54,58 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
   f32x4 acc[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Inside a 64-wide chunk, x and W_g use the same K permutation: lane
+  // (r16, kb) holds bytes [32kb, 32kb+32) of its row for two MFMAs, so the
+  // four lanes of a row read one whole 128-byte line.
   const int r16 = lane & 15, kb = lane >> 4;
   const int tok = t0 + r16;
   const bf16_t* xr = x + (int64_t)(tok < T ? tok : 0) * D;
-  const int nchunks = (D + 31) / 32;
+  const int nchunks = (D + 63) / 64;
   constexpr int CG = NCT < 8 ? NCT : 8;  // column tiles whose weights are loaded together
+  const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int ch0 = wave; ch0 < nchunks; ch0 += UNR * kWaves) {
 #pragma unroll
     for (int c0 = 0; c0 < NCT; c0 += CG) {
-      u32x4 av[UNR], bv[UNR][CG];
+      u32x4 av[UNR][2], bv[UNR][CG][2];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int kk = (ch0 + u * kWaves) * 32 + kb * 8;  // D % 8 == 0: 8-runs are all in or out
-        const bool kin = ch0 + u * kWaves < nchunks && kk < D;
-        av[u] = (tok < T && kin) ? ld16(xr + kk) : u32x4{0u, 0u, 0u, 0u};
+        const int kk = (ch0 + u * kWaves) * 64 + kb * 16;  // D % 8 == 0: 8-runs are all in or out
+        const bool in0 = ch0 + u * kWaves < nchunks && kk < D, in1 = in0 && kk + 8 < D;
+        av[u][0] = (tok < T && in0) ? ld16(xr + kk) : zero;
+        av[u][1] = (tok < T && in1) ? ld16(xr + kk + 8) : zero;
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
           const int e = (c0 + c) * 16 + r16;
-          bv[u][c] = (e < E && kin) ? ld16(wg + (int64_t)e * D + kk) : u32x4{0u, 0u, 0u, 0u};
+          const bf16_t* wr = wg + (int64_t)(e < E ? e : 0) * D + kk;
+          bv[u][c][0] = (e < E && in0) ? ld16(wr) : zero;
+          bv[u][c][1] = (e < E && in1) ? ld16(wr + 8) : zero;
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // all loads of the trip before the MFMAs
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
 #pragma unroll
-        for (int c = 0; c < CG; ++c)
-          acc[c0 + c] = mfma16(as_bf16x8(av[u]), as_bf16x8(bv[u][c]), acc[c0 + c]);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+            acc[c0 + c] = mfma16(as_bf16x8(av[u][h]), as_bf16x8(bv[u][c][h]), acc[c0 + c]);
     }
   }
 
-  // ---- fixed tree over the partial sums: level h adds wave w + 2^h into wave w
+  // ---- partial sums of all waves into LDS; each logit is then the sum over
+  // the waves in wave order (one barrier instead of a tree of them)
 #pragma unroll
-  for (int h = kLevels - 1; h >= 0; --h) {
-    const int half = 1 << h;
-    if (wave >= half && wave < 2 * half) {
+  for (int c = 0; c < NCT; ++c)
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+    for (int r = 0; r < 4; ++r) slot(wave, 4 * kb + r, c * 16 + r16) = acc[c][r];
+  __syncthreads();
+  for (int idx = tid; idx < kTok * EP; idx += kWaves * 64) {
+    const int row = idx / EP, col = idx - row * EP;
+    float sum = slot(0, row, col);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) slot(wave - half, 4 * kb + r, c * 16 + r16) = acc[c][r];
-    }
-    __syncthreads();
-    if (wave < half) {
-#pragma unroll
-      for (int c = 0; c < NCT; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[c][r] += slot(wave, 4 * kb + r, c * 16 + r16);
-    }
-    __syncthreads();
-  }
-  if (wave == 0) {
-#pragma unroll
-    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = c * 16 + r16;
-        float s = acc[c][r];
-        if (bias && col < E) s += bias[col];
-        slot(0, 4 * kb + r, col) = s;
-      }
+    for (int w = 1; w < kWaves; ++w) sum += slot(w, row, col);
+    if (bias && col < E) sum += bias[col];
+    slot(0, row, col) = sum;  // only this thread reads or writes this element
   }
   __syncthreads();
 
@@ -123,57 +113,10 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
   for (int r = wave; r < kTok; r += kWaves) {
     const int t = t0 + r;
     if (t >= T) break;
-    float v[4];
-    bool live[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      live[q] = e < E;
-      v[q] = live[q] ? slot(0, r, e) : 0.f;
-    }
-    float my_v = 0.f, vmax = 0.f;
-    int my_i = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = 0.f;
-      int bi = 0x7fffffff;
-      bool have = false;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q;
-        if (live[q] && (!have || better(v[q], e, bv, bi))) {
-          bv = v[q];
-          bi = e;
-          have = true;
-        }
-      }
-      // lanes with nothing left carry index INT_MAX and lose every comparison
-      if (!have) bv = -__builtin_inff();
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (lane + 64 * q == bi) live[q] = false;
-      if (j == 0) vmax = bv;
-      if (lane == j) {
-        my_v = bv;
-        my_i = bi;
-      }
-    }
-    float s = lane < k ? expf(my_v - vmax) : 0.f;
-    float tot = s;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
-    if (lane < k) {
-      ids[(int64_t)t * k + lane] = my_i;
-      wts[(int64_t)t * k + lane] = s / tot;
-    }
+    topk_softmax(&slot(0, r, 0), E, k, lane, [&](int q, int e, float w) {
+      ids[(int64_t)t * k + q] = e;
+      wts[(int64_t)t * k + q] = w;
+    });
   }
 }
 
@@ -181,7 +124,7 @@ template <int NCT>
 hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias, int T, int D,
                       int E, int k, int32_t* ids, float* wts, hipStream_t s) {
   constexpr int kWaves = waves_for<NCT>();
-  const size_t lds = sizeof(float) * (kWaves / 2) * kTok * (16 * NCT + 1);
+  const size_t lds = sizeof(float) * kWaves * kTok * (16 * NCT + 1);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)moe_router_kernel<NCT>,
@@ -195,7 +138,105 @@ hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias,
   return hipGetLastError();
 }
 
+
+// Partial logits for few tokens: workgroup (token tile, p) owns the 64-wide K
+// chunks p*8 .. p*8+7; wave w takes chunks w and w+4 of them, the four waves
+// are added in wave order, and the sum is stored as partial[p][t][e].  The
+// chunk of every product depends on D only, so the logits do not depend on T.
+constexpr int kPartWaves = 4;
+
+template <int NCT>
+__global__ __launch_bounds__(kPartWaves * 64) void moe_router_partial_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, int T, int D, int E,
+    float* __restrict__ partial) {
+  constexpr int EP = 16 * NCT;
+  constexpr int CG = NCT < 8 ? NCT : 8;
+  extern __shared__ float part[];  // [kPartWaves][kTok][EP + 1]
+  auto slot = [&](int s, int row, int col) -> float& {
+    return part[(s * kTok + row) * (EP + 1) + col];
+  };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * kTok, p = blockIdx.y;
+  f32x4 acc[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r16 = lane & 15, kb = lane >> 4;
+  const int tok = t0 + r16;
+  const bf16_t* xr = x + (int64_t)(tok < T ? tok : 0) * D;
+  const int nchunks = (D + 63) / 64;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int c0 = 0; c0 < NCT; c0 += CG) {
+    u32x4 av[2][2], bv[2][CG][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ch = p * kRouterPartChunks + wave + u * kPartWaves;
+      const int kk = ch * 64 + kb * 16;  // same K permutation as the full router
+      const bool in0 = ch < nchunks && kk < D, in1 = in0 && kk + 8 < D;
+      av[u][0] = (tok < T && in0) ? ld16(xr + kk) : zero;
+      av[u][1] = (tok < T && in1) ? ld16(xr + kk + 8) : zero;
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        const int e = (c0 + c) * 16 + r16;
+        const bf16_t* wr = wg + (int64_t)(e < E ? e : 0) * D + kk;
+        bv[u][c][0] = (e < E && in0) ? ld16(wr) : zero;
+        bv[u][c][1] = (e < E && in1) ? ld16(wr + 8) : zero;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+          acc[c0 + c] = mfma16(as_bf16x8(av[u][h]), as_bf16x8(bv[u][c][h]), acc[c0 + c]);
+  }
+#pragma unroll
+  for (int c = 0; c < NCT; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) slot(wave, 4 * kb + r, c * 16 + r16) = acc[c][r];
+  __syncthreads();
+  for (int idx = tid; idx < kTok * E; idx += kPartWaves * 64) {
+    const int row = idx / E, col = idx - row * E;
+    if (t0 + row >= T) continue;
+    float sum = slot(0, row, col);
+#pragma unroll
+    for (int w = 1; w < kPartWaves; ++w) sum += slot(w, row, col);
+    partial[((int64_t)p * T + t0 + row) * E + col] = sum;
+  }
+}
+
+template <int NCT>
+hipError_t launch_partial_nct(const uint16_t* x, const uint16_t* w_g, int T, int D, int E,
+                              float* partial, hipStream_t s) {
+  const size_t lds = sizeof(float) * kPartWaves * kTok * (16 * NCT + 1);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)moe_router_partial_kernel<NCT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid((T + kTok - 1) / kTok, router_parts(D));
+  hipLaunchKernelGGL(moe_router_partial_kernel<NCT>, grid, dim3(kPartWaves * 64), lds, s, x, w_g, T,
+                     D, E, partial);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w_g, int T, int D, int E,
+                                 float* partial, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nct = (E + 15) / 16;
+  if (nct <= 1) return launch_partial_nct<1>(x, w_g, T, D, E, partial, s);
+  if (nct <= 2) return launch_partial_nct<2>(x, w_g, T, D, E, partial, s);
+  if (nct <= 4) return launch_partial_nct<4>(x, w_g, T, D, E, partial, s);
+  if (nct <= 8) return launch_partial_nct<8>(x, w_g, T, D, E, partial, s);
+  return launch_partial_nct<16>(x, w_g, T, D, E, partial, s);
+}
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_g, const float* bias, int T, int D,
                          int E, int k, int32_t* ids, float* wts, hipStream_t s) {
