@@ -62,6 +62,9 @@ def _load():
             lib.oracle_experts.restype = ctypes.c_int
             lib.oracle_experts.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p,
                                            _p, _i64, _p, _p]
+            lib.oracle_experts_shard.restype = ctypes.c_int
+            lib.oracle_experts_shard.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                                 _i32, _i32, _p, _p, _p, _i64, _p, _p]
             lib.oracle_forward.restype = ctypes.c_int
             lib.oracle_forward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i32,
                                            _i32, _p, _p, _p, _p]
@@ -121,9 +124,15 @@ def route(x, w_g, router_bias, k: int):
     return ids, p, margin, logits
 
 
-def experts(inp, ids, p, tokens=None, count_macs: bool = False):
+def experts(inp, ids, p, tokens=None, count_macs: bool = False, expert_begin: int = 0,
+            n_local=None):
     """Expert outputs y [n, D] (float64) for ``tokens`` (default: all rows of x)
-    under the routing (ids [T,k] int, p [T,k] float)."""
+    under the routing (ids [T,k] int, p [T,k] float).
+
+    With ``n_local`` set, ``inp.w_gate_up`` / ``inp.w_down`` hold only experts
+    expert_begin .. expert_begin+n_local-1 of the ``inp.shape.E`` the router
+    scores, and only slots routed to them contribute (one expert-parallel
+    shard); the shared expert is included when ``inp`` carries it."""
     lib = _load()
     s = inp.shape
     px, kx = _bf16_ptr(inp.x)
@@ -136,6 +145,9 @@ def experts(inp, ids, p, tokens=None, count_macs: bool = False):
     T = inp.x.shape[0]
     if ids.shape != (T, s.k) or p.shape != (T, s.k):
         raise ValueError("routing shape mismatch")
+    nl = s.E if n_local is None else int(n_local)
+    if inp.w_gate_up.shape[0] != nl or inp.w_down.shape[0] != nl:
+        raise ValueError("expert weights hold %d experts, expected %d" % (inp.w_gate_up.shape[0], nl))
     if tokens is None:
         tok = None
         n = T
@@ -146,11 +158,12 @@ def experts(inp, ids, p, tokens=None, count_macs: bool = False):
         n = tok.size
     y = np.empty((n, s.D), np.float64)
     macs = ctypes.c_int64(0)
-    rc = lib.oracle_experts(px, pgu, pdn, psgu, psdn, s.D, s.E, s.F, s.k, s.Fs, ids.ctypes.data,
-                            p.ctypes.data, None if tok is None else tok.ctypes.data, n,
-                            y.ctypes.data, ctypes.byref(macs))
+    rc = lib.oracle_experts_shard(px, pgu, pdn, psgu, psdn, s.D, s.E, int(expert_begin), nl, s.F,
+                                  s.k, s.Fs, ids.ctypes.data, p.ctypes.data,
+                                  None if tok is None else tok.ctypes.data, n, y.ctypes.data,
+                                  ctypes.byref(macs))
     if rc:
-        raise ValueError("oracle_experts failed: %d" % rc)
+        raise ValueError("oracle_experts_shard failed: %d" % rc)
     return (y, macs.value) if count_macs else y
 
 

@@ -170,18 +170,26 @@ static void swiglu_accumulate(const uint16_t* w_gu, const uint16_t* w_dn, int32_
 }
 
 /*
- * Expert outputs for n_tokens tokens given their routing.
+ * Expert outputs for n_tokens tokens given their routing, for one shard of
+ * the experts (expert parallelism: "Mixture of Experts optimiza Transformers
+ * y LLMs", section "Expert Parallelism"; "Transformers v5 El Secreto Detrás
+ * de los Modelos MoE Más Rápidos", section "Paralelismo de Expertos"): only
+ * the slots routed to experts e0 .. e0+n_local-1 contribute, and w_gate_up /
+ * w_down hold just those n_local experts.  The shards' outputs add up to the
+ * layer's (the shared expert is added by whichever call passes it).
  *   x [T,D] bf16 (rows picked by tokens[], or rows 0..n_tokens-1 when tokens is NULL)
- *   w_gate_up [E,2F,D], w_down [E,D,F] bf16; ws_gate_up [2Fs,D], ws_down [D,Fs] bf16 or NULL
- *   ids [*,k], p [*,k]: the routing rows of the same tokens (indexed by token id)
+ *   w_gate_up [n_local,2F,D], w_down [n_local,D,F] bf16; ws_gate_up [2Fs,D], ws_down [D,Fs] bf16 or NULL
+ *   ids [*,k] (global expert ids), p [*,k]: the routing rows of the same tokens (indexed by token id)
  *   y [n_tokens, D] double out; macs: total multiply-adds performed (may be NULL)
  * Slots are accumulated in order j = 0..k-1, the shared expert last.
  */
-int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
-                   const uint16_t* ws_gate_up, const uint16_t* ws_down, int32_t D, int32_t E,
-                   int32_t F, int32_t k, int32_t Fs, const int32_t* ids, const double* p,
-                   const int64_t* tokens, int64_t n_tokens, double* y, int64_t* macs) {
+int oracle_experts_shard(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
+                         const uint16_t* ws_gate_up, const uint16_t* ws_down, int32_t D, int32_t E,
+                         int32_t e0, int32_t n_local, int32_t F, int32_t k, int32_t Fs,
+                         const int32_t* ids, const double* p, const int64_t* tokens,
+                         int64_t n_tokens, double* y, int64_t* macs) {
   if (D <= 0 || E <= 0 || F <= 0 || k <= 0 || k > E || Fs < 0 || n_tokens < 0) return -1;
+  if (e0 < 0 || n_local < 0 || e0 + n_local > E) return -1;
   if (Fs > 0 && (!ws_gate_up || !ws_down)) return -1;
   int err = 0;
   int64_t total = 0;
@@ -202,8 +210,8 @@ int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t*
         for (int32_t d = 0; d < D; ++d) xd[d] = bf(xt[d]);
         for (int32_t d = 0; d < D; ++d) yt[d] = 0.0;
         for (int32_t j = 0; j < k; ++j) {
-          int32_t e = ids[t * k + j];
-          if (e < 0 || e >= E) continue; /* never produced by the router */
+          int32_t e = ids[t * k + j] - e0; /* index inside this shard */
+          if (e < 0 || e >= n_local) continue; /* another shard's expert */
           swiglu_accumulate(w_gate_up + (int64_t)e * 2 * F * D, w_down + (int64_t)e * D * F, F, D,
                             xd, h, p[t * k + j], yt, &total);
         }
@@ -215,6 +223,15 @@ int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t*
   }
   if (macs) *macs = total;
   return err;
+}
+
+/* Expert outputs with every expert present (the unsharded layer). */
+int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
+                   const uint16_t* ws_gate_up, const uint16_t* ws_down, int32_t D, int32_t E,
+                   int32_t F, int32_t k, int32_t Fs, const int32_t* ids, const double* p,
+                   const int64_t* tokens, int64_t n_tokens, double* y, int64_t* macs) {
+  return oracle_experts_shard(x, w_gate_up, w_down, ws_gate_up, ws_down, D, E, 0, E, F, k, Fs, ids,
+                              p, tokens, n_tokens, y, macs);
 }
 
 /*
