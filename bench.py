@@ -86,6 +86,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (removes host launch gaps)")
+    ap.add_argument("--ep", type=int, default=1,
+                    help="expert-parallel degree: time the shard of one rank (E/ep experts; the "
+                         "shared expert on rank 0) at the workload's real shape")
+    ap.add_argument("--rank", type=int, default=0, help="which shard --ep times")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="run one plain device copy of this many GiB first (a known-size kernel "
                          "for calibrating rocprofv3 byte counters)")
@@ -113,9 +117,21 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     s = wl.shape if args.T is None else wl.shape.with_T(args.T)
+    if args.ep < 1 or s.E % args.ep or not 0 <= args.rank < args.ep:
+        raise SystemExit("--ep must divide E=%d and 0 <= --rank < --ep" % s.E)
     _log("generating %s T=%d inputs" % (wl.name, s.T))
     inp = W.make_inputs(s, seed=0)
+    e_loc = s.E // args.ep
+    e0 = args.rank * e_loc
+    if args.ep > 1:  # this rank's shard: its experts, the shared expert on rank 0 only
+        keep_shared = args.rank == 0
+        inp = W.LayerInputs(s, inp.x, inp.w_g, inp.w_gate_up[e0:e0 + e_loc].contiguous(),
+                            inp.w_down[e0:e0 + e_loc].contiguous(), inp.router_bias,
+                            inp.ws_gate_up if keep_shared else None,
+                            inp.ws_down if keep_shared else None)
     g = inp.to(dev)
+    shard = dict(expert_begin=e0) if args.ep > 1 else {}
+    fs_used = s.Fs if (args.ep == 1 or args.rank == 0) else 0
     # Rotate over weight copies when one copy would sit in the Infinity Cache.
     wbytes = inp.w_gate_up.numel() * 2 + inp.w_down.numel() * 2
     n_copies = 1 if wbytes > 4 * LLC_BYTES else 4
@@ -124,7 +140,8 @@ def main():
         sets.append(W.LayerInputs(s, g.x, g.w_g, g.w_gate_up.clone(), g.w_down.clone(), g.router_bias,
                                   None if g.ws_gate_up is None else g.ws_gate_up.clone(),
                                   None if g.ws_down is None else g.ws_down.clone()))
-    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias)
+    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, fs_used, s.router_bias,
+                           e0 if args.ep > 1 else 0, e_loc if args.ep > 1 else 0)
     ws = moe.alloc_workspace(shape, dev)
     y = torch.empty((s.T, s.D), dtype=torch.float32, device=dev)
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
@@ -143,7 +160,7 @@ def main():
     def step(i):
         q = sets[i % len(sets)]
         moe.moe_forward(q.x, q.w_g, q.w_gate_up, q.w_down, s.k, q.router_bias, q.ws_gate_up,
-                        q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws)
+                        q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws, **shard)
 
     run = step
     if args.graph:
@@ -177,7 +194,8 @@ def main():
     for i in range(args.steps):
         q = sets[i % len(sets)]
         moe.moe_forward_timed(ev[i], q.x, q.w_g, q.w_gate_up, q.w_down, s.k, q.router_bias,
-                              q.ws_gate_up, q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws)
+                              q.ws_gate_up, q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws,
+                              **shard)
     torch.cuda.synchronize()
     per_kernel = {name: float(np.mean([e.elapsed_ms(j, j + 1) for e in ev]))
                   for j, name in enumerate(KERNELS)}
@@ -185,23 +203,29 @@ def main():
         e.close()
 
     loads = np.bincount(ids.cpu().numpy().ravel(), minlength=s.E)
-    touched = int((loads > 0).sum())
-    flops = W.algorithmic_flops(s)
-    nbytes = W.algorithmic_bytes(s, touched)
+    local = loads[e0:e0 + e_loc]  # the whole layer when ep == 1
+    touched = int((local > 0).sum())
+    n_assign = int(local.sum())   # routed rows this call computes
+    # algorithmic work of this call: router over all E, its routed rows, the
+    # shared expert where it runs; bytes: touched experts' weights, W_g, x, y
+    gu_flops = 4 * n_assign * s.D * s.F + 4 * s.T * s.D * fs_used
+    flops = 2 * s.T * s.D * s.E + gu_flops + 2 * n_assign * s.D * s.F + 2 * s.T * s.D * fs_used
+    nbytes = (touched * W.expert_params(s) * 2 + 3 * s.D * fs_used * 2 + s.E * s.D * 2
+              + s.T * s.D * 2 + s.T * s.D * 4)
     t_ideal = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
     layer_bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9) else "hbm"
 
     gu_ms = per_kernel["moe_gemm_gate_up"]
     shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias)
     gemm_file = "gemm_prefill.hip" if moe.moe_block_m(shape) == 256 else "gemm_decode.hip"
-    traffic = _traffic_from_profile(wl.name, s.T, _kernel_sources_sha(gemm_file))
+    traffic = _traffic_from_profile(wl.name, s.T, _kernel_sources_sha(gemm_file)) if args.ep == 1 else None
     if layer_bound == "mfma":
-        achieved = W.gate_up_flops(s) / (gu_ms * 1e-3) / 1e12
+        achieved = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     else:
         # expert weights of the gate/up half actually touched + gathered x
-        gu_bytes = touched * 2 * s.F * s.D * 2 + 2 * s.Fs * s.D * 2 + s.T * s.D * 2
+        gu_bytes = touched * 2 * s.F * s.D * 2 + 2 * fs_used * s.D * 2 + s.T * s.D * 2
         achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
@@ -224,7 +248,9 @@ def main():
         "data": "synthetic (seeded counter-based normal draws: x ~ N(0,1), weights ~ N(0,0.02), bf16)",
         "config": {"workload": wl.name, "T": s.T, "D": s.D, "E": s.E, "k": s.k, "d_ff": s.F,
                    "shared_d_ff": s.Fs, "router_bias": bool(s.router_bias),
-                   "weight_copies_rotated": n_copies, "hip_graph": bool(args.graph)},
+                   "weight_copies_rotated": n_copies, "hip_graph": bool(args.graph),
+                   **({"expert_parallel": args.ep, "rank": args.rank, "local_experts": [e0, e0 + e_loc],
+                       "local_rows": n_assign} if args.ep > 1 else {})},
         "roofline": roof,
         "layer": {"bound": layer_bound, "algorithmic_tflop": round(flops / 1e12, 4),
                   "algorithmic_gb": round(nbytes / 1e9, 4), "ideal_ms": round(t_ideal * 1e3, 4),
@@ -233,7 +259,7 @@ def main():
                   "touched_experts": touched, "max_expert_rows": int(loads.max())},
         "kernel_ms": {k_: round(v, 4) for k_, v in per_kernel.items()},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.ep == 1:
         _log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
         out["cpu_baseline"] = _cpu_baseline(inp, args.cpu_seconds)
         out["cpu_baseline"]["sample"] = out["cpu_baseline"]["sample"].replace("same", wl.name)

@@ -79,14 +79,25 @@ typedef struct moe_shape {
   int32_t k;               /* experts per token */
   int32_t F_shared;        /* shared expert hidden width, 0 = none */
   int32_t has_router_bias; /* nonzero: weights->router_bias is used */
+  /* Expert-parallel shard ("Mixture of Experts optimiza Transformers y LLMs",
+   * section "Expert Parallelism"; "Transformers v5 El Secreto Detrás de los
+   * Modelos MoE Más Rápidos", section "Paralelismo de Expertos").  With
+   * num_local_experts > 0 the call holds only experts expert_begin ..
+   * expert_begin + num_local_experts - 1: w_gate_up / w_down have
+   * num_local_experts leading entries, the router still scores all E, and
+   * only assignments to the held experts contribute, so y is this shard's
+   * part of the layer (the shards' y add up to the whole layer; pass the
+   * shared expert to one shard only).  Both 0: every expert (no sharding). */
+  int32_t expert_begin;
+  int32_t num_local_experts;
 } moe_shape;
 
 typedef struct moe_weights {
   const void* x;            /* bf16 [T, D] */
   const void* w_g;          /* bf16 [E, D] */
   const float* router_bias; /* fp32 [E], or NULL when has_router_bias == 0 */
-  const void* w_gate_up;    /* bf16 [E, 2F, D] */
-  const void* w_down;       /* bf16 [E, D, F] */
+  const void* w_gate_up;    /* bf16 [E, 2F, D] ([num_local_experts, 2F, D] for a shard) */
+  const void* w_down;       /* bf16 [E, D, F] ([num_local_experts, D, F] for a shard) */
   const void* ws_gate_up;   /* bf16 [2*F_shared, D] or NULL */
   const void* ws_down;      /* bf16 [D, F_shared] or NULL */
 } moe_weights;

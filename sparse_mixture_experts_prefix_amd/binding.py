@@ -36,7 +36,8 @@ class MoEError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("k", ctypes.c_int32), ("F_shared", ctypes.c_int32),
-                ("has_router_bias", ctypes.c_int32)]
+                ("has_router_bias", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
+                ("num_local_experts", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -107,8 +108,12 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def make_shape(T, D, E, F, k, F_shared=0, has_router_bias=False) -> Shape:
-    return Shape(int(T), int(D), int(E), int(F), int(k), int(F_shared), 1 if has_router_bias else 0)
+def make_shape(T, D, E, F, k, F_shared=0, has_router_bias=False, expert_begin=0,
+               num_local_experts=0) -> Shape:
+    """moe_shape; num_local_experts > 0 makes the call one expert-parallel
+    shard holding experts expert_begin .. expert_begin+num_local_experts-1."""
+    return Shape(int(T), int(D), int(E), int(F), int(k), int(F_shared), 1 if has_router_bias else 0,
+                 int(expert_begin), int(num_local_experts))
 
 
 def workspace_size(shape: Shape) -> int:
@@ -121,12 +126,17 @@ def block_m(shape: Shape) -> int:
     return _check(load_library().moe_block_m(ctypes.byref(shape)))
 
 
-def _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, has_bias):
+def _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, has_bias, n_experts=None, expert_begin=None):
+    """Shape of a layer call; the call is a shard when the expert weights hold
+    fewer experts than the router scores (n_experts) or expert_begin is given."""
     T, D = x.shape
-    E, twoF, D2 = w_gate_up.shape
+    E_loc, twoF, D2 = w_gate_up.shape
     F = twoF // 2
     Fs = 0 if ws_gate_up is None else ws_gate_up.shape[0] // 2
-    return make_shape(T, D, E, F, k, Fs, has_bias)
+    E = E_loc if n_experts is None else int(n_experts)
+    if expert_begin is None and E == E_loc:
+        return make_shape(T, D, E, F, k, Fs, has_bias)
+    return make_shape(T, D, E, F, k, Fs, has_bias, expert_begin or 0, E_loc)
 
 
 def alloc_workspace(shape: Shape, device) -> torch.Tensor:
@@ -162,17 +172,24 @@ def _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down):
 
 
 def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None, ws_down=None, *,
-                y=None, topk_ids=None, topk_w=None, workspace=None):
+                y=None, topk_ids=None, topk_w=None, workspace=None, expert_begin=None):
     """Whole MoE layer.  Returns y (fp32 [T, D]).
 
     Optional preallocated outputs (y, topk_ids int32 [T,k], topk_w fp32 [T,k])
     and workspace (uint8, >= workspace_size bytes) avoid any allocation here.
+    Expert-parallel shard: pass w_gate_up / w_down of experts expert_begin ..
+    expert_begin + n - 1 only (w_g still covers all E); y is then the shard's
+    part of the layer.
     """
-    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    T, D, E_loc, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    _dev(w_g, "w_g", torch.bfloat16)
+    E = w_g.shape[0]
     _dev(w_g, "w_g", torch.bfloat16, (E, D))
+    if E_loc != E and expert_begin is None:
+        raise ValueError("w_gate_up holds %d of %d experts: pass expert_begin" % (E_loc, E))
     if router_bias is not None:
         _dev(router_bias, "router_bias", torch.float32, (E,))
-    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, router_bias is not None)
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, router_bias is not None, E, expert_begin)
     if y is None:
         y = torch.empty((T, D), dtype=torch.float32, device=x.device)
     _dev(y, "y", torch.float32, (T, D))
@@ -235,13 +252,15 @@ def moe_align(topk_ids, E: int, block_m_: int, shared_rows: int = 0):
 
 
 def moe_forward_routed(x, w_gate_up, w_down, topk_ids, topk_w, ws_gate_up=None, ws_down=None, *,
-                       y=None, workspace=None):
-    """The layer under a given routing (topk_ids int32 [T,k], topk_w fp32 [T,k])."""
+                       y=None, workspace=None, n_experts=None, expert_begin=None):
+    """The layer under a given routing (topk_ids int32 [T,k], topk_w fp32 [T,k]).
+    For a shard, n_experts is the router's expert count and expert_begin the
+    first held expert."""
     T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
     k = topk_ids.shape[1]
     _dev(topk_ids, "topk_ids", torch.int32, (T, k))
     _dev(topk_w, "topk_w", torch.float32, (T, k))
-    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, False)
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, False, n_experts, expert_begin)
     if y is None:
         y = torch.empty((T, D), dtype=torch.float32, device=x.device)
     _dev(y, "y", torch.float32, (T, D))
@@ -297,10 +316,12 @@ class HipEvents:
 
 
 def moe_forward_timed(events: HipEvents, x, w_g, w_gate_up, w_down, k, router_bias=None,
-                      ws_gate_up=None, ws_down=None, *, y, topk_ids, topk_w, workspace):
+                      ws_gate_up=None, ws_down=None, *, y, topk_ids, topk_w, workspace,
+                      expert_begin=None):
     """moe_forward recording events[0..5] around its five kernels (all buffers preallocated)."""
     T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
-    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, router_bias is not None)
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, router_bias is not None,
+                         w_g.shape[0], expert_begin)
     w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
     lib = load_library()
     lib.moe_forward_timed.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), ctypes.c_void_p,

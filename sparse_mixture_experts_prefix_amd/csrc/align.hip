@@ -23,7 +23,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
 __global__ __launch_bounds__(kThreads) void moe_align_kernel(
-    const int32_t* __restrict__ ids, int A, int k, int E, int BM, int shared_rows,
+    const int32_t* __restrict__ ids, int A, int k, int E, int id_base, int BM, int shared_rows,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ padded,
     int32_t* __restrict__ sorted_assign, int32_t* __restrict__ row_of,
     int32_t* __restrict__ row_token, int32_t* __restrict__ tile_group,
@@ -42,12 +42,12 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
     // logits of all T <= kSmallRouteT tokens (part order, then the bias),
     // picks each token's top-k (E <= kSmallRouteE) and keeps the ids in LDS;
     // workgroup 0 also stores ids and weights.
-    extern __shared__ float lg[];  // [T][E + 1]
-    const int T = A / k;
-    for (int idx = tid; idx < T * E; idx += kThreads) {
-      const int t = idx / E, e = idx - t * E;
-      const float* src = fin.partial + (int64_t)t * E + e;
-      const int64_t stride = (int64_t)T * E;
+    extern __shared__ float lg[];  // [T][EL + 1]
+    const int T = A / k, EL = fin.E;
+    for (int idx = tid; idx < T * EL; idx += kThreads) {
+      const int t = idx / EL, e = idx - t * EL;
+      const float* src = fin.partial + (int64_t)t * EL + e;
+      const int64_t stride = (int64_t)T * EL;
       float v = 0.f;
       for (int q0 = 0; q0 < fin.P; q0 += 16) {
         float pv[16];  // every load of the group in flight before the in-order sum
@@ -58,25 +58,25 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
           if (q0 + q < fin.P) v = (q0 + q == 0) ? pv[q] : v + pv[q];
       }
       if (fin.bias) v += fin.bias[e];
-      lg[t * (E + 1) + e] = v;
+      lg[t * (EL + 1) + e] = v;
     }
     __syncthreads();
     // slot of every (token, expert): the number of the token's logits that
     // rank before it (value descending, ties to the lower index); one thread
     // per pair, so all tokens are ranked at once
-    for (int idx = tid; idx < T * E; idx += kThreads) {
-      const int t = idx / E, e = idx - t * E;
-      const float* row = lg + t * (E + 1);
+    for (int idx = tid; idx < T * EL; idx += kThreads) {
+      const int t = idx / EL, e = idx - t * EL;
+      const float* row = lg + t * (EL + 1);
       const float v = row[e];
       int rank = 0;
-      for (int j = 0; j < E; ++j) rank += ranks_before(row[j], j, v, e) ? 1 : 0;
+      for (int j = 0; j < EL; ++j) rank += ranks_before(row[j], j, v, e) ? 1 : 0;
       if (rank < k) s_ids[t * k + rank] = e;
     }
     __syncthreads();
     if (g == 0) {  // softmax over the chosen, adding exp(l - l_max) in slot order
       for (int idx = tid; idx < T * k; idx += kThreads) {
         const int t = idx / k, q = idx - t * k;
-        const float* row = lg + t * (E + 1);
+        const float* row = lg + t * (EL + 1);
         const float vmax = row[s_ids[t * k]];
         float tot = 0.f, mine = 0.f;
         for (int j = 0; j < k; ++j) {
@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
       }
     }
   }
-  auto id_of = [&](int a) { return fin.partial ? s_ids[a] : ids[a]; };
+  // group of assignment a (ids are global; this call holds experts id_base ..)
+  auto id_of = [&](int a) { return (fin.partial ? s_ids[a] : ids[a]) - id_base; };
 
   for (int i = tid; i < G; i += kThreads) hist[i] = (i == E) ? shared_rows : 0;
   __syncthreads();
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
 
 }  // namespace
 
-hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int shared_rows,
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int id_base, int BM, int shared_rows,
                         int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
                         int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
                         const RouteFinish* fin, hipStream_t s) {
@@ -168,9 +169,9 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int sha
   RouteFinish f{};
   size_t lds = 0;
   if (fin) {
-    if (T > kSmallRouteT || k > 8 || E > kSmallRouteE) return hipErrorInvalidValue;
+    if (T > kSmallRouteT || k > 8 || fin->E > kSmallRouteE) return hipErrorInvalidValue;
     f = *fin;
-    lds = sizeof(float) * (size_t)T * (E + 1);
+    lds = sizeof(float) * (size_t)T * (fin->E + 1);
     static bool attr_set = false;
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)moe_align_kernel,
@@ -180,7 +181,7 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int sha
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL(moe_align_kernel, dim3(G), dim3(kThreads), lds, s, ids, T * k, k, E, BM,
+  hipLaunchKernelGGL(moe_align_kernel, dim3(G), dim3(kThreads), lds, s, ids, T * k, k, E, id_base, BM,
                      shared_rows, counts, offsets, padded, sorted_assign, row_of, row_token,
                      tile_group, n_tiles, f);
   return hipGetLastError();

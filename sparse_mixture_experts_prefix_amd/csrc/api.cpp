@@ -73,7 +73,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
     if (e0 != hipSuccess) return hip_fail(e0);
   }
 
-  hipError_t e = launch_align(ids, (int)P.T, (int)P.k, (int)P.E, P.BM, shared_rows, counts, offsets,
+  hipError_t e = launch_align(ids, (int)P.T, (int)P.k, (int)P.E_loc, (int)P.e0, P.BM, shared_rows, counts, offsets,
                               padded, sorted, row_of, row_token, tile_group, n_tiles, fin, s);
   if (e == hipSuccess) e = mk.mark(2, s);
   if (e != hipSuccess) return hip_fail(e);
@@ -84,7 +84,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   gu.lda = P.D;
   gu.B_routed = static_cast<const uint16_t*>(w->w_gate_up);
   gu.B_shared = static_cast<const uint16_t*>(w->ws_gate_up);
-  gu.E = (int)P.E;
+  gu.E = (int)P.E_loc;
   gu.N_routed = (int)P.F;
   gu.N_shared = (int)P.Fs;
   gu.K_routed = (int)P.D;
@@ -122,7 +122,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   if (e == hipSuccess) e = mk.mark(4, s);
   if (e != hipSuccess) return hip_fail(e);
 
-  e = launch_combine(Yp, row_of, wts, padded, (int)P.T, (int)P.D, (int)P.k, (int)P.E,
+  e = launch_combine(Yp, row_of, wts, padded, (int)P.T, (int)P.D, (int)P.k, (int)P.E_loc,
                      P.Fs > 0 ? 1 : 0, y, s);
   if (e == hipSuccess) e = mk.mark(5, s);
   if (e != hipSuccess) return hip_fail(e);
@@ -180,7 +180,7 @@ static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, 
                                      (int)P.E, rpart, s);
     if (e == hipSuccess) e = mk.mark(1, s);
     if (e != hipSuccess) return hip_fail(e);
-    const moe::RouteFinish fin{rpart, moe::router_parts(P.D), bias, ids, wts};
+    const moe::RouteFinish fin{rpart, moe::router_parts(P.D), (int)P.E, bias, ids, wts};
     return run_experts(P, w, ids, wts, y, workspace, s, mk, &fin);
   }
   if (e == hipSuccess)
@@ -235,7 +235,7 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t 
   if (!counts || !offsets || !padded_offsets || !row_token || !tile_group || !n_tiles)
     return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !sorted_assign || !row_of)) return MOE_ERR_INVALID_ARG;
-  hipError_t e = moe::launch_align(topk_ids, T, k, E, block_m, shared_rows, counts, offsets,
+  hipError_t e = moe::launch_align(topk_ids, T, k, E, 0, block_m, shared_rows, counts, offsets,
                                    padded_offsets, sorted_assign, row_of, row_token, tile_group,
                                    n_tiles, nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);

@@ -21,14 +21,16 @@ hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w_g, int T, 
 struct RouteFinish {
   const float* partial;  // [P][T][E]
   int P;
+  int E;                 // experts the router scores (all of them, also for a shard)
   const float* bias;     // fp32 [E] or NULL
   int32_t* ids;          // top-k ids out [T, k]
   float* wts;            // top-k weights out [T, k]
 };
 
 // Expert grouping of the assignments (see moe_align in moe.h).
+// E groups hold experts id_base .. id_base+E-1 (ids outside get no row).
 // With fin != NULL the ids come from fin (T <= kSmallRouteT) and `ids` is unused.
-hipError_t launch_align(const int32_t* ids, int T, int k, int E, int BM, int shared_rows,
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int id_base, int BM, int shared_rows,
                         int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
                         int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
                         const RouteFinish* fin, hipStream_t s);

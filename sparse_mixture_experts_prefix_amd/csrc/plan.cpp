@@ -13,6 +13,10 @@ int check_shape(const moe_shape* s) {
   if (s->T < 0 || s->D <= 0 || s->E <= 0 || s->F <= 0 || s->k <= 0 || s->F_shared < 0)
     return MOE_ERR_INVALID_ARG;
   if (s->k > s->E) return MOE_ERR_INVALID_ARG;
+  if (s->expert_begin < 0 || s->num_local_experts < 0 ||
+      (int64_t)s->expert_begin + s->num_local_experts > s->E ||
+      (s->num_local_experts == 0 && s->expert_begin != 0))
+    return MOE_ERR_INVALID_ARG;
   if (s->D % 8 || s->F % 8 || s->F_shared % 8) return MOE_ERR_INVALID_ARG;
   if (s->E > 256 || s->k > 8) return MOE_ERR_UNSUPPORTED;
   // every padded row index and every x/y element offset per row must fit 32 bits
@@ -46,7 +50,9 @@ int make_plan(const moe_shape* s, Plan* p) {
   p->F = s->F;
   p->k = s->k;
   p->Fs = s->F_shared;
-  p->G = s->E + (s->F_shared > 0 ? 1 : 0);
+  p->e0 = s->expert_begin;
+  p->E_loc = s->num_local_experts > 0 ? s->num_local_experts : s->E;
+  p->G = (int)p->E_loc + (s->F_shared > 0 ? 1 : 0);
   p->BM = choose_block_m(s);
   p->A = p->T * p->k;
   p->cap_rows = p->A + (int64_t)p->G * (p->BM - 1) + (p->Fs > 0 ? p->T : 0);

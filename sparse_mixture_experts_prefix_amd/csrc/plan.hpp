@@ -25,7 +25,8 @@ constexpr int64_t kPartialTileFloats = 256 * 256;
 // Row-tile height of the grouped GEMMs and the per-call workspace layout.
 struct Plan {
   int64_t T, D, E, F, k, Fs;
-  int G;              // groups: E routed (+1 shared)
+  int64_t e0, E_loc;  // experts held by this call: e0 .. e0+E_loc-1 (all E unless sharded)
+  int G;              // groups: E_loc routed (+1 shared)
   int BM;             // row-tile height; every group is padded to a multiple of it
   int64_t A;          // assignments T*k
   int64_t cap_rows;   // upper bound of padded rows over all groups

@@ -66,6 +66,11 @@ def _fwd(lib, shape, w, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
     (dict(k=3, E=2), B.MOE_ERR_INVALID_ARG), (dict(E=257), B.MOE_ERR_UNSUPPORTED),
     (dict(D=100), B.MOE_ERR_INVALID_ARG), (dict(F=12), B.MOE_ERR_INVALID_ARG),
     (dict(T=-1), B.MOE_ERR_INVALID_ARG), (dict(F_shared=4), B.MOE_ERR_INVALID_ARG),
+    # expert-parallel shards: the held range must lie inside [0, E)
+    (dict(expert_begin=6, num_local_experts=3), B.MOE_ERR_INVALID_ARG),
+    (dict(expert_begin=-1, num_local_experts=2), B.MOE_ERR_INVALID_ARG),
+    (dict(expert_begin=2, num_local_experts=0), B.MOE_ERR_INVALID_ARG),
+    (dict(num_local_experts=-1), B.MOE_ERR_INVALID_ARG),
     (dict(T=1 << 30, k=8), B.MOE_ERR_UNSUPPORTED)])
 def test_shape_errors(lib, kw, code):
     assert _fwd(lib, _shape(**kw), _weights()) == code
@@ -113,6 +118,23 @@ def test_align_argument_errors(lib):
     assert lib.moe_align(P, 10, 2, 8, 0, 0, P, P, P, P, P, P, P, P, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_align(P, 10, 9, 16, 16, 0, P, P, P, P, P, P, P, P, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_align(P, 10, 2, 8, 16, 0, None, P, P, P, P, P, P, P, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_shape_struct_matches_header():
+    """moe_shape is nine int32 fields in the header's order."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct moe_shape \{(.*?)\} moe_shape;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"int32_t\s+(\w+);", body)
+    assert names == [f[0] for f in B.Shape._fields_]
+    assert ctypes.sizeof(B.Shape) == 4 * len(names)
+
+
+def test_shard_workspace_is_smaller(lib):
+    full = B.workspace_size(_shape(T=4096, E=64, k=2))
+    shard = B.workspace_size(_shape(T=4096, E=64, k=2, expert_begin=8, num_local_experts=8))
+    assert 0 < shard < full
+    assert B.workspace_size(_shape(T=4096, E=64, k=2, expert_begin=0, num_local_experts=64)) == full
 
 
 def test_strerror(lib):

@@ -2,6 +2,8 @@
 
 Every call goes through the C ABI (libmoe.so) via the ctypes binding.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -202,6 +204,53 @@ def test_layer_split_last_round(T, D, E, k, F, Fs):
         assert s_dn >= 2  # the down GEMM is the one cut for these shapes
     print("m-tiles %d: gate/up S=%d, down S=%d" % (mt, s_gu, s_dn))
     assert max(s_gu, s_dn) >= 2
+
+
+def _shard_inputs(inp, a, b, with_shared):
+    return W.LayerInputs(inp.shape if with_shared else dataclasses.replace(inp.shape, Fs=0), inp.x,
+                         inp.w_g, inp.w_gate_up[a:b].contiguous(), inp.w_down[a:b].contiguous(),
+                         inp.router_bias, inp.ws_gate_up if with_shared else None,
+                         inp.ws_down if with_shared else None)
+
+
+@pytest.mark.parametrize("T,D,E,k,F,Fs,bounds", [
+    (300, 256, 8, 2, 384, 64, [0, 2, 4, 6, 8]),                  # 256-row tiles, shared on shard 0
+    (64, 2880, 32, 4, 2880, 0, [0, 4, 8, 12, 16, 20, 24, 28, 32]),  # gpt-oss decode over 8 shards
+    (2048, 512, 8, 2, 1024, 0, [0, 3, 8]),                        # uneven shards, K-split tail
+    (5, 128, 8, 2, 256, 0, [0, 1, 7, 8]),                         # shards that get no token
+    (700, 512, 64, 8, 256, 256, [0, 16, 48, 64]),                 # 64 experts, top-8, shared
+])
+def test_layer_expert_shards(T, D, E, k, F, Fs, bounds):
+    """Expert-parallel shards: each call holds a slice of the experts; its y
+    matches the oracle's shard under the same routing, every shard routes
+    identically, and the shards' y add up to the whole layer's."""
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs)
+    inp = W.make_inputs(s, seed=T + 3 * E)
+    g = _gpu(inp)
+    y_full, ids_full, w_full = _forward(inp)
+    ids_or, p_or, margin, logits = oracle.route(inp.x, inp.w_g, None, k)
+    check_routing(ids_full, w_full, ids_or, p_or, margin, logits, k)
+    y_or = oracle.experts(inp, ids_full, w_full.astype(np.float64))
+    rms = float(np.sqrt(np.mean(np.square(y_or))))
+    total = np.zeros_like(y_full, dtype=np.float64)
+    for r, (a, b) in enumerate(zip(bounds[:-1], bounds[1:])):
+        sh = r == 0
+        ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        y = moe.moe_forward(g.x, g.w_g, g.w_gate_up[a:b].contiguous(), g.w_down[a:b].contiguous(), k,
+                            None, g.ws_gate_up if sh else None, g.ws_down if sh else None,
+                            topk_ids=ids, topk_w=w, expert_begin=a)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), ids_full) and np.array_equal(w.cpu().numpy(), w_full)
+        ref = oracle.experts(_shard_inputs(inp, a, b, sh), ids_full, w_full.astype(np.float64),
+                             expert_begin=a, n_local=b - a)
+        err = float(np.max(np.abs(y.cpu().numpy().astype(np.float64) - ref)))
+        print("shard %d [%d, %d): max|err|/RMS(layer) = %.4g" % (r, a, b, err / rms))
+        assert err <= 2e-2 * rms
+        total += y.cpu().numpy()
+    # not bitwise: a shard's tile count changes the K-split of its GEMMs, and a
+    # different fp32 summation order can move H by one bf16 ulp (2^-8)
+    assert float(np.max(np.abs(total - y_full))) <= 1e-2 * rms
 
 
 def test_layer_E1_k1_dense_ffn():
