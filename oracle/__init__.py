@@ -59,6 +59,9 @@ def _load():
             lib = ctypes.CDLL(_LIB_PATH)
             lib.oracle_route.restype = ctypes.c_int
             lib.oracle_route.argtypes = [_p, _p, _p, _i64, _i32, _i32, _i32, _p, _p, _p, _p]
+            lib.oracle_route_mode.restype = ctypes.c_int
+            lib.oracle_route_mode.argtypes = [_p, _p, _p, _i32, _i64, _i32, _i32, _i32, _p, _p, _p,
+                                              _p]
             lib.oracle_experts.restype = ctypes.c_int
             lib.oracle_experts.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p,
                                            _p, _i64, _p, _p]
@@ -66,8 +69,8 @@ def _load():
             lib.oracle_experts_shard.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                                  _i32, _i32, _p, _p, _p, _i64, _p, _p]
             lib.oracle_forward.restype = ctypes.c_int
-            lib.oracle_forward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i32,
-                                           _i32, _p, _p, _p, _p]
+            lib.oracle_forward.argtypes = [_p, _p, _p, _i32, _p, _p, _p, _p, _i64, _i32, _i32, _i32,
+                                           _i32, _i32, _p, _p, _p, _p]
             lib.oracle_align.restype = ctypes.c_int
             lib.oracle_align.argtypes = [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
                                          _i64, _p, _p]
@@ -102,10 +105,19 @@ def _f32_ptr(t):
     return t.data_ptr(), t
 
 
-def route(x, w_g, router_bias, k: int):
-    """Router for every row of x.
+def bias_mode(router_bias, select_only: bool) -> int:
+    """0 no bias, 1 bias inside the logits, 2 selection-only bias."""
+    if router_bias is None:
+        return 0
+    return 2 if select_only else 1
 
-    Returns (ids int32 [T,k], p float64 [T,k], margin float64 [T], logits float32 [T,E]).
+
+def route(x, w_g, router_bias, k: int, select_only: bool = False):
+    """Router for every row of x.  With select_only the bias moves only the
+    top-k selection; the weights are the softmax of the plain chosen logits.
+
+    Returns (ids int32 [T,k], p float64 [T,k], margin float64 [T] on the
+    selection keys, logits float32 [T,E] without a selection-only bias).
     """
     lib = _load()
     T, D = x.shape
@@ -117,10 +129,11 @@ def route(x, w_g, router_bias, k: int):
     ids = np.empty((T, k), np.int32)
     p = np.empty((T, k), np.float64)
     margin = np.empty((T,), np.float64)
-    rc = lib.oracle_route(px, pw, pb, T, D, E, k, logits.ctypes.data, ids.ctypes.data,
-                          p.ctypes.data, margin.ctypes.data)
+    rc = lib.oracle_route_mode(px, pw, pb, bias_mode(router_bias, select_only), T, D, E, k,
+                               logits.ctypes.data, ids.ctypes.data, p.ctypes.data,
+                               margin.ctypes.data)
     if rc:
-        raise ValueError("oracle_route failed: %d" % rc)
+        raise ValueError("oracle_route_mode failed: %d" % rc)
     return ids, p, margin, logits
 
 
@@ -183,7 +196,8 @@ def forward(inp):
     p = np.empty((T, s.k), np.float64)
     margin = np.empty((T,), np.float64)
     y = np.empty((T, s.D), np.float64)
-    rc = lib.oracle_forward(px, pg, pb, pgu, pdn, psgu, psdn, T, s.D, s.E, s.F, s.k, s.Fs,
+    mode = bias_mode(inp.router_bias, s.bias_select)
+    rc = lib.oracle_forward(px, pg, pb, mode, pgu, pdn, psgu, psdn, T, s.D, s.E, s.F, s.k, s.Fs,
                             ids.ctypes.data, p.ctypes.data, margin.ctypes.data, y.ctypes.data)
     if rc:
         raise ValueError("oracle_forward failed: %d" % rc)

@@ -80,16 +80,17 @@ static void token_logits(const uint16_t* xt, const uint16_t* w_g, const float* b
   }
 }
 
-/* Top-k by (logit descending, index ascending), then softmax over the chosen.
- * margin = l_(k) - l_(k+1) with 1-based order statistics (+inf when k == E). */
-static void token_topk_softmax(const float* l, int32_t E, int32_t k, unsigned char* taken,
-                               int32_t* ids, double* p, double* margin) {
+/* Top-k by (key descending, index ascending), then softmax of the values l
+ * over the chosen.  key == l unless a selection-only bias is in use.
+ * margin = key_(k) - key_(k+1) with 1-based order statistics (+inf when k == E). */
+static void token_topk_softmax(const float* key, const float* l, int32_t E, int32_t k,
+                               unsigned char* taken, int32_t* ids, double* p, double* margin) {
   memset(taken, 0, (size_t)E);
   for (int32_t j = 0; j < k; ++j) {
     int32_t best = -1;
     for (int32_t e = 0; e < E; ++e) {
       if (taken[e]) continue;
-      if (best < 0 || l[e] > l[best]) best = e; /* strict: the lower index wins ties */
+      if (best < 0 || key[e] > key[best]) best = e; /* strict: the lower index wins ties */
     }
     taken[best] = 1;
     ids[j] = best;
@@ -100,11 +101,13 @@ static void token_topk_softmax(const float* l, int32_t E, int32_t k, unsigned ch
     } else {
       int32_t next = -1;
       for (int32_t e = 0; e < E; ++e)
-        if (!taken[e] && (next < 0 || l[e] > l[next])) next = e;
-      *margin = (double)l[ids[k - 1]] - (double)l[next];
+        if (!taken[e] && (next < 0 || key[e] > key[next])) next = e;
+      *margin = (double)key[ids[k - 1]] - (double)key[next];
     }
   }
   double m = (double)l[ids[0]];
+  for (int32_t j = 1; j < k; ++j)
+    if ((double)l[ids[j]] > m) m = (double)l[ids[j]];
   double s[256];
   double tot = 0.0;
   for (int32_t j = 0; j < k; ++j) {
@@ -116,33 +119,53 @@ static void token_topk_softmax(const float* l, int32_t E, int32_t k, unsigned ch
 
 /*
  * Route T tokens.
- *   x [T,D] bf16, w_g [E,D] bf16, bias [E] fp32 or NULL
- *   logits [T,E] fp32 out or NULL; ids [T,k] out; p [T,k] out; margin [T] out or NULL
- * Returns 0, or -1 on an invalid size.
+ *   x [T,D] bf16, w_g [E,D] bf16, bias [E] fp32 (NULL exactly when bias_mode == 0)
+ *   bias_mode 1: the bias is part of the logit (it moves selection and weights).
+ *   bias_mode 2: selection-only bias, the auxiliary-loss-free load balancer of
+ *     the glossary "MoE (Mixture of Experts - Mezcla de Expertos)", section 2,
+ *     item 4: the top-k is taken on key = fp32(l + b) (one fp32 add of the fp32
+ *     logit and the bias), while the softmax runs over the plain logits l of
+ *     the chosen experts, so the bias steers the load and never the weights.
+ *   logits [T,E] fp32 out (the plain logits l) or NULL; ids [T,k] out;
+ *   p [T,k] out; margin [T] out or NULL (taken on the selection keys)
+ * Returns 0, or -1 on an invalid size or mode.
  */
-int oracle_route(const uint16_t* x, const uint16_t* w_g, const float* bias, int64_t T, int32_t D,
-                 int32_t E, int32_t k, float* logits, int32_t* ids, double* p, double* margin) {
+int oracle_route_mode(const uint16_t* x, const uint16_t* w_g, const float* bias, int32_t bias_mode,
+                      int64_t T, int32_t D, int32_t E, int32_t k, float* logits, int32_t* ids,
+                      double* p, double* margin) {
   if (T < 0 || D <= 0 || E <= 0 || E > 256 || k <= 0 || k > E) return -1;
+  if (bias_mode < 0 || bias_mode > 2 || (bias_mode != 0) != (bias != NULL)) return -1;
   int err = 0;
 #pragma omp parallel
   {
     float* l = (float*)malloc(sizeof(float) * (size_t)E);
+    float* key = (float*)malloc(sizeof(float) * (size_t)E);
     unsigned char* taken = (unsigned char*)malloc((size_t)E);
-    if (!l || !taken) {
+    if (!l || !key || !taken) {
 #pragma omp atomic write
       err = -2;
     } else {
 #pragma omp for schedule(dynamic, 4)
       for (int64_t t = 0; t < T; ++t) {
-        token_logits(x + t * D, w_g, bias, D, E, l);
+        token_logits(x + t * D, w_g, bias_mode == 1 ? bias : NULL, D, E, l);
         if (logits) memcpy(logits + t * E, l, sizeof(float) * (size_t)E);
-        token_topk_softmax(l, E, k, taken, ids + t * k, p + t * k, margin ? margin + t : NULL);
+        if (bias_mode == 2)
+          for (int32_t e = 0; e < E; ++e) key[e] = l[e] + bias[e]; /* fp32 add */
+        token_topk_softmax(bias_mode == 2 ? key : l, l, E, k, taken, ids + t * k, p + t * k,
+                           margin ? margin + t : NULL);
       }
     }
     free(l);
+    free(key);
     free(taken);
   }
   return err;
+}
+
+/* oracle_route_mode with the bias, when given, part of the logits (mode 1). */
+int oracle_route(const uint16_t* x, const uint16_t* w_g, const float* bias, int64_t T, int32_t D,
+                 int32_t E, int32_t k, float* logits, int32_t* ids, double* p, double* margin) {
+  return oracle_route_mode(x, w_g, bias, bias ? 1 : 0, T, D, E, k, logits, ids, p, margin);
 }
 
 /* ----------------------------------------------------------------- experts */
@@ -236,13 +259,13 @@ int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t*
 
 /*
  * Whole layer for T tokens: route every token, then run its experts.
- * ids/p/margin outputs as in oracle_route; y [T,D] double.
+ * bias/bias_mode and ids/p/margin as in oracle_route_mode; y [T,D] double.
  */
-int oracle_forward(const uint16_t* x, const uint16_t* w_g, const float* bias,
+int oracle_forward(const uint16_t* x, const uint16_t* w_g, const float* bias, int32_t bias_mode,
                    const uint16_t* w_gate_up, const uint16_t* w_down, const uint16_t* ws_gate_up,
                    const uint16_t* ws_down, int64_t T, int32_t D, int32_t E, int32_t F, int32_t k,
                    int32_t Fs, int32_t* ids, double* p, double* margin, double* y) {
-  int rc = oracle_route(x, w_g, bias, T, D, E, k, NULL, ids, p, margin);
+  int rc = oracle_route_mode(x, w_g, bias, bias_mode, T, D, E, k, NULL, ids, p, margin);
   if (rc) return rc;
   return oracle_experts(x, w_gate_up, w_down, ws_gate_up, ws_down, D, E, F, k, Fs, ids, p, NULL, T,
                         y, NULL);

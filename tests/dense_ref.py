@@ -18,18 +18,26 @@ def f64(t):
 
 
 def dense_logits(inp):
+    """fp32 logits; a bias in the logits is added before the rounding, a
+    selection-only bias is not added at all."""
     X = f64(inp.x)
     l = X @ f64(inp.w_g).T
-    if inp.router_bias is not None:
+    if inp.router_bias is not None and not inp.shape.bias_select:
         l = l + inp.router_bias.to(torch.float64).numpy()[None, :]
     # the selection is defined on fp32 logits
     return l.astype(np.float32).astype(np.float64)
 
 
 def dense_routing(inp):
+    """Top-k by stable argsort of the selection keys, softmax of the logits.
+    With a selection-only bias the keys are the fp32 sum logit + bias."""
     l = dense_logits(inp)
+    key = l
+    if inp.router_bias is not None and inp.shape.bias_select:
+        b = inp.router_bias.numpy().astype(np.float32)
+        key = (l.astype(np.float32) + b[None, :]).astype(np.float64)
     k = inp.shape.k
-    ids = np.argsort(-l, axis=1, kind="stable")[:, :k]
+    ids = np.argsort(-key, axis=1, kind="stable")[:, :k]
     chosen = np.take_along_axis(l, ids, axis=1)
     p = sps.softmax(chosen, axis=1)
     return ids, p, l

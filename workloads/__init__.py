@@ -41,6 +41,7 @@ TAG_W_DOWN = 3
 TAG_WS_GATE_UP = 4
 TAG_WS_DOWN = 5
 TAG_X = 6
+TAG_ROUTER_BIAS = 7
 
 WEIGHT_STD = 0.02
 X_STD = 1.0
@@ -121,6 +122,9 @@ class Shape:
     F: int
     Fs: int = 0
     router_bias: bool = False
+    # the router bias only moves the top-k selection, not the weights
+    # (auxiliary-loss-free load balancing); needs router_bias
+    bias_select: bool = False
 
     def with_T(self, T: int) -> "Shape":
         return dataclasses.replace(self, T=T)
@@ -142,6 +146,25 @@ def skew_bias(E: int) -> torch.Tensor:
     assignments.
     """
     return torch.tensor([-3.6 * math.log(e + 1.0) for e in range(E)], dtype=torch.float32)
+
+
+BALANCE_BIAS_STD = 0.5
+
+
+def balance_bias(E: int, seed: int = 0) -> torch.Tensor:
+    """Per-expert selection bias of the load-balancing mode: N(0, 0.5^2) fp32,
+    drawn from stream (seed, TAG_ROUTER_BIAS).  Its spread is a fraction of
+    the logits' (about 1 to 1.7 for the shapes here), so it moves a share of
+    the selections without dominating them."""
+    return normal_f32((E,), seed, TAG_ROUTER_BIAS, BALANCE_BIAS_STD)
+
+
+def router_bias_for(shape: Shape, seed: int = 0) -> torch.Tensor | None:
+    """The bias input a shape asks for: none, the skew bias (part of the
+    logits) or the balancing bias (selection only)."""
+    if not shape.router_bias:
+        return None
+    return balance_bias(shape.E, seed) if shape.bias_select else skew_bias(shape.E)
 
 
 WORKLOADS = {
@@ -189,7 +212,7 @@ def make_weights(shape: Shape, seed: int = 0, std: float = WEIGHT_STD) -> LayerI
     if Fs:
         ws_gu = normal_bf16((2 * Fs, D), seed, TAG_WS_GATE_UP, std)
         ws_d = normal_bf16((D, Fs), seed, TAG_WS_DOWN, std)
-    bias = skew_bias(E) if shape.router_bias else None
+    bias = router_bias_for(shape, seed)
     return LayerInputs(shape, torch.empty((0, D), dtype=torch.bfloat16), w_g, w_gu, w_d, bias, ws_gu, ws_d)
 
 
@@ -214,7 +237,7 @@ def make_grid_inputs(shape: Shape, seed: int = 0) -> LayerInputs:
         ws_d = grid_bf16((D, Fs), seed, TAG_WS_DOWN)
     return LayerInputs(shape, grid_bf16((shape.T, D), seed, TAG_X), grid_bf16((E, D), seed, TAG_W_G),
                        grid_bf16((E, 2 * F, D), seed, TAG_W_GATE_UP), grid_bf16((E, D, F), seed, TAG_W_DOWN),
-                       skew_bias(E) if shape.router_bias else None, ws_gu, ws_d)
+                       router_bias_for(shape, seed), ws_gu, ws_d)
 
 
 # ---------------------------------------------------------------- size counts
