@@ -27,8 +27,14 @@
  *    current device and must be 16-byte aligned.
  *  - x         bf16 [T, D]
  *  - w_g       bf16 [E, D]        router weight, one row per expert
- *  - router_bias fp32 [E] or NULL added to the fp32 router logits before
- *              the selection and the softmax
+ *  - router_bias fp32 [E] or NULL.  has_router_bias == MOE_ROUTER_BIAS_LOGITS:
+ *              added to the fp32 router logits before the selection and the
+ *              softmax.  MOE_ROUTER_BIAS_SELECT: the load balancer without an
+ *              auxiliary loss of the glossary "MoE (Mixture of Experts -
+ *              Mezcla de Expertos)", section 2 item 4 (per-expert router
+ *              biases): the top-k is taken on the fp32 sum logit + bias, the
+ *              weights are the softmax of the plain logits of the chosen
+ *              experts, so the bias moves the load and not the weights
  *  - w_gate_up bf16 [E, 2F, D]    rows 0..F-1 of expert e are the activated
  *              (SiLU) projection, rows F..2F-1 the one it multiplies
  *  - w_down    bf16 [E, D, F]
@@ -71,6 +77,11 @@ enum {
   MOE_ERR_HIP = -5          /* a HIP launch failed; moe_strerror gives HIP's text */
 };
 
+/* moe_shape.has_router_bias (any other value: MOE_ERR_INVALID_ARG) */
+#define MOE_ROUTER_BIAS_NONE 0   /* no bias; router_bias is not read */
+#define MOE_ROUTER_BIAS_LOGITS 1 /* bias inside the logits: selection and weights */
+#define MOE_ROUTER_BIAS_SELECT 2 /* bias for the top-k selection only */
+
 typedef struct moe_shape {
   int32_t T;               /* tokens */
   int32_t D;               /* model width */
@@ -78,7 +89,7 @@ typedef struct moe_shape {
   int32_t F;               /* routed expert hidden width (d_ff) */
   int32_t k;               /* experts per token */
   int32_t F_shared;        /* shared expert hidden width, 0 = none */
-  int32_t has_router_bias; /* nonzero: weights->router_bias is used */
+  int32_t has_router_bias; /* MOE_ROUTER_BIAS_*: how weights->router_bias is used */
   /* Expert-parallel shard ("Mixture of Experts optimiza Transformers y LLMs",
    * section "Expert Parallelism"; "Transformers v5 El Secreto Detrás de los
    * Modelos MoE Más Rápidos", section "Paralelismo de Expertos").  With
@@ -95,7 +106,7 @@ typedef struct moe_shape {
 typedef struct moe_weights {
   const void* x;            /* bf16 [T, D] */
   const void* w_g;          /* bf16 [E, D] */
-  const float* router_bias; /* fp32 [E], or NULL when has_router_bias == 0 */
+  const float* router_bias; /* fp32 [E], or NULL with MOE_ROUTER_BIAS_NONE */
   const void* w_gate_up;    /* bf16 [E, 2F, D] ([num_local_experts, 2F, D] for a shard) */
   const void* w_down;       /* bf16 [E, D, F] ([num_local_experts, D, F] for a shard) */
   const void* ws_gate_up;   /* bf16 [2*F_shared, D] or NULL */

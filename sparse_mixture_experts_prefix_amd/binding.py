@@ -108,11 +108,28 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def make_shape(T, D, E, F, k, F_shared=0, has_router_bias=False, expert_begin=0,
+# moe_shape.has_router_bias values
+ROUTER_BIAS_NONE = 0
+ROUTER_BIAS_LOGITS = 1   # the bias is part of the logits
+ROUTER_BIAS_SELECT = 2   # the bias moves the top-k selection only
+
+
+def bias_mode(router_bias, bias_select: bool) -> int:
+    """has_router_bias for a call given its bias tensor (or None)."""
+    if router_bias is None:
+        if bias_select:
+            raise ValueError("bias_select needs a router_bias")
+        return ROUTER_BIAS_NONE
+    return ROUTER_BIAS_SELECT if bias_select else ROUTER_BIAS_LOGITS
+
+
+def make_shape(T, D, E, F, k, F_shared=0, has_router_bias=0, expert_begin=0,
                num_local_experts=0) -> Shape:
-    """moe_shape; num_local_experts > 0 makes the call one expert-parallel
+    """moe_shape; has_router_bias is a ROUTER_BIAS_* value (a bool means
+    none / logits); num_local_experts > 0 makes the call one expert-parallel
     shard holding experts expert_begin .. expert_begin+num_local_experts-1."""
-    return Shape(int(T), int(D), int(E), int(F), int(k), int(F_shared), 1 if has_router_bias else 0,
+    mode = (1 if has_router_bias else 0) if isinstance(has_router_bias, bool) else int(has_router_bias)
+    return Shape(int(T), int(D), int(E), int(F), int(k), int(F_shared), mode,
                  int(expert_begin), int(num_local_experts))
 
 
@@ -172,8 +189,12 @@ def _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down):
 
 
 def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None, ws_down=None, *,
-                y=None, topk_ids=None, topk_w=None, workspace=None, expert_begin=None):
+                y=None, topk_ids=None, topk_w=None, workspace=None, expert_begin=None,
+                bias_select=False):
     """Whole MoE layer.  Returns y (fp32 [T, D]).
+
+    bias_select: router_bias moves only the top-k selection (load balancing);
+    the weights are the softmax of the plain chosen logits.
 
     Optional preallocated outputs (y, topk_ids int32 [T,k], topk_w fp32 [T,k])
     and workspace (uint8, >= workspace_size bytes) avoid any allocation here.
@@ -189,7 +210,8 @@ def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None,
         raise ValueError("w_gate_up holds %d of %d experts: pass expert_begin" % (E_loc, E))
     if router_bias is not None:
         _dev(router_bias, "router_bias", torch.float32, (E,))
-    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, router_bias is not None, E, expert_begin)
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, bias_mode(router_bias, bias_select), E,
+                         expert_begin)
     if y is None:
         y = torch.empty((T, D), dtype=torch.float32, device=x.device)
     _dev(y, "y", torch.float32, (T, D))
@@ -207,7 +229,7 @@ def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None,
     return y
 
 
-def moe_route(x, w_g, k, router_bias=None, *, topk_ids=None, topk_w=None):
+def moe_route(x, w_g, k, router_bias=None, *, topk_ids=None, topk_w=None, bias_select=False):
     """Router only.  Returns (topk_ids int32 [T,k], topk_w fp32 [T,k])."""
     _dev(x, "x", torch.bfloat16)
     T, D = x.shape
@@ -222,7 +244,7 @@ def moe_route(x, w_g, k, router_bias=None, *, topk_ids=None, topk_w=None):
         topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     _dev(topk_ids, "topk_ids", torch.int32, (T, k))
     _dev(topk_w, "topk_w", torch.float32, (T, k))
-    shape = make_shape(T, D, E, 8, k, 0, router_bias is not None)
+    shape = make_shape(T, D, E, 8, k, 0, bias_mode(router_bias, bias_select))
     w = Weights(_ptr(x), _ptr(w_g), _ptr(router_bias), None, None, None, None)
     _check(load_library().moe_route(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids),
                                     _ptr(topk_w), _stream(x.device)))
@@ -317,10 +339,10 @@ class HipEvents:
 
 def moe_forward_timed(events: HipEvents, x, w_g, w_gate_up, w_down, k, router_bias=None,
                       ws_gate_up=None, ws_down=None, *, y, topk_ids, topk_w, workspace,
-                      expert_begin=None):
+                      expert_begin=None, bias_select=False):
     """moe_forward recording events[0..5] around its five kernels (all buffers preallocated)."""
     T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
-    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, router_bias is not None,
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, bias_mode(router_bias, bias_select),
                          w_g.shape[0], expert_begin)
     w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
     lib = load_library()

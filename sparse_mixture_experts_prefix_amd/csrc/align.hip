@@ -42,8 +42,10 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
     // logits of all T <= kSmallRouteT tokens (part order, then the bias),
     // picks each token's top-k (E <= kSmallRouteE) and keeps the ids in LDS;
     // workgroup 0 also stores ids and weights.
-    extern __shared__ float lg[];  // [T][EL + 1]
+    // [T][EL + 1] logits, then (selection-only bias) [T][EL + 1] top-k keys
+    extern __shared__ float lg[];
     const int T = A / k, EL = fin.E;
+    float* const key = fin.sel ? lg + T * (EL + 1) : lg;
     for (int idx = tid; idx < T * EL; idx += kThreads) {
       const int t = idx / EL, e = idx - t * EL;
       const float* src = fin.partial + (int64_t)t * EL + e;
@@ -59,25 +61,27 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
       }
       if (fin.bias) v += fin.bias[e];
       lg[t * (EL + 1) + e] = v;
+      if (fin.sel) key[t * (EL + 1) + e] = v + fin.sel[e];
     }
     __syncthreads();
-    // slot of every (token, expert): the number of the token's logits that
-    // rank before it (value descending, ties to the lower index); one thread
-    // per pair, so all tokens are ranked at once
+    // slot of every (token, expert): the number of the token's keys that
+    // rank before its own (value descending, ties to the lower index); one
+    // thread per pair, so all tokens are ranked at once
     for (int idx = tid; idx < T * EL; idx += kThreads) {
       const int t = idx / EL, e = idx - t * EL;
-      const float* row = lg + t * (EL + 1);
+      const float* row = key + t * (EL + 1);
       const float v = row[e];
       int rank = 0;
       for (int j = 0; j < EL; ++j) rank += ranks_before(row[j], j, v, e) ? 1 : 0;
       if (rank < k) s_ids[t * k + rank] = e;
     }
     __syncthreads();
-    if (g == 0) {  // softmax over the chosen, adding exp(l - l_max) in slot order
+    if (g == 0) {  // softmax over the chosen logits, adding exp(l - l_max) in slot order
       for (int idx = tid; idx < T * k; idx += kThreads) {
         const int t = idx / k, q = idx - t * k;
         const float* row = lg + t * (EL + 1);
-        const float vmax = row[s_ids[t * k]];
+        float vmax = row[s_ids[t * k]];
+        for (int j = 1; j < k; ++j) vmax = fmaxf(vmax, row[s_ids[t * k + j]]);
         float tot = 0.f, mine = 0.f;
         for (int j = 0; j < k; ++j) {
           const float ex = expf(row[s_ids[t * k + j]] - vmax);
@@ -171,12 +175,12 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int id_base, in
   if (fin) {
     if (T > kSmallRouteT || k > 8 || fin->E > kSmallRouteE) return hipErrorInvalidValue;
     f = *fin;
-    lds = sizeof(float) * (size_t)T * (fin->E + 1);
+    lds = sizeof(float) * (size_t)T * (fin->E + 1) * (fin->sel ? 2 : 1);
     static bool attr_set = false;
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)moe_align_kernel,
                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)(sizeof(float) * kSmallRouteT * (kSmallRouteE + 1)));
+                                         (int)(sizeof(float) * 2 * kSmallRouteT * (kSmallRouteE + 1)));
       if (e != hipSuccess) return e;
       attr_set = true;
     }

@@ -169,7 +169,8 @@ static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, 
   const Marks mk{events};
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(workspace, P.off_ids);
   float* wts = topk_w ? topk_w : at<float>(workspace, P.off_w);
-  const float* bias = shape->has_router_bias ? w->router_bias : nullptr;
+  const float* bias = shape->has_router_bias == MOE_ROUTER_BIAS_LOGITS ? w->router_bias : nullptr;
+  const float* sel = shape->has_router_bias == MOE_ROUTER_BIAS_SELECT ? w->router_bias : nullptr;
   hipError_t e = mk.mark(0, s);
   if (P.T <= moe::kSmallRouteT && P.E <= moe::kSmallRouteE) {
     // few tokens: partial logits over many workgroups, routing finished in align
@@ -180,12 +181,12 @@ static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, 
                                      (int)P.E, rpart, s);
     if (e == hipSuccess) e = mk.mark(1, s);
     if (e != hipSuccess) return hip_fail(e);
-    const moe::RouteFinish fin{rpart, moe::router_parts(P.D), (int)P.E, bias, ids, wts};
+    const moe::RouteFinish fin{rpart, moe::router_parts(P.D), (int)P.E, bias, sel, ids, wts};
     return run_experts(P, w, ids, wts, y, workspace, s, mk, &fin);
   }
   if (e == hipSuccess)
     e = moe::launch_router(static_cast<const uint16_t*>(w->x), static_cast<const uint16_t*>(w->w_g),
-                           bias, (int)P.T, (int)P.D, (int)P.E, (int)P.k, ids, wts, s);
+                           bias, sel, (int)P.T, (int)P.D, (int)P.E, (int)P.k, ids, wts, s);
   if (e == hipSuccess) e = mk.mark(1, s);
   if (e != hipSuccess) return hip_fail(e);
   return run_experts(P, w, ids, wts, y, workspace, s, mk);
@@ -214,11 +215,12 @@ int moe_route(const moe_shape* shape, const moe_weights* w, int32_t* topk_ids, f
   if (!moe::aligned16(w->x) || !moe::aligned16(w->w_g) || !moe::aligned16(topk_ids) ||
       !moe::aligned16(topk_w))
     return MOE_ERR_ALIGNMENT;
-  hipError_t e = moe::launch_router(static_cast<const uint16_t*>(w->x),
-                                    static_cast<const uint16_t*>(w->w_g),
-                                    shape->has_router_bias ? w->router_bias : nullptr, shape->T,
-                                    shape->D, shape->E, shape->k, topk_ids, topk_w,
-                                    static_cast<hipStream_t>(stream));
+  const int mode = shape->has_router_bias;
+  hipError_t e = moe::launch_router(
+      static_cast<const uint16_t*>(w->x), static_cast<const uint16_t*>(w->w_g),
+      mode == MOE_ROUTER_BIAS_LOGITS ? w->router_bias : nullptr,
+      mode == MOE_ROUTER_BIAS_SELECT ? w->router_bias : nullptr, shape->T, shape->D, shape->E,
+      shape->k, topk_ids, topk_w, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return MOE_OK;
 }

@@ -8,8 +8,9 @@
 namespace moe {
 
 // Router: logits = x W_g^T (+ bias) in fp32, top-k, softmax over the chosen.
-hipError_t launch_router(const uint16_t* x, const uint16_t* w_g, const float* bias, int T, int D,
-                         int E, int k, int32_t* ids, float* wts, hipStream_t s);
+// sel (or NULL): selection-only bias, added to the keys of the top-k only.
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_g, const float* bias, const float* sel,
+                         int T, int D, int E, int k, int32_t* ids, float* wts, hipStream_t s);
 
 // Few tokens: the router's K range is split over router_parts(D) workgroups
 // per 16 tokens, which write partial logits [P][T][E] (fp32); the align
@@ -22,7 +23,8 @@ struct RouteFinish {
   const float* partial;  // [P][T][E]
   int P;
   int E;                 // experts the router scores (all of them, also for a shard)
-  const float* bias;     // fp32 [E] or NULL
+  const float* bias;     // fp32 [E] or NULL, added to the logits
+  const float* sel;      // fp32 [E] or NULL, added to the top-k keys only
   int32_t* ids;          // top-k ids out [T, k]
   float* wts;            // top-k weights out [T, k]
 };

@@ -13,6 +13,9 @@ int check_shape(const moe_shape* s) {
   if (s->T < 0 || s->D <= 0 || s->E <= 0 || s->F <= 0 || s->k <= 0 || s->F_shared < 0)
     return MOE_ERR_INVALID_ARG;
   if (s->k > s->E) return MOE_ERR_INVALID_ARG;
+  if (s->has_router_bias != MOE_ROUTER_BIAS_NONE && s->has_router_bias != MOE_ROUTER_BIAS_LOGITS &&
+      s->has_router_bias != MOE_ROUTER_BIAS_SELECT)
+    return MOE_ERR_INVALID_ARG;
   if (s->expert_begin < 0 || s->num_local_experts < 0 ||
       (int64_t)s->expert_begin + s->num_local_experts > s->E ||
       (s->num_local_experts == 0 && s->expert_begin != 0))

@@ -33,7 +33,8 @@ constexpr int waves_for() { return NCT > 8 ? 8 : 16; }
 template <int NCT>  // 16-expert column tiles; E <= 16 * NCT
 __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ wg,
-                                                          const float* __restrict__ bias, int T,
+                                                          const float* __restrict__ bias,
+                                                          const float* __restrict__ sel, int T,
                                                           int D, int E, int k,
                                                           int32_t* __restrict__ ids,
                                                           float* __restrict__ wts) {
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
   for (int r = wave; r < kTok; r += kWaves) {
     const int t = t0 + r;
     if (t >= T) break;
-    topk_softmax(&slot(0, r, 0), E, k, lane, [&](int q, int e, float w) {
+    topk_softmax(&slot(0, r, 0), sel, E, k, lane, [&](int q, int e, float w) {
       ids[(int64_t)t * k + q] = e;
       wts[(int64_t)t * k + q] = w;
     });
@@ -121,8 +122,8 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
 }
 
 template <int NCT>
-hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias, int T, int D,
-                      int E, int k, int32_t* ids, float* wts, hipStream_t s) {
+hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias, const float* sel,
+                      int T, int D, int E, int k, int32_t* ids, float* wts, hipStream_t s) {
   constexpr int kWaves = waves_for<NCT>();
   const size_t lds = sizeof(float) * kWaves * kTok * (16 * NCT + 1);
   static bool attr_set = false;
@@ -134,7 +135,7 @@ hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias,
   }
   const int blocks = (T + kTok - 1) / kTok;
   hipLaunchKernelGGL(moe_router_kernel<NCT>, dim3(blocks), dim3(kWaves * 64), lds, s, x, w_g, bias,
-                     T, D, E, k, ids, wts);
+                     sel, T, D, E, k, ids, wts);
   return hipGetLastError();
 }
 
@@ -238,15 +239,15 @@ hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w_g, int T, 
   return launch_partial_nct<16>(x, w_g, T, D, E, partial, s);
 }
 
-hipError_t launch_router(const uint16_t* x, const uint16_t* w_g, const float* bias, int T, int D,
-                         int E, int k, int32_t* ids, float* wts, hipStream_t s) {
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_g, const float* bias, const float* sel,
+                         int T, int D, int E, int k, int32_t* ids, float* wts, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nct = (E + 15) / 16;
-  if (nct <= 1) return launch_nct<1>(x, w_g, bias, T, D, E, k, ids, wts, s);
-  if (nct <= 2) return launch_nct<2>(x, w_g, bias, T, D, E, k, ids, wts, s);
-  if (nct <= 4) return launch_nct<4>(x, w_g, bias, T, D, E, k, ids, wts, s);
-  if (nct <= 8) return launch_nct<8>(x, w_g, bias, T, D, E, k, ids, wts, s);
-  return launch_nct<16>(x, w_g, bias, T, D, E, k, ids, wts, s);
+  if (nct <= 1) return launch_nct<1>(x, w_g, bias, sel, T, D, E, k, ids, wts, s);
+  if (nct <= 2) return launch_nct<2>(x, w_g, bias, sel, T, D, E, k, ids, wts, s);
+  if (nct <= 4) return launch_nct<4>(x, w_g, bias, sel, T, D, E, k, ids, wts, s);
+  if (nct <= 8) return launch_nct<8>(x, w_g, bias, sel, T, D, E, k, ids, wts, s);
+  return launch_nct<16>(x, w_g, bias, sel, T, D, E, k, ids, wts, s);
 }
 
 }  // namespace moe

@@ -35,6 +35,14 @@ def test_header_declares_the_boundary():
         assert n in names
 
 
+def test_router_bias_modes_match_the_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define (MOE_ROUTER_BIAS_[A-Z]+) (\d+)", text))
+    assert defs == {"MOE_ROUTER_BIAS_NONE": str(B.ROUTER_BIAS_NONE),
+                    "MOE_ROUTER_BIAS_LOGITS": str(B.ROUTER_BIAS_LOGITS),
+                    "MOE_ROUTER_BIAS_SELECT": str(B.ROUTER_BIAS_SELECT)}
+
+
 def test_every_declared_symbol_is_exported(lib):
     for n in declared_functions():
         assert hasattr(lib, n), n
@@ -71,6 +79,9 @@ def _fwd(lib, shape, w, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
     (dict(expert_begin=-1, num_local_experts=2), B.MOE_ERR_INVALID_ARG),
     (dict(expert_begin=2, num_local_experts=0), B.MOE_ERR_INVALID_ARG),
     (dict(num_local_experts=-1), B.MOE_ERR_INVALID_ARG),
+    # router bias modes are 0 (none), 1 (in the logits), 2 (selection only)
+    (dict(has_router_bias=3), B.MOE_ERR_INVALID_ARG),
+    (dict(has_router_bias=-1), B.MOE_ERR_INVALID_ARG),
     (dict(T=1 << 30, k=8), B.MOE_ERR_UNSUPPORTED)])
 def test_shape_errors(lib, kw, code):
     assert _fwd(lib, _shape(**kw), _weights()) == code
@@ -86,6 +97,7 @@ def test_pointer_errors(lib):
     assert _fwd(lib, s, _weights(x=FAKE + 8)) == B.MOE_ERR_ALIGNMENT
     assert _fwd(lib, s, _weights(), y=FAKE + 4) == B.MOE_ERR_ALIGNMENT
     assert _fwd(lib, _shape(has_router_bias=1), _weights()) == B.MOE_ERR_INVALID_ARG
+    assert _fwd(lib, _shape(has_router_bias=2), _weights()) == B.MOE_ERR_INVALID_ARG
     assert _fwd(lib, _shape(F_shared=64), _weights()) == B.MOE_ERR_INVALID_ARG
 
 

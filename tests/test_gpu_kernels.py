@@ -36,15 +36,24 @@ def _forward(inp, **kw):
     ids = torch.empty((T, s.k), dtype=torch.int32, device=DEV)
     w = torch.empty((T, s.k), dtype=torch.float32, device=DEV)
     y = moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias, g.ws_gate_up,
-                        g.ws_down, topk_ids=ids, topk_w=w, **kw)
+                        g.ws_down, topk_ids=ids, topk_w=w, bias_select=s.bias_select, **kw)
     torch.cuda.synchronize()
     return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _route_oracle(inp, k):
+    """Oracle routing plus the values the selection is taken on (the logits,
+    or logit + bias with a selection-only bias)."""
+    sel = inp.shape.bias_select
+    ids, p, margin, logits = oracle.route(inp.x, inp.w_g, inp.router_bias, k, select_only=sel)
+    keys = logits + inp.router_bias.numpy()[None, :] if sel else logits
+    return ids, p, margin, keys
 
 
 def _layer_parity(inp, tokens=None):
     s = inp.shape
     y, ids_g, w_g = _forward(inp)
-    ids_or, p_or, margin, logits = oracle.route(inp.x, inp.w_g, inp.router_bias, s.k)
+    ids_or, p_or, margin, logits = _route_oracle(inp, s.k)
     flipped = check_routing(ids_g, w_g, ids_or, p_or, margin, logits, s.k)
     T = inp.x.shape[0]
     tok = np.arange(T) if tokens is None else tokens
@@ -68,6 +77,23 @@ def test_router_parity(T, D, E, k, bias):
     torch.cuda.synchronize()
     ids_or, p_or, margin, logits = oracle.route(inp.x, inp.w_g, inp.router_bias, k)
     check_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_or, p_or, margin, logits, k)
+
+
+@pytest.mark.parametrize("T,D,E,k", [
+    (64, 128, 8, 2), (300, 2880, 32, 4), (97, 7168, 256, 8), (33, 136, 17, 5), (70, 512, 128, 6)])
+def test_router_parity_selection_bias(T, D, E, k):
+    """Selection-only bias (load balancing): ids from logit + bias, weights from
+    the plain logits, on both top-k paths (E <= 64 and E > 64)."""
+    s = W.Shape(T=T, D=D, E=E, k=k, F=8, router_bias=True, bias_select=True)
+    inp = W.make_inputs(s, seed=T + E)
+    g = _gpu(inp)
+    ids, w = moe.moe_route(g.x, g.w_g, k, g.router_bias, bias_select=True)
+    torch.cuda.synchronize()
+    ids_or, p_or, margin, keys = _route_oracle(inp, k)
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_or, p_or, margin, keys, k)
+    # the bias must have moved selections, or the test proves nothing
+    ids_plain, _, _, _ = oracle.route(inp.x, inp.w_g, None, k)
+    assert np.mean(np.sort(ids_plain, 1) != np.sort(ids_or, 1)) > 0.05
 
 
 def test_router_exact_ties_on_grid_inputs():
@@ -159,6 +185,31 @@ LAYER_CASES = [
 def test_layer_parity(T, D, E, k, F, Fs, bias):
     s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, router_bias=bias)
     _layer_parity(W.make_inputs(s, seed=T + E))
+
+
+@pytest.mark.parametrize("T,D,E,k,F,Fs", [
+    (64, 2880, 32, 4, 512, 0),     # few tokens: routing finished in the align kernel
+    (7, 512, 64, 6, 256, 256),     # few tokens, 64 experts, shared expert
+    (300, 1024, 8, 2, 512, 0),     # full router, E <= 64 top-k
+    (40, 1024, 256, 8, 256, 256),  # full router, E > 64 top-k
+])
+def test_layer_selection_bias(T, D, E, k, F, Fs):
+    """Whole layer with a selection-only router bias against the oracle."""
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, router_bias=True, bias_select=True)
+    _layer_parity(W.make_inputs(s, seed=T + E + 1))
+
+
+@pytest.mark.parametrize("T", [16, 200])
+def test_layer_selection_bias_forces_expert_not_weight(T):
+    """+1000 on expert 3: it is every token's slot 0, with the weight the plain
+    logits give it (a bias inside the logits would give it weight ~1)."""
+    s = W.Shape(T=T, D=512, E=8, k=2, F=256, router_bias=True, bias_select=True)
+    inp = W.make_inputs(s, seed=5)
+    inp.router_bias = torch.zeros(8, dtype=torch.float32)
+    inp.router_bias[3] = 1000.0
+    _, ids, w = _layer_parity(inp)
+    assert np.all(ids[:, 0] == 3)
+    assert w[:, 0].min() < 0.5
 
 
 def _split(V, ctas, kmin):
