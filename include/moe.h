@@ -193,6 +193,28 @@ int moe_forward_timed(const moe_shape* shape, const moe_weights* w, float* y, in
                       float* topk_w, void* workspace, size_t ws_bytes, void* stream,
                       void* const* events);
 
+/*
+ * Per-expert load of the last moe_forward / moe_forward_timed /
+ * moe_forward_routed call that ran with this shape and this workspace, for a
+ * load-balancing signal: "Mixture of experts: por qué un modelo enorme apenas
+ * usa sus parámetros", section on the cost of the approach (the auxiliary
+ * balancing loss is computed from how many tokens each expert receives), and
+ * the balancer of the glossary "MoE (Mixture of Experts - Mezcla de
+ * Expertos)", section 2 item 4, which adjusts the router biases from the same
+ * loads.
+ *   counts  device int32 [G] out, G = E (num_local_experts for a shard), plus
+ *           one last entry = T when F_shared > 0 (the shared expert's rows):
+ *           counts[g] = number of assignments (t, j) routed to held expert g.
+ * Enqueued on `stream` after that call (a device-to-device copy out of the
+ * workspace; all zeros when T == 0).  The workspace must not have been used
+ * by another call in between.  Errors: as moe_workspace_size for the shape;
+ * MOE_ERR_INVALID_ARG for a NULL counts (or NULL workspace with T > 0);
+ * MOE_ERR_WORKSPACE when ws_bytes is below moe_workspace_size; MOE_ERR_ALIGNMENT
+ * for a counts pointer not 4-byte aligned.
+ */
+int moe_expert_load(const moe_shape* shape, const void* workspace, size_t ws_bytes,
+                    int32_t* counts, void* stream);
+
 /* Static text for an error code (for MOE_ERR_HIP: the last HIP error seen by
  * this thread).  Never NULL. */
 const char* moe_strerror(int code);

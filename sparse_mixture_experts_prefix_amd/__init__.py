@@ -7,10 +7,12 @@ the first call does, and raises if it is missing.
 """
 from .binding import (MOE_ERR_ALIGNMENT, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
                       MOE_ERR_WORKSPACE, MOE_OK, MoEError, Shape, Weights, alloc_workspace,
-                      HipEvents, block_m, load_library, make_shape, moe_align, moe_block_m, moe_forward,
-                      moe_forward_routed, moe_forward_timed, moe_route, moe_strerror, moe_workspace_size, strerror,
-                      workspace_size)
+                      ROUTER_BIAS_LOGITS, ROUTER_BIAS_NONE, ROUTER_BIAS_SELECT,
+                      HipEvents, block_m, layer_shape, load_library, make_shape, moe_align, moe_block_m,
+                      moe_expert_load, moe_forward, moe_forward_routed, moe_forward_timed, moe_route,
+                      moe_strerror, moe_workspace_size, strerror, workspace_size)
 
 __all__ = ["moe_forward", "moe_route", "moe_align", "moe_forward_routed", "moe_workspace_size",
-           "moe_block_m", "moe_strerror", "moe_forward_timed", "HipEvents", "MoEError", "make_shape", "alloc_workspace",
-           "load_library"]
+           "moe_block_m", "moe_strerror", "moe_forward_timed", "moe_expert_load", "HipEvents", "MoEError",
+           "make_shape", "layer_shape", "alloc_workspace", "load_library", "ROUTER_BIAS_NONE",
+           "ROUTER_BIAS_LOGITS", "ROUTER_BIAS_SELECT"]

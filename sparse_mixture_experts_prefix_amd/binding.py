@@ -24,7 +24,7 @@ MOE_ERR_ALIGNMENT = -4
 MOE_ERR_HIP = -5
 
 EXPORTS = ("moe_workspace_size", "moe_block_m", "moe_forward", "moe_route", "moe_align",
-           "moe_forward_routed", "moe_forward_timed", "moe_strerror")
+           "moe_forward_routed", "moe_forward_timed", "moe_expert_load", "moe_strerror")
 
 
 class MoEError(RuntimeError):
@@ -68,6 +68,9 @@ def load_library(path: str = LIB_PATH):
             lib.moe_align.argtypes = [P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
             lib.moe_forward_routed.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P,
                                                P, P, ctypes.c_size_t, P]
+            lib.moe_forward_timed.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P,
+                                              P, P, ctypes.c_size_t, P, P]
+            lib.moe_expert_load.argtypes = [ctypes.POINTER(Shape), P, ctypes.c_size_t, P, P]
             lib.moe_strerror.argtypes = [ctypes.c_int]
             lib.moe_strerror.restype = ctypes.c_char_p
             for name in EXPORTS[:-1]:
@@ -295,6 +298,28 @@ def moe_forward_routed(x, w_gate_up, w_down, topk_ids, topk_w, ws_gate_up=None, 
     return y
 
 
+def layer_shape(x, w_g, w_gate_up, k, ws_gate_up=None, router_bias=None, *, bias_select=False,
+                expert_begin=None) -> Shape:
+    """The moe_shape moe_forward builds for these tensors (for workspace_size
+    and moe_expert_load)."""
+    return _layer_shape(x, w_gate_up, None, k, ws_gate_up, bias_mode(router_bias, bias_select),
+                        w_g.shape[0], expert_begin)
+
+
+def moe_expert_load(shape: Shape, workspace, counts=None):
+    """Per-expert assignment counts of the last layer call on ``workspace``
+    with ``shape``: int32 [G] on the workspace's device, G = held experts (+1
+    for the shared expert, whose entry is T)."""
+    G = (shape.num_local_experts or shape.E) + (1 if shape.F_shared > 0 else 0)
+    _dev(workspace, "workspace", torch.uint8)
+    if counts is None:
+        counts = torch.empty(G, dtype=torch.int32, device=workspace.device)
+    _dev(counts, "counts", torch.int32, (G,))
+    _check(load_library().moe_expert_load(ctypes.byref(shape), _ptr(workspace), workspace.numel(),
+                                          _ptr(counts), _stream(workspace.device)))
+    return counts
+
+
 # the C names, one to one
 moe_workspace_size = workspace_size
 moe_block_m = block_m
@@ -346,10 +371,6 @@ def moe_forward_timed(events: HipEvents, x, w_g, w_gate_up, w_down, k, router_bi
                          w_g.shape[0], expert_begin)
     w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
     lib = load_library()
-    lib.moe_forward_timed.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), ctypes.c_void_p,
-                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
-    lib.moe_forward_timed.restype = ctypes.c_int
     _check(lib.moe_forward_timed(ctypes.byref(shape), ctypes.byref(w), _ptr(y), _ptr(topk_ids),
                                  _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(x.device),
                                  ctypes.cast(events.array, ctypes.c_void_p)))

@@ -261,6 +261,26 @@ int moe_forward_routed(const moe_shape* shape, const moe_weights* w, const int32
   return run_experts(P, w, topk_ids, topk_w, y, workspace, static_cast<hipStream_t>(stream));
 }
 
+int moe_expert_load(const moe_shape* shape, const void* workspace, size_t ws_bytes,
+                    int32_t* counts, void* stream) {
+  moe::Plan P;
+  int rc = moe::make_plan(shape, &P);
+  if (rc) return rc;
+  if (!counts || (P.T > 0 && !workspace)) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(counts) & 3u) return MOE_ERR_ALIGNMENT;
+  if (P.T > 0 && ws_bytes < P.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (P.T == 0) {
+    e = moe::launch_fill_i32(counts, P.G, 0, s);
+  } else {
+    const int32_t* src = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) +
+                                                          P.off_counts);
+    e = hipMemcpyAsync(counts, src, sizeof(int32_t) * (size_t)P.G, hipMemcpyDeviceToDevice, s);
+  }
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 const char* moe_strerror(int code) {
   switch (code) {
     case MOE_OK: return "ok";

@@ -35,6 +35,13 @@ def test_header_declares_the_boundary():
         assert n in names
 
 
+def test_every_export_has_its_argument_types():
+    """Pointers and sizes are 64-bit: a missing argtypes would pass them as C int."""
+    lib = B.load_library()
+    for n in B.EXPORTS:
+        assert getattr(lib, n).argtypes is not None, n
+
+
 def test_router_bias_modes_match_the_header():
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define (MOE_ROUTER_BIAS_[A-Z]+) (\d+)", text))
@@ -159,3 +166,15 @@ def test_python_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         moe.moe_forward(x, x, x.view(1, 4, 8), x.view(1, 8, 4), 1)
+
+
+def test_expert_load_errors(lib):
+    s = _shape()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == B.MOE_OK
+    load = lib.moe_expert_load
+    assert load(ctypes.byref(s), FAKE, n.value, None, None) == B.MOE_ERR_INVALID_ARG
+    assert load(ctypes.byref(s), None, n.value, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert load(ctypes.byref(s), FAKE, n.value - 1, FAKE, None) == B.MOE_ERR_WORKSPACE
+    assert load(ctypes.byref(s), FAKE, n.value, FAKE + 2, None) == B.MOE_ERR_ALIGNMENT
+    assert load(ctypes.byref(_shape(k=0)), FAKE, n.value, FAKE, None) == B.MOE_ERR_INVALID_ARG

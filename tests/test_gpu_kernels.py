@@ -212,6 +212,61 @@ def test_layer_selection_bias_forces_expert_not_weight(T):
     assert w[:, 0].min() < 0.5
 
 
+@pytest.mark.parametrize("T,D,E,k,F,Fs,sel,shard", [
+    (64, 2880, 32, 4, 256, 0, False, None),    # few tokens: routing finished in align
+    (300, 512, 8, 2, 256, 128, True, None),    # shared expert: last entry is T
+    (700, 512, 64, 8, 256, 0, False, (16, 40)),  # a shard: its held experts only
+    (0, 256, 8, 2, 256, 0, False, None),       # no tokens: all zeros
+])
+def test_expert_load_counts(T, D, E, k, F, Fs, sel, shard):
+    """moe_expert_load: bit-exact per-expert counts of the last call's routing."""
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, router_bias=sel, bias_select=sel)
+    g = _gpu(W.make_inputs(s, seed=T + 3))
+    a, b = shard if shard else (0, E)
+    gu, dn = g.w_gate_up[a:b].contiguous(), g.w_down[a:b].contiguous()
+    eb = a if shard else None
+    shape = moe.layer_shape(g.x, g.w_g, gu, k, g.ws_gate_up, g.router_bias, bias_select=sel,
+                            expert_begin=eb)
+    ws = moe.alloc_workspace(shape, DEV)
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    moe.moe_forward(g.x, g.w_g, gu, dn, k, g.router_bias, g.ws_gate_up, g.ws_down, topk_ids=ids,
+                    workspace=ws, expert_begin=eb, bias_select=sel)
+    G = (b - a) + (1 if Fs else 0)
+    counts = torch.full((G,), -7, dtype=torch.int32, device=DEV)
+    moe.moe_expert_load(shape, ws, counts)
+    torch.cuda.synchronize()
+    flat = ids.cpu().numpy().ravel()
+    expect = np.bincount(flat[(flat >= a) & (flat < b)] - a, minlength=b - a)
+    if Fs:
+        expect = np.append(expect, T)
+    assert np.array_equal(counts.cpu().numpy(), expect)
+
+
+def test_expert_load_drives_selection_bias_balancing():
+    """The loop the two pieces make: loads out of moe_expert_load, a
+    selection-only bias nudged against the over-loaded experts, repeated;
+    the most loaded expert's share must drop well below where it started."""
+    s = W.Shape(T=1024, D=256, E=8, k=2, F=256, router_bias=True, bias_select=True)
+    inp = W.make_inputs(s, seed=0)
+    inp.x += 0.25       # a direction every token shares ...
+    inp.w_g[0] += 0.02  # ... that expert 0 scores: it is in most tokens' top-2
+    g = _gpu(inp)
+    b = torch.zeros(8, dtype=torch.float32, device=DEV)
+    shape = moe.layer_shape(g.x, g.w_g, g.w_gate_up, 2, None, b, bias_select=True)
+    ws = moe.alloc_workspace(shape, DEV)
+    shares = []
+    for _ in range(12):
+        moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, 2, b, workspace=ws, bias_select=True)
+        load = moe.moe_expert_load(shape, ws).float()
+        share = load / load.sum()
+        shares.append(share.max().item())
+        b -= 0.1 * torch.sign(share - 1.0 / 8)
+    torch.cuda.synchronize()
+    print("max expert share per step:", ["%.3f" % v for v in shares])
+    assert shares[0] > 0.3
+    assert min(shares[-4:]) < 0.6 * shares[0]
+
+
 def _split(V, ctas, kmin):
     """(R, S) of the prefill GEMMs' last-round split: R tiles cut in S pieces."""
     if V % ctas == 0 or V >= 4 * ctas:

@@ -117,9 +117,11 @@ def test_balancing_bias_evens_out_the_load():
     must lower the largest expert load."""
     s = W.Shape(T=2048, D=256, E=8, k=2, F=8)
     inp = W.make_inputs(s, seed=0)
-    inp.w_g[0] += 0.02  # expert 0 scores high for many tokens
+    inp.x += 0.25       # a direction every token shares ...
+    inp.w_g[0] += 0.02  # ... that expert 0 scores: it is in most tokens' top-2
     ids0, _, _, _ = oracle.route(inp.x, inp.w_g, None, 2)
     load0 = np.bincount(ids0.ravel(), minlength=8) / ids0.size
+    assert load0.max() > 0.4
     b = torch.tensor(-2.0 * (load0 - load0.mean()), dtype=torch.float32)
     ids1, _, _, _ = oracle.route(inp.x, inp.w_g, b, 2, select_only=True)
     load1 = np.bincount(ids1.ravel(), minlength=8) / ids1.size
