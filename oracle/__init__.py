@@ -68,9 +68,11 @@ def _load():
             lib.oracle_experts_shard.restype = ctypes.c_int
             lib.oracle_experts_shard.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                                  _i32, _i32, _p, _p, _p, _i64, _p, _p]
-            lib.oracle_forward.restype = ctypes.c_int
-            lib.oracle_forward.argtypes = [_p, _p, _p, _i32, _p, _p, _p, _p, _i64, _i32, _i32, _i32,
-                                           _i32, _i32, _p, _p, _p, _p]
+            lib.oracle_experts_q.restype = ctypes.c_int
+            lib.oracle_experts_q.argtypes = [_p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32,
+                                             _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _p, _p]
+            lib.oracle_e4m3_decode.restype = None
+            lib.oracle_e4m3_decode.argtypes = [_p, _i64, _p]
             lib.oracle_align.restype = ctypes.c_int
             lib.oracle_align.argtypes = [_p, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
                                          _i64, _p, _p]
@@ -96,6 +98,24 @@ def _bf16_ptr(t):
         raise TypeError("oracle takes CPU bfloat16 tensors")
     t = t.contiguous()
     return t.data_ptr(), t
+
+
+def _w_ptr(t):
+    """Pointer to a contiguous CPU weight tensor: bf16, or uint8 E4M3 codes."""
+    if t is None:
+        return None, None
+    if t.device.type != "cpu" or t.dtype not in (torch.bfloat16, torch.uint8):
+        raise TypeError("oracle takes CPU bfloat16 or uint8 (E4M3) weight tensors")
+    t = t.contiguous()
+    return t.data_ptr(), t
+
+
+def e4m3_decode(codes):
+    """Values of E4M3 codes (uint8 array) as float64, from the format's definition."""
+    c = np.ascontiguousarray(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e4m3_decode(c.ctypes.data, c.size, out.ctypes.data)
+    return out
 
 
 def _f32_ptr(t):
@@ -149,10 +169,15 @@ def experts(inp, ids, p, tokens=None, count_macs: bool = False, expert_begin: in
     lib = _load()
     s = inp.shape
     px, kx = _bf16_ptr(inp.x)
-    pgu, k1 = _bf16_ptr(inp.w_gate_up)
-    pdn, k2 = _bf16_ptr(inp.w_down)
-    psgu, k3 = _bf16_ptr(inp.ws_gate_up)
-    psdn, k4 = _bf16_ptr(inp.ws_down)
+    fp8 = inp.w_gate_up.dtype == torch.uint8
+    pgu, k1 = _w_ptr(inp.w_gate_up)
+    pdn, k2 = _w_ptr(inp.w_down)
+    psgu, k3 = _w_ptr(inp.ws_gate_up)
+    psdn, k4 = _w_ptr(inp.ws_down)
+    q1, r1 = _f32_ptr(inp.w_gate_up_scale if fp8 else None)
+    q2, r2 = _f32_ptr(inp.w_down_scale if fp8 else None)
+    q3, r3 = _f32_ptr(inp.ws_gate_up_scale if fp8 else None)
+    q4, r4 = _f32_ptr(inp.ws_down_scale if fp8 else None)
     ids = np.ascontiguousarray(ids, np.int32)
     p = np.ascontiguousarray(p, np.float64)
     T = inp.x.shape[0]
@@ -171,37 +196,21 @@ def experts(inp, ids, p, tokens=None, count_macs: bool = False, expert_begin: in
         n = tok.size
     y = np.empty((n, s.D), np.float64)
     macs = ctypes.c_int64(0)
-    rc = lib.oracle_experts_shard(px, pgu, pdn, psgu, psdn, s.D, s.E, int(expert_begin), nl, s.F,
-                                  s.k, s.Fs, ids.ctypes.data, p.ctypes.data,
-                                  None if tok is None else tok.ctypes.data, n, y.ctypes.data,
-                                  ctypes.byref(macs))
+    rc = lib.oracle_experts_q(px, pgu, pdn, psgu, psdn, 1 if fp8 else 0, q1, q2, q3, q4, s.D, s.E,
+                              int(expert_begin), nl, s.F, s.k, s.Fs, ids.ctypes.data,
+                              p.ctypes.data, None if tok is None else tok.ctypes.data, n,
+                              y.ctypes.data, ctypes.byref(macs))
     if rc:
-        raise ValueError("oracle_experts_shard failed: %d" % rc)
+        raise ValueError("oracle_experts_q failed: %d" % rc)
     return (y, macs.value) if count_macs else y
 
 
 def forward(inp):
-    """Whole layer for every token: returns (y float64 [T,D], ids, p, margin)."""
-    lib = _load()
-    s = inp.shape
-    T = inp.x.shape[0]
-    px, kx = _bf16_ptr(inp.x)
-    pg, kg = _bf16_ptr(inp.w_g)
-    pb, kb = _f32_ptr(inp.router_bias)
-    pgu, k1 = _bf16_ptr(inp.w_gate_up)
-    pdn, k2 = _bf16_ptr(inp.w_down)
-    psgu, k3 = _bf16_ptr(inp.ws_gate_up)
-    psdn, k4 = _bf16_ptr(inp.ws_down)
-    ids = np.empty((T, s.k), np.int32)
-    p = np.empty((T, s.k), np.float64)
-    margin = np.empty((T,), np.float64)
-    y = np.empty((T, s.D), np.float64)
-    mode = bias_mode(inp.router_bias, s.bias_select)
-    rc = lib.oracle_forward(px, pg, pb, mode, pgu, pdn, psgu, psdn, T, s.D, s.E, s.F, s.k, s.Fs,
-                            ids.ctypes.data, p.ctypes.data, margin.ctypes.data, y.ctypes.data)
-    if rc:
-        raise ValueError("oracle_forward failed: %d" % rc)
-    return y, ids, p, margin
+    """Whole layer for every token: route every row of x, then run its experts.
+    Returns (y float64 [T,D], ids, p, margin)."""
+    ids, p, margin, _ = route(inp.x, inp.w_g, inp.router_bias, inp.shape.k,
+                              select_only=inp.shape.bias_select)
+    return experts(inp, ids, p), ids, p, margin
 
 
 def align(ids, E: int, block_m: int, shared: bool = False):

@@ -170,25 +170,71 @@ int oracle_route(const uint16_t* x, const uint16_t* w_g, const float* bias, int6
 
 /* ----------------------------------------------------------------- experts */
 
+/*
+ * OCP 8-bit floating point E4M3 ("fn": no infinities), the format of the
+ * quantised expert weights: sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits.  Exponent field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN.
+ * Per-expert quantised weights: "Mixture of Experts optimiza Transformers y
+ * LLMs", section on the resources the method needs, and "Transformers v5 El
+ * Secreto Detrás de los Modelos MoE Más Rápidos", section on its limits, name
+ * per-expert quantisation without a format; this one is the reading taken.
+ */
+static double e4m3(uint8_t c) {
+  const int sign = c >> 7, ex = (c >> 3) & 15, man = c & 7;
+  double v;
+  if (ex == 15 && man == 7) return NAN;
+  if (ex == 0)
+    v = ldexp((double)man, -9);
+  else
+    v = ldexp(1.0 + man / 8.0, ex - 7);
+  return sign ? -v : v;
+}
+
+/* One expert matrix, row-major with `cols` columns: bf16 words, or (scale
+ * != NULL) E4M3 bytes whose row r stands for e4m3(q[r][c]) * scale[r]. */
+typedef struct {
+  const void* w;
+  const float* scale;
+  int64_t cols;
+} wmat;
+
+static wmat wm(const void* base, const float* scale, int64_t row0, int64_t cols) {
+  wmat m;
+  m.cols = cols;
+  m.scale = scale ? scale + row0 : NULL;
+  m.w = scale ? (const void*)((const uint8_t*)base + row0 * cols)
+              : (const void*)((const uint16_t*)base + row0 * cols);
+  return m;
+}
+
+/* sum_c W[r][c] * v[c] with every weight dequantised exactly in double
+ * (an E4M3 value times an fp32 scale needs 4 + 24 significant bits). */
+static double row_dot(const wmat* m, int64_t r, const double* v) {
+  double s = 0.0;
+  if (m->scale) {
+    const uint8_t* q = (const uint8_t*)m->w + r * m->cols;
+    const double sc = (double)m->scale[r];
+    for (int64_t c = 0; c < m->cols; ++c) s += e4m3(q[c]) * sc * v[c];
+  } else {
+    const uint16_t* b = (const uint16_t*)m->w + r * m->cols;
+    for (int64_t c = 0; c < m->cols; ++c) s += bf(b[c]) * v[c];
+  }
+  return s;
+}
+
 /* yt[o] += coef * sum_f W_down[o,f] * h[f],  h[f] = SiLU(g_f) * u_f,
  * g_f = W_gu[f,:] . x,  u_f = W_gu[F+f,:] . x,  SiLU(g) = g / (1 + exp(-g)). */
-static void swiglu_accumulate(const uint16_t* w_gu, const uint16_t* w_dn, int32_t F, int32_t D,
+static void swiglu_accumulate(const wmat* gu, const wmat* dn, int32_t F, int32_t D,
                               const double* xd, double* h, double coef, double* yt, int64_t* macs) {
   for (int32_t f = 0; f < F; ++f) {
-    const uint16_t* wg = w_gu + (int64_t)f * D;
-    const uint16_t* wu = w_gu + (int64_t)(F + f) * D;
-    double g = 0.0, u = 0.0;
-    for (int32_t d = 0; d < D; ++d) g += bf(wg[d]) * xd[d];
-    for (int32_t d = 0; d < D; ++d) u += bf(wu[d]) * xd[d];
+    const double g = row_dot(gu, f, xd);
+    const double u = row_dot(gu, F + f, xd);
     *macs += 2 * (int64_t)D;
     h[f] = g / (1.0 + exp(-g)) * u;
   }
   for (int32_t o = 0; o < D; ++o) {
-    const uint16_t* wd = w_dn + (int64_t)o * F;
-    double s = 0.0;
-    for (int32_t f = 0; f < F; ++f) s += bf(wd[f]) * h[f];
     *macs += F;
-    yt[o] += coef * s;
+    yt[o] += coef * row_dot(dn, o, h);
   }
 }
 
@@ -201,19 +247,25 @@ static void swiglu_accumulate(const uint16_t* w_gu, const uint16_t* w_dn, int32_
  * w_down hold just those n_local experts.  The shards' outputs add up to the
  * layer's (the shared expert is added by whichever call passes it).
  *   x [T,D] bf16 (rows picked by tokens[], or rows 0..n_tokens-1 when tokens is NULL)
- *   w_gate_up [n_local,2F,D], w_down [n_local,D,F] bf16; ws_gate_up [2Fs,D], ws_down [D,Fs] bf16 or NULL
+ *   w_gate_up [n_local,2F,D], w_down [n_local,D,F]; ws_gate_up [2Fs,D], ws_down [D,Fs] or NULL
+ *   fp8 == 0: those are bf16.  fp8 == 1: they are E4M3 bytes, and sgu [n_local,2F],
+ *     sdn [n_local,D], ssgu [2Fs], ssdn [D] are the fp32 scales of their rows
  *   ids [*,k] (global expert ids), p [*,k]: the routing rows of the same tokens (indexed by token id)
  *   y [n_tokens, D] double out; macs: total multiply-adds performed (may be NULL)
  * Slots are accumulated in order j = 0..k-1, the shared expert last.
  */
-int oracle_experts_shard(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
-                         const uint16_t* ws_gate_up, const uint16_t* ws_down, int32_t D, int32_t E,
-                         int32_t e0, int32_t n_local, int32_t F, int32_t k, int32_t Fs,
-                         const int32_t* ids, const double* p, const int64_t* tokens,
-                         int64_t n_tokens, double* y, int64_t* macs) {
+int oracle_experts_q(const uint16_t* x, const void* w_gate_up, const void* w_down,
+                     const void* ws_gate_up, const void* ws_down, int32_t fp8, const float* sgu,
+                     const float* sdn, const float* ssgu, const float* ssdn, int32_t D, int32_t E,
+                     int32_t e0, int32_t n_local, int32_t F, int32_t k, int32_t Fs,
+                     const int32_t* ids, const double* p, const int64_t* tokens, int64_t n_tokens,
+                     double* y, int64_t* macs) {
   if (D <= 0 || E <= 0 || F <= 0 || k <= 0 || k > E || Fs < 0 || n_tokens < 0) return -1;
   if (e0 < 0 || n_local < 0 || e0 + n_local > E) return -1;
   if (Fs > 0 && (!ws_gate_up || !ws_down)) return -1;
+  if (fp8 != 0 && fp8 != 1) return -1;
+  if (fp8 && (!sgu || !sdn || (Fs > 0 && (!ssgu || !ssdn)))) return -1;
+  if (!fp8) sgu = sdn = ssgu = ssdn = NULL;
   int err = 0;
   int64_t total = 0;
   int32_t hmax = F > Fs ? F : Fs;
@@ -235,10 +287,15 @@ int oracle_experts_shard(const uint16_t* x, const uint16_t* w_gate_up, const uin
         for (int32_t j = 0; j < k; ++j) {
           int32_t e = ids[t * k + j] - e0; /* index inside this shard */
           if (e < 0 || e >= n_local) continue; /* another shard's expert */
-          swiglu_accumulate(w_gate_up + (int64_t)e * 2 * F * D, w_down + (int64_t)e * D * F, F, D,
-                            xd, h, p[t * k + j], yt, &total);
+          const wmat gu = wm(w_gate_up, sgu, (int64_t)e * 2 * F, D);
+          const wmat dn = wm(w_down, sdn, (int64_t)e * D, F);
+          swiglu_accumulate(&gu, &dn, F, D, xd, h, p[t * k + j], yt, &total);
         }
-        if (Fs > 0) swiglu_accumulate(ws_gate_up, ws_down, Fs, D, xd, h, 1.0, yt, &total);
+        if (Fs > 0) {
+          const wmat gu = wm(ws_gate_up, ssgu, 0, D);
+          const wmat dn = wm(ws_down, ssdn, 0, Fs);
+          swiglu_accumulate(&gu, &dn, Fs, D, xd, h, 1.0, yt, &total);
+        }
       }
     }
     free(xd);
@@ -248,6 +305,21 @@ int oracle_experts_shard(const uint16_t* x, const uint16_t* w_gate_up, const uin
   return err;
 }
 
+/* oracle_experts_q with bf16 weights. */
+int oracle_experts_shard(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
+                         const uint16_t* ws_gate_up, const uint16_t* ws_down, int32_t D, int32_t E,
+                         int32_t e0, int32_t n_local, int32_t F, int32_t k, int32_t Fs,
+                         const int32_t* ids, const double* p, const int64_t* tokens,
+                         int64_t n_tokens, double* y, int64_t* macs) {
+  return oracle_experts_q(x, w_gate_up, w_down, ws_gate_up, ws_down, 0, NULL, NULL, NULL, NULL, D,
+                          E, e0, n_local, F, k, Fs, ids, p, tokens, n_tokens, y, macs);
+}
+
+/* E4M3 decode of n codes (exposed for the tests). */
+void oracle_e4m3_decode(const uint8_t* codes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3(codes[i]);
+}
+
 /* Expert outputs with every expert present (the unsharded layer). */
 int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
                    const uint16_t* ws_gate_up, const uint16_t* ws_down, int32_t D, int32_t E,
@@ -255,20 +327,6 @@ int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t*
                    const int64_t* tokens, int64_t n_tokens, double* y, int64_t* macs) {
   return oracle_experts_shard(x, w_gate_up, w_down, ws_gate_up, ws_down, D, E, 0, E, F, k, Fs, ids,
                               p, tokens, n_tokens, y, macs);
-}
-
-/*
- * Whole layer for T tokens: route every token, then run its experts.
- * bias/bias_mode and ids/p/margin as in oracle_route_mode; y [T,D] double.
- */
-int oracle_forward(const uint16_t* x, const uint16_t* w_g, const float* bias, int32_t bias_mode,
-                   const uint16_t* w_gate_up, const uint16_t* w_down, const uint16_t* ws_gate_up,
-                   const uint16_t* ws_down, int64_t T, int32_t D, int32_t E, int32_t F, int32_t k,
-                   int32_t Fs, int32_t* ids, double* p, double* margin, double* y) {
-  int rc = oracle_route_mode(x, w_g, bias, bias_mode, T, D, E, k, NULL, ids, p, margin);
-  if (rc) return rc;
-  return oracle_experts(x, w_gate_up, w_down, ws_gate_up, ws_down, D, E, F, k, Fs, ids, p, NULL, T,
-                        y, NULL);
 }
 
 /* ------------------------------------------------------------------- align */

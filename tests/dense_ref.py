@@ -17,6 +17,16 @@ def f64(t):
     return None if t is None else t.to(torch.float64).numpy()
 
 
+def weights64(t, scale):
+    """Expert weights as float64: bf16 widened, or E4M3 codes decoded by
+    torch's float8_e4m3fn type (a library decode) times each row's scale."""
+    if t is None:
+        return None
+    if t.dtype == torch.uint8:
+        return t.view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale.double().numpy()[..., None]
+    return f64(t)
+
+
 def dense_logits(inp):
     """fp32 logits; a bias in the logits is added before the rounding, a
     selection-only bias is not added at all."""
@@ -59,11 +69,12 @@ def dense_forward(inp):
     T = X.shape[0]
     G = np.zeros((T, s.E))
     np.put_along_axis(G, ids, p, axis=1)
-    Wgu = f64(inp.w_gate_up)
-    Wd = f64(inp.w_down)
+    Wgu = weights64(inp.w_gate_up, inp.w_gate_up_scale)
+    Wd = weights64(inp.w_down, inp.w_down_scale)
     Y = np.zeros((T, s.D))
     for e in range(s.E):
         Y += G[:, e:e + 1] * swiglu_ffn(X, Wgu[e], Wd[e])
     if s.Fs:
-        Y += swiglu_ffn(X, f64(inp.ws_gate_up), f64(inp.ws_down))
+        Y += swiglu_ffn(X, weights64(inp.ws_gate_up, inp.ws_gate_up_scale),
+                        weights64(inp.ws_down, inp.ws_down_scale))
     return Y, ids, p

@@ -125,6 +125,9 @@ class Shape:
     # the router bias only moves the top-k selection, not the weights
     # (auxiliary-loss-free load balancing); needs router_bias
     bias_select: bool = False
+    # expert weights (routed and shared) stored as E4M3 bytes with one fp32
+    # scale per row, instead of bf16
+    fp8: bool = False
 
     def with_T(self, T: int) -> "Shape":
         return dataclasses.replace(self, T=T)
@@ -194,16 +197,43 @@ class LayerInputs:
     router_bias: torch.Tensor | None = None   # fp32 [E]
     ws_gate_up: torch.Tensor | None = None    # bf16 [2Fs, D]
     ws_down: torch.Tensor | None = None       # bf16 [D, Fs]
+    # shape.fp8: the four expert tensors above are uint8 E4M3 codes, and these
+    # hold the fp32 scale of each of their rows
+    w_gate_up_scale: torch.Tensor | None = None   # [E, 2F]
+    w_down_scale: torch.Tensor | None = None      # [E, D]
+    ws_gate_up_scale: torch.Tensor | None = None  # [2Fs]
+    ws_down_scale: torch.Tensor | None = None     # [D]
 
     def to(self, device) -> "LayerInputs":
         def mv(t):
             return None if t is None else t.to(device)
         return LayerInputs(self.shape, mv(self.x), mv(self.w_g), mv(self.w_gate_up), mv(self.w_down),
-                           mv(self.router_bias), mv(self.ws_gate_up), mv(self.ws_down))
+                           mv(self.router_bias), mv(self.ws_gate_up), mv(self.ws_down),
+                           mv(self.w_gate_up_scale), mv(self.w_down_scale), mv(self.ws_gate_up_scale),
+                           mv(self.ws_down_scale))
+
+    def with_x(self, x) -> "LayerInputs":
+        return dataclasses.replace(self, x=x)
+
+
+E4M3_MAX = 448.0
+
+
+def quantize_rows_e4m3(w: torch.Tensor):
+    """Per-row quantisation of a weight tensor [..., rows, cols] to E4M3 codes:
+    scale = max|row| / 448 (1 for an all-zero row), code = E4M3 nearest to
+    fp32(w / scale) (torch's float8_e4m3fn conversion, ties to even).  This only
+    prepares inputs; the layer takes codes and scales as given."""
+    wf = w.to(torch.float32)
+    amax = wf.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    q = (wf / scale).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.contiguous(), scale.squeeze(-1).contiguous()
 
 
 def make_weights(shape: Shape, seed: int = 0, std: float = WEIGHT_STD) -> LayerInputs:
-    """Weights of the layer (x left empty); independent of T."""
+    """Weights of the layer (x left empty); independent of T.  With shape.fp8
+    the expert weights are the same draws quantised per row to E4M3."""
     E, D, F, Fs = shape.E, shape.D, shape.F, shape.Fs
     w_g = normal_bf16((E, D), seed, TAG_W_G, std)
     w_gu = normal_bf16((E, 2 * F, D), seed, TAG_W_GATE_UP, std)
@@ -213,7 +243,19 @@ def make_weights(shape: Shape, seed: int = 0, std: float = WEIGHT_STD) -> LayerI
         ws_gu = normal_bf16((2 * Fs, D), seed, TAG_WS_GATE_UP, std)
         ws_d = normal_bf16((D, Fs), seed, TAG_WS_DOWN, std)
     bias = router_bias_for(shape, seed)
-    return LayerInputs(shape, torch.empty((0, D), dtype=torch.bfloat16), w_g, w_gu, w_d, bias, ws_gu, ws_d)
+    out = LayerInputs(shape, torch.empty((0, D), dtype=torch.bfloat16), w_g, w_gu, w_d, bias, ws_gu, ws_d)
+    return quantize_inputs(out) if shape.fp8 else out
+
+
+def quantize_inputs(inp: LayerInputs) -> LayerInputs:
+    """The same layer with its expert weights quantised per row to E4M3."""
+    out = dataclasses.replace(inp, shape=dataclasses.replace(inp.shape, fp8=True))
+    out.w_gate_up, out.w_gate_up_scale = quantize_rows_e4m3(inp.w_gate_up)
+    out.w_down, out.w_down_scale = quantize_rows_e4m3(inp.w_down)
+    if inp.ws_gate_up is not None:
+        out.ws_gate_up, out.ws_gate_up_scale = quantize_rows_e4m3(inp.ws_gate_up)
+        out.ws_down, out.ws_down_scale = quantize_rows_e4m3(inp.ws_down)
+    return out
 
 
 def make_x(T: int, D: int, seed: int = 0, std: float = X_STD) -> torch.Tensor:
@@ -224,7 +266,7 @@ def make_inputs(shape: Shape, seed: int = 0, weights: LayerInputs | None = None)
     """Full inputs; pass ``weights`` to reuse one weight set across several T."""
     w = weights if weights is not None else make_weights(shape, seed)
     x = make_x(shape.T, shape.D, seed)
-    return LayerInputs(shape, x, w.w_g, w.w_gate_up, w.w_down, w.router_bias, w.ws_gate_up, w.ws_down)
+    return dataclasses.replace(w, shape=shape, x=x)
 
 
 def make_grid_inputs(shape: Shape, seed: int = 0) -> LayerInputs:
