@@ -8,6 +8,7 @@ in HBM.  Default workload: the Mixtral-8x7B-shaped prefill layer
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -59,8 +60,7 @@ def _cpu_baseline(inp, target_s):
     s = inp.shape
 
     def run(n):
-        sub = W.LayerInputs(s.with_T(n), inp.x[:n].contiguous(), inp.w_g, inp.w_gate_up, inp.w_down,
-                            inp.router_bias, inp.ws_gate_up, inp.ws_down)
+        sub = dataclasses.replace(inp, shape=s.with_T(n), x=inp.x[:n].contiguous())
         t0 = time.perf_counter()
         oracle.forward(sub)
         return time.perf_counter() - t0
@@ -90,6 +90,9 @@ def main():
                     help="expert-parallel degree: time the shard of one rank (E/ep experts; the "
                          "shared expert on rank 0) at the workload's real shape")
     ap.add_argument("--rank", type=int, default=0, help="which shard --ep times")
+    ap.add_argument("--fp8", action="store_true",
+                    help="expert weights as E4M3 codes with one fp32 scale per row (the same "
+                         "draws quantised per row)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="run one plain device copy of this many GiB first (a known-size kernel "
                          "for calibrating rocprofv3 byte counters)")
@@ -117,6 +120,8 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     s = wl.shape if args.T is None else wl.shape.with_T(args.T)
+    if args.fp8:
+        s = dataclasses.replace(s, fp8=True)
     if args.ep < 1 or s.E % args.ep or not 0 <= args.rank < args.ep:
         raise SystemExit("--ep must divide E=%d and 0 <= --rank < --ep" % s.E)
     _log("generating %s T=%d inputs" % (wl.name, s.T))
@@ -125,23 +130,43 @@ def main():
     e0 = args.rank * e_loc
     if args.ep > 1:  # this rank's shard: its experts, the shared expert on rank 0 only
         keep_shared = args.rank == 0
-        inp = W.LayerInputs(s, inp.x, inp.w_g, inp.w_gate_up[e0:e0 + e_loc].contiguous(),
-                            inp.w_down[e0:e0 + e_loc].contiguous(), inp.router_bias,
-                            inp.ws_gate_up if keep_shared else None,
-                            inp.ws_down if keep_shared else None)
+        def cut(t):
+            return None if t is None else t[e0:e0 + e_loc].contiguous()
+
+        def sh(t):
+            return t if keep_shared else None
+
+        inp = dataclasses.replace(inp, w_gate_up=cut(inp.w_gate_up), w_down=cut(inp.w_down),
+                                  w_gate_up_scale=cut(inp.w_gate_up_scale),
+                                  w_down_scale=cut(inp.w_down_scale), ws_gate_up=sh(inp.ws_gate_up),
+                                  ws_down=sh(inp.ws_down), ws_gate_up_scale=sh(inp.ws_gate_up_scale),
+                                  ws_down_scale=sh(inp.ws_down_scale))
     g = inp.to(dev)
     shard = dict(expert_begin=e0) if args.ep > 1 else {}
     fs_used = s.Fs if (args.ep == 1 or args.rank == 0) else 0
     # Rotate over weight copies when one copy would sit in the Infinity Cache.
-    wbytes = inp.w_gate_up.numel() * 2 + inp.w_down.numel() * 2
+    wel = 1 if s.fp8 else 2  # bytes per expert weight
+    wbytes = (inp.w_gate_up.numel() + inp.w_down.numel()) * wel
     n_copies = 1 if wbytes > 4 * LLC_BYTES else 4
     sets = [g]
+
+    def clone(t):
+        return None if t is None else t.clone()
+
     for _ in range(n_copies - 1):
-        sets.append(W.LayerInputs(s, g.x, g.w_g, g.w_gate_up.clone(), g.w_down.clone(), g.router_bias,
-                                  None if g.ws_gate_up is None else g.ws_gate_up.clone(),
-                                  None if g.ws_down is None else g.ws_down.clone()))
+        sets.append(dataclasses.replace(
+            g, w_gate_up=clone(g.w_gate_up), w_down=clone(g.w_down), ws_gate_up=clone(g.ws_gate_up),
+            ws_down=clone(g.ws_down), w_gate_up_scale=clone(g.w_gate_up_scale),
+            w_down_scale=clone(g.w_down_scale), ws_gate_up_scale=clone(g.ws_gate_up_scale),
+            ws_down_scale=clone(g.ws_down_scale)))
+
+    def scales(q):
+        return ((q.w_gate_up_scale, q.w_down_scale, q.ws_gate_up_scale, q.ws_down_scale)
+                if s.fp8 else None)
+
+    fmt = moe.WEIGHTS_FP8_E4M3 if s.fp8 else moe.WEIGHTS_BF16
     shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, fs_used, s.router_bias,
-                           e0 if args.ep > 1 else 0, e_loc if args.ep > 1 else 0)
+                           e0 if args.ep > 1 else 0, e_loc if args.ep > 1 else 0, fmt)
     ws = moe.alloc_workspace(shape, dev)
     y = torch.empty((s.T, s.D), dtype=torch.float32, device=dev)
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
@@ -160,7 +185,8 @@ def main():
     def step(i):
         q = sets[i % len(sets)]
         moe.moe_forward(q.x, q.w_g, q.w_gate_up, q.w_down, s.k, q.router_bias, q.ws_gate_up,
-                        q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws, **shard)
+                        q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws, scales=scales(q),
+                        **shard)
 
     run = step
     if args.graph:
@@ -195,7 +221,7 @@ def main():
         q = sets[i % len(sets)]
         moe.moe_forward_timed(ev[i], q.x, q.w_g, q.w_gate_up, q.w_down, s.k, q.router_bias,
                               q.ws_gate_up, q.ws_down, y=y, topk_ids=ids, topk_w=wts, workspace=ws,
-                              **shard)
+                              scales=scales(q), **shard)
     torch.cuda.synchronize()
     per_kernel = {name: float(np.mean([e.elapsed_ms(j, j + 1) for e in ev]))
                   for j, name in enumerate(KERNELS)}
@@ -207,25 +233,30 @@ def main():
     touched = int((local > 0).sum())
     n_assign = int(local.sum())   # routed rows this call computes
     # algorithmic work of this call: router over all E, its routed rows, the
-    # shared expert where it runs; bytes: touched experts' weights, W_g, x, y
+    # shared expert where it runs; bytes: touched experts' weights (with their
+    # row scales when E4M3), W_g, x, y
     gu_flops = 4 * n_assign * s.D * s.F + 4 * s.T * s.D * fs_used
     flops = 2 * s.T * s.D * s.E + gu_flops + 2 * n_assign * s.D * s.F + 2 * s.T * s.D * fs_used
-    nbytes = (touched * W.expert_params(s) * 2 + 3 * s.D * fs_used * 2 + s.E * s.D * 2
-              + s.T * s.D * 2 + s.T * s.D * 4)
+    sc = 4 if s.fp8 else 0  # scale bytes per weight row
+    nbytes = (touched * (W.expert_params(s) * wel + (2 * s.F + s.D) * sc)
+              + 3 * s.D * fs_used * wel + (2 * fs_used + s.D) * sc * (fs_used > 0)
+              + s.E * s.D * 2 + s.T * s.D * 2 + s.T * s.D * 4)
     t_ideal = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
     layer_bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9) else "hbm"
 
     gu_ms = per_kernel["moe_gemm_gate_up"]
-    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias)
+    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias, weight_format=fmt)
     gemm_file = "gemm_prefill.hip" if moe.moe_block_m(shape) == 256 else "gemm_decode.hip"
-    traffic = _traffic_from_profile(wl.name, s.T, _kernel_sources_sha(gemm_file)) if args.ep == 1 else None
+    wl_tag = wl.name + ("_fp8" if s.fp8 else "")
+    traffic = _traffic_from_profile(wl_tag, s.T, _kernel_sources_sha(gemm_file)) if args.ep == 1 else None
     if layer_bound == "mfma":
         achieved = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
     else:
-        # expert weights of the gate/up half actually touched + gathered x
-        gu_bytes = touched * 2 * s.F * s.D * 2 + 2 * fs_used * s.D * 2 + s.T * s.D * 2
+        # expert weights of the gate/up half actually touched (+ row scales) + gathered x
+        gu_bytes = (touched * 2 * s.F * (s.D * wel + sc) + 2 * fs_used * (s.D * wel + sc)
+                    + s.T * s.D * 2)
         achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
@@ -245,9 +276,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded counter-based normal draws: x ~ N(0,1), weights ~ N(0,0.02), bf16)",
+        "data": "synthetic (seeded counter-based normal draws: x ~ N(0,1), weights ~ N(0,0.02), bf16"
+                + ("; expert weights quantised per row to e4m3)" if s.fp8 else ")"),
         "config": {"workload": wl.name, "T": s.T, "D": s.D, "E": s.E, "k": s.k, "d_ff": s.F,
                    "shared_d_ff": s.Fs, "router_bias": bool(s.router_bias),
+                   "expert_weights": "e4m3 + fp32 row scale" if s.fp8 else "bf16",
                    "weight_copies_rotated": n_copies, "hip_graph": bool(args.graph),
                    **({"expert_parallel": args.ep, "rank": args.rank, "local_experts": [e0, e0 + e_loc],
                        "local_rows": n_assign} if args.ep > 1 else {})},

@@ -40,6 +40,8 @@
  *  - w_down    bf16 [E, D, F]
  *  - ws_gate_up bf16 [2Fs, D], ws_down bf16 [D, Fs]: the shared expert, or
  *              NULL when F_shared == 0
+ *  - the four expert tensors may instead hold E4M3 codes with per-row fp32
+ *    scales (MOE_WEIGHTS_FP8_E4M3 below)
  *  - y         fp32 [T, D] (written, never read)
  *  - topk_ids  int32 [T, k], topk_w fp32 [T, k]: slot j is the j-th highest
  *              logit (ties to the lower expert index); weights sum to 1.
@@ -77,6 +79,18 @@ enum {
   MOE_ERR_HIP = -5          /* a HIP launch failed; moe_strerror gives HIP's text */
 };
 
+/* moe_shape.weight_format (any other value: MOE_ERR_INVALID_ARG).
+ * Per-expert quantised expert weights ("Mixture of Experts optimiza
+ * Transformers y LLMs", section on the resources the method needs;
+ * "Transformers v5 El Secreto Detrás de los Modelos MoE Más Rápidos", section
+ * on its limits): with MOE_WEIGHTS_FP8_E4M3, w_gate_up, w_down, ws_gate_up and
+ * ws_down hold one byte per weight, an OCP FP8 E4M3 code (bias 7, no
+ * infinities, NaN codes outside the contract), and the *_scale arrays of
+ * moe_weights give one fp32 scale per row: weight = value(code) * scale[row].
+ * x, w_g and everything downstream stay as for bf16 weights. */
+#define MOE_WEIGHTS_BF16 0
+#define MOE_WEIGHTS_FP8_E4M3 1
+
 /* moe_shape.has_router_bias (any other value: MOE_ERR_INVALID_ARG) */
 #define MOE_ROUTER_BIAS_NONE 0   /* no bias; router_bias is not read */
 #define MOE_ROUTER_BIAS_LOGITS 1 /* bias inside the logits: selection and weights */
@@ -101,16 +115,24 @@ typedef struct moe_shape {
    * shared expert to one shard only).  Both 0: every expert (no sharding). */
   int32_t expert_begin;
   int32_t num_local_experts;
+  int32_t weight_format;   /* MOE_WEIGHTS_*: storage of the four expert tensors */
 } moe_shape;
 
 typedef struct moe_weights {
   const void* x;            /* bf16 [T, D] */
   const void* w_g;          /* bf16 [E, D] */
   const float* router_bias; /* fp32 [E], or NULL with MOE_ROUTER_BIAS_NONE */
-  const void* w_gate_up;    /* bf16 [E, 2F, D] ([num_local_experts, 2F, D] for a shard) */
-  const void* w_down;       /* bf16 [E, D, F] ([num_local_experts, D, F] for a shard) */
+  /* the four expert tensors: bf16, or E4M3 bytes (weight_format) */
+  const void* w_gate_up;    /* [E, 2F, D] ([num_local_experts, 2F, D] for a shard) */
+  const void* w_down;       /* [E, D, F] ([num_local_experts, D, F] for a shard) */
   const void* ws_gate_up;   /* bf16 [2*F_shared, D] or NULL */
   const void* ws_down;      /* bf16 [D, F_shared] or NULL */
+  /* MOE_WEIGHTS_FP8_E4M3 only (not read otherwise); 4-byte aligned:
+   * fp32 scale of each row of the four tensors above */
+  const float* w_gate_up_scale;  /* [E, 2F] ([num_local_experts, 2F] for a shard) */
+  const float* w_down_scale;     /* [E, D]  ([num_local_experts, D] for a shard) */
+  const float* ws_gate_up_scale; /* [2*F_shared] or NULL */
+  const float* ws_down_scale;    /* [D] or NULL */
 } moe_weights;
 
 /*

@@ -7,7 +7,8 @@ the first call does, and raises if it is missing.
 """
 from .binding import (MOE_ERR_ALIGNMENT, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
                       MOE_ERR_WORKSPACE, MOE_OK, MoEError, Shape, Weights, alloc_workspace,
-                      ROUTER_BIAS_LOGITS, ROUTER_BIAS_NONE, ROUTER_BIAS_SELECT,
+                      ROUTER_BIAS_LOGITS, ROUTER_BIAS_NONE, ROUTER_BIAS_SELECT, WEIGHTS_BF16,
+                      WEIGHTS_FP8_E4M3,
                       HipEvents, block_m, layer_shape, load_library, make_shape, moe_align, moe_block_m,
                       moe_expert_load, moe_forward, moe_forward_routed, moe_forward_timed, moe_route,
                       moe_strerror, moe_workspace_size, strerror, workspace_size)
@@ -15,4 +16,4 @@ from .binding import (MOE_ERR_ALIGNMENT, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_E
 __all__ = ["moe_forward", "moe_route", "moe_align", "moe_forward_routed", "moe_workspace_size",
            "moe_block_m", "moe_strerror", "moe_forward_timed", "moe_expert_load", "HipEvents", "MoEError",
            "make_shape", "layer_shape", "alloc_workspace", "load_library", "ROUTER_BIAS_NONE",
-           "ROUTER_BIAS_LOGITS", "ROUTER_BIAS_SELECT"]
+           "ROUTER_BIAS_LOGITS", "ROUTER_BIAS_SELECT", "WEIGHTS_BF16", "WEIGHTS_FP8_E4M3"]

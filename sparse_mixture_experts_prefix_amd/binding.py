@@ -37,13 +37,15 @@ class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("k", ctypes.c_int32), ("F_shared", ctypes.c_int32),
                 ("has_router_bias", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
-                ("num_local_experts", ctypes.c_int32)]
+                ("num_local_experts", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("w_g", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
-                ("ws_gate_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p)]
+                ("ws_gate_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p),
+                ("w_gate_up_scale", ctypes.c_void_p), ("w_down_scale", ctypes.c_void_p),
+                ("ws_gate_up_scale", ctypes.c_void_p), ("ws_down_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -111,6 +113,10 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# moe_shape.weight_format values
+WEIGHTS_BF16 = 0
+WEIGHTS_FP8_E4M3 = 1   # uint8 E4M3 codes with one fp32 scale per row
+
 # moe_shape.has_router_bias values
 ROUTER_BIAS_NONE = 0
 ROUTER_BIAS_LOGITS = 1   # the bias is part of the logits
@@ -127,13 +133,13 @@ def bias_mode(router_bias, bias_select: bool) -> int:
 
 
 def make_shape(T, D, E, F, k, F_shared=0, has_router_bias=0, expert_begin=0,
-               num_local_experts=0) -> Shape:
+               num_local_experts=0, weight_format=WEIGHTS_BF16) -> Shape:
     """moe_shape; has_router_bias is a ROUTER_BIAS_* value (a bool means
     none / logits); num_local_experts > 0 makes the call one expert-parallel
     shard holding experts expert_begin .. expert_begin+num_local_experts-1."""
     mode = (1 if has_router_bias else 0) if isinstance(has_router_bias, bool) else int(has_router_bias)
     return Shape(int(T), int(D), int(E), int(F), int(k), int(F_shared), mode,
-                 int(expert_begin), int(num_local_experts))
+                 int(expert_begin), int(num_local_experts), int(weight_format))
 
 
 def workspace_size(shape: Shape) -> int:
@@ -148,44 +154,67 @@ def block_m(shape: Shape) -> int:
 
 def _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, has_bias, n_experts=None, expert_begin=None):
     """Shape of a layer call; the call is a shard when the expert weights hold
-    fewer experts than the router scores (n_experts) or expert_begin is given."""
+    fewer experts than the router scores (n_experts) or expert_begin is given.
+    uint8 expert weights are E4M3 codes."""
     T, D = x.shape
     E_loc, twoF, D2 = w_gate_up.shape
     F = twoF // 2
     Fs = 0 if ws_gate_up is None else ws_gate_up.shape[0] // 2
     E = E_loc if n_experts is None else int(n_experts)
+    fmt = WEIGHTS_FP8_E4M3 if w_gate_up.dtype == torch.uint8 else WEIGHTS_BF16
     if expert_begin is None and E == E_loc:
-        return make_shape(T, D, E, F, k, Fs, has_bias)
-    return make_shape(T, D, E, F, k, Fs, has_bias, expert_begin or 0, E_loc)
+        return make_shape(T, D, E, F, k, Fs, has_bias, weight_format=fmt)
+    return make_shape(T, D, E, F, k, Fs, has_bias, expert_begin or 0, E_loc, fmt)
 
 
 def alloc_workspace(shape: Shape, device) -> torch.Tensor:
     return torch.empty(max(workspace_size(shape), 1), dtype=torch.uint8, device=device)
 
 
-def _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down) -> Weights:
+def _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down, scales=None) -> Weights:
+    sc = tuple(scales) if scales is not None else (None, None, None, None)
     return Weights(_ptr(x), _ptr(w_g), _ptr(router_bias), _ptr(w_gate_up), _ptr(w_down),
-                   _ptr(ws_gate_up), _ptr(ws_down))
+                   _ptr(ws_gate_up), _ptr(ws_down), *[_ptr(t) for t in sc])
 
 
-def _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down):
+def _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down, scales=None):
+    """Checks the layer tensors.  Expert weights are all bf16, or all uint8
+    E4M3 codes with scales = (w_gate_up_scale [E,2F], w_down_scale [E,D],
+    ws_gate_up_scale [2Fs] or None, ws_down_scale [D] or None), fp32."""
     _dev(x, "x", torch.bfloat16)
     if x.dim() != 2:
         raise ValueError("x must be [T, D]")
     T, D = x.shape
-    _dev(w_gate_up, "w_gate_up", torch.bfloat16)
+    wdt = w_gate_up.dtype if w_gate_up is not None else torch.bfloat16
+    if wdt not in (torch.bfloat16, torch.uint8):
+        raise ValueError("expert weights must be bf16 or uint8 (E4M3 codes)")
+    _dev(w_gate_up, "w_gate_up", wdt)
     if w_gate_up.dim() != 3 or w_gate_up.shape[2] != D or w_gate_up.shape[1] % 2:
         raise ValueError("w_gate_up must be [E, 2F, D]")
     E, twoF, _ = w_gate_up.shape
-    _dev(w_down, "w_down", torch.bfloat16, (E, D, twoF // 2))
+    _dev(w_down, "w_down", wdt, (E, D, twoF // 2))
     if (ws_gate_up is None) != (ws_down is None):
         raise ValueError("ws_gate_up and ws_down go together")
     if ws_gate_up is not None:
-        _dev(ws_gate_up, "ws_gate_up", torch.bfloat16)
+        _dev(ws_gate_up, "ws_gate_up", wdt)
         if ws_gate_up.dim() != 2 or ws_gate_up.shape[1] != D or ws_gate_up.shape[0] % 2:
             raise ValueError("ws_gate_up must be [2Fs, D]")
-        _dev(ws_down, "ws_down", torch.bfloat16, (D, ws_gate_up.shape[0] // 2))
-    for t in (w_gate_up, w_down, ws_gate_up, ws_down):
+        _dev(ws_down, "ws_down", wdt, (D, ws_gate_up.shape[0] // 2))
+    tensors = [w_gate_up, w_down, ws_gate_up, ws_down]
+    if wdt == torch.uint8:
+        if scales is None or len(scales) != 4:
+            raise ValueError("E4M3 weights need scales=(w_gate_up_scale, w_down_scale, "
+                             "ws_gate_up_scale, ws_down_scale)")
+        sgu, sdn, ssgu, ssdn = scales
+        _dev(sgu, "w_gate_up_scale", torch.float32, (E, twoF))
+        _dev(sdn, "w_down_scale", torch.float32, (E, D))
+        if ws_gate_up is not None:
+            _dev(ssgu, "ws_gate_up_scale", torch.float32, (ws_gate_up.shape[0],))
+            _dev(ssdn, "ws_down_scale", torch.float32, (D,))
+        tensors += [sgu, sdn, ssgu, ssdn]
+    elif scales is not None and any(t is not None for t in scales):
+        raise ValueError("scales are only for uint8 (E4M3) weights")
+    for t in tensors:
         if t is not None and t.device != x.device:
             raise ValueError("all tensors must be on one device")
     return T, D, E, twoF // 2
@@ -193,11 +222,15 @@ def _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down):
 
 def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None, ws_down=None, *,
                 y=None, topk_ids=None, topk_w=None, workspace=None, expert_begin=None,
-                bias_select=False):
+                bias_select=False, scales=None):
     """Whole MoE layer.  Returns y (fp32 [T, D]).
 
     bias_select: router_bias moves only the top-k selection (load balancing);
     the weights are the softmax of the plain chosen logits.
+
+    uint8 expert weights are E4M3 codes; then scales = (w_gate_up_scale
+    [E,2F], w_down_scale [E,D], ws_gate_up_scale [2Fs], ws_down_scale [D])
+    gives the fp32 scale of every weight row.
 
     Optional preallocated outputs (y, topk_ids int32 [T,k], topk_w fp32 [T,k])
     and workspace (uint8, >= workspace_size bytes) avoid any allocation here.
@@ -205,7 +238,7 @@ def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None,
     expert_begin + n - 1 only (w_g still covers all E); y is then the shard's
     part of the layer.
     """
-    T, D, E_loc, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    T, D, E_loc, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down, scales)
     _dev(w_g, "w_g", torch.bfloat16)
     E = w_g.shape[0]
     _dev(w_g, "w_g", torch.bfloat16, (E, D))
@@ -225,7 +258,7 @@ def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None,
     if workspace is None:
         workspace = alloc_workspace(shape, x.device)
     _dev(workspace, "workspace", torch.uint8)
-    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
+    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down, scales)
     _check(load_library().moe_forward(ctypes.byref(shape), ctypes.byref(w), _ptr(y), _ptr(topk_ids),
                                       _ptr(topk_w), _ptr(workspace), workspace.numel(),
                                       _stream(x.device)))
@@ -248,7 +281,7 @@ def moe_route(x, w_g, k, router_bias=None, *, topk_ids=None, topk_w=None, bias_s
     _dev(topk_ids, "topk_ids", torch.int32, (T, k))
     _dev(topk_w, "topk_w", torch.float32, (T, k))
     shape = make_shape(T, D, E, 8, k, 0, bias_mode(router_bias, bias_select))
-    w = Weights(_ptr(x), _ptr(w_g), _ptr(router_bias), None, None, None, None)
+    w = _weights(x, w_g, router_bias, None, None, None, None)
     _check(load_library().moe_route(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids),
                                     _ptr(topk_w), _stream(x.device)))
     return topk_ids, topk_w
@@ -277,11 +310,11 @@ def moe_align(topk_ids, E: int, block_m_: int, shared_rows: int = 0):
 
 
 def moe_forward_routed(x, w_gate_up, w_down, topk_ids, topk_w, ws_gate_up=None, ws_down=None, *,
-                       y=None, workspace=None, n_experts=None, expert_begin=None):
+                       y=None, workspace=None, n_experts=None, expert_begin=None, scales=None):
     """The layer under a given routing (topk_ids int32 [T,k], topk_w fp32 [T,k]).
     For a shard, n_experts is the router's expert count and expert_begin the
-    first held expert."""
-    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    first held expert.  scales: as in moe_forward."""
+    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down, scales)
     k = topk_ids.shape[1]
     _dev(topk_ids, "topk_ids", torch.int32, (T, k))
     _dev(topk_w, "topk_w", torch.float32, (T, k))
@@ -291,7 +324,7 @@ def moe_forward_routed(x, w_gate_up, w_down, topk_ids, topk_w, ws_gate_up=None, 
     _dev(y, "y", torch.float32, (T, D))
     if workspace is None:
         workspace = alloc_workspace(shape, x.device)
-    w = _weights(x, None, None, w_gate_up, w_down, ws_gate_up, ws_down)
+    w = _weights(x, None, None, w_gate_up, w_down, ws_gate_up, ws_down, scales)
     _check(load_library().moe_forward_routed(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids),
                                              _ptr(topk_w), _ptr(y), _ptr(workspace),
                                              workspace.numel(), _stream(x.device)))
@@ -364,12 +397,12 @@ class HipEvents:
 
 def moe_forward_timed(events: HipEvents, x, w_g, w_gate_up, w_down, k, router_bias=None,
                       ws_gate_up=None, ws_down=None, *, y, topk_ids, topk_w, workspace,
-                      expert_begin=None, bias_select=False):
+                      expert_begin=None, bias_select=False, scales=None):
     """moe_forward recording events[0..5] around its five kernels (all buffers preallocated)."""
-    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down, scales)
     shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, bias_mode(router_bias, bias_select),
                          w_g.shape[0], expert_begin)
-    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
+    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down, scales)
     lib = load_library()
     _check(lib.moe_forward_timed(ctypes.byref(shape), ctypes.byref(w), _ptr(y), _ptr(topk_ids),
                                  _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(x.device),

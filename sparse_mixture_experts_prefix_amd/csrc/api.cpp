@@ -82,8 +82,11 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   gu.A = static_cast<const uint16_t*>(w->x);
   gu.row_token = row_token;
   gu.lda = P.D;
-  gu.B_routed = static_cast<const uint16_t*>(w->w_gate_up);
-  gu.B_shared = static_cast<const uint16_t*>(w->ws_gate_up);
+  gu.B_routed = w->w_gate_up;
+  gu.B_shared = w->ws_gate_up;
+  gu.fp8 = P.fp8;
+  gu.S_routed = P.fp8 ? w->w_gate_up_scale : nullptr;
+  gu.S_shared = P.fp8 ? w->ws_gate_up_scale : nullptr;
   gu.E = (int)P.E_loc;
   gu.N_routed = (int)P.F;
   gu.N_shared = (int)P.Fs;
@@ -109,8 +112,10 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   dn.A = H;
   dn.row_token = nullptr;
   dn.lda = P.ldh;
-  dn.B_routed = static_cast<const uint16_t*>(w->w_down);
-  dn.B_shared = static_cast<const uint16_t*>(w->ws_down);
+  dn.B_routed = w->w_down;
+  dn.B_shared = w->ws_down;
+  dn.S_routed = P.fp8 ? w->w_down_scale : nullptr;
+  dn.S_shared = P.fp8 ? w->ws_down_scale : nullptr;
   dn.N_routed = (int)P.D;
   dn.N_shared = (int)P.D;
   dn.K_routed = (int)P.F;

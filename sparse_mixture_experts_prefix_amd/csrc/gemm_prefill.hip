@@ -255,8 +255,9 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const __amdgpu_buffer_rsrc_t rsA =
       GATE_UP ? make_rsrc(p.A, (uint32_t)p.a_bytes)
               : make_rsrc(p.A + row0 * p.lda, (uint32_t)(BM * p.lda * 2));
-  const bf16_t* Bg = shared ? p.B_shared
-                            : p.B_routed + (int64_t)g * (GATE_UP ? 2 : 1) * (int64_t)N * K;
+  const bf16_t* Bg = shared ? static_cast<const bf16_t*>(p.B_shared)
+                            : static_cast<const bf16_t*>(p.B_routed) +
+                                  (int64_t)g * (GATE_UP ? 2 : 1) * (int64_t)N * K;
   const __amdgpu_buffer_rsrc_t rsB =
       make_rsrc(Bg, (uint32_t)((int64_t)(GATE_UP ? 2 : 1) * N * K * 2));
   uint32_t offA[8], offB[8];

@@ -44,8 +44,11 @@ struct GroupedGemm {
   const uint16_t* A;          // gate/up: x [T, D] (rows gathered by row_token); down: H
   const int32_t* row_token;   // gate/up only
   int64_t lda;                // elements
-  const uint16_t* B_routed;   // w_gate_up [E, 2F, D] or w_down [E, D, F]
-  const uint16_t* B_shared;   // ws_gate_up [2Fs, D] or ws_down [D, Fs]; NULL without shared
+  const void* B_routed;       // w_gate_up [E, 2F, D] or w_down [E, D, F]
+  const void* B_shared;       // ws_gate_up [2Fs, D] or ws_down [D, Fs]; NULL without shared
+  int fp8;                    // B holds E4M3 bytes with one fp32 scale per row (else bf16)
+  const float* S_routed;      // fp8: row scales [E, 2F] or [E, D]
+  const float* S_shared;      // fp8: row scales [2Fs] or [D]
   int E;
   int N_routed, N_shared;     // output columns (gate/up: F, Fs; down: D, D)
   int K_routed, K_shared;     // reduction length (gate/up: D, D; down: F, Fs)

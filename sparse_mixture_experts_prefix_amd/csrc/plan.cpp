@@ -16,6 +16,8 @@ int check_shape(const moe_shape* s) {
   if (s->has_router_bias != MOE_ROUTER_BIAS_NONE && s->has_router_bias != MOE_ROUTER_BIAS_LOGITS &&
       s->has_router_bias != MOE_ROUTER_BIAS_SELECT)
     return MOE_ERR_INVALID_ARG;
+  if (s->weight_format != MOE_WEIGHTS_BF16 && s->weight_format != MOE_WEIGHTS_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
   if (s->expert_begin < 0 || s->num_local_experts < 0 ||
       (int64_t)s->expert_begin + s->num_local_experts > s->E ||
       (s->num_local_experts == 0 && s->expert_begin != 0))
@@ -61,6 +63,8 @@ int make_plan(const moe_shape* s, Plan* p) {
   p->cap_rows = p->A + (int64_t)p->G * (p->BM - 1) + (p->Fs > 0 ? p->T : 0);
   p->max_tiles = p->cap_rows / p->BM + 1;
   p->ldh = p->F > p->Fs ? p->F : p->Fs;
+  p->fp8 = s->weight_format == MOE_WEIGHTS_FP8_E4M3;
+  if (p->fp8 && p->BM == 256) return MOE_ERR_UNSUPPORTED;  // decode-sized tiles only
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -102,6 +106,14 @@ int check_weights(const moe_shape* s, const moe_weights* w, bool need_router) {
                         need_router ? w->w_g : nullptr};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MOE_ERR_ALIGNMENT;
+  if (s->weight_format == MOE_WEIGHTS_FP8_E4M3) {
+    if (!w->w_gate_up_scale || !w->w_down_scale) return MOE_ERR_INVALID_ARG;
+    if (s->F_shared > 0 && (!w->ws_gate_up_scale || !w->ws_down_scale)) return MOE_ERR_INVALID_ARG;
+    const float* sc[] = {w->w_gate_up_scale, w->w_down_scale, w->ws_gate_up_scale,
+                         w->ws_down_scale};
+    for (const float* q : sc)
+      if (q && (reinterpret_cast<uintptr_t>(q) & 3u)) return MOE_ERR_ALIGNMENT;
+  }
   if (need_router && s->has_router_bias && (reinterpret_cast<uintptr_t>(w->router_bias) & 3u))
     return MOE_ERR_ALIGNMENT;
   return MOE_OK;

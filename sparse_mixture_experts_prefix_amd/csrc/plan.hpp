@@ -32,6 +32,7 @@ struct Plan {
   int64_t cap_rows;   // upper bound of padded rows over all groups
   int64_t max_tiles;  // upper bound of BM-row tiles
   int64_t ldh;        // row stride (elements) of the hidden activations H: max(F, Fs)
+  int fp8;            // expert weights are E4M3 codes with per-row scales
   // byte offsets inside the workspace
   size_t off_ids, off_w, off_counts, off_offsets, off_padded, off_ntiles, off_sorted, off_rowof,
       off_rowtoken, off_tilegroup, off_h, off_yp, off_partial, off_rpart, total;

@@ -50,6 +50,13 @@ def test_router_bias_modes_match_the_header():
                     "MOE_ROUTER_BIAS_SELECT": str(B.ROUTER_BIAS_SELECT)}
 
 
+def test_weight_formats_match_the_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define (MOE_WEIGHTS_[A-Z0-9_]+) (\d+)", text))
+    assert defs == {"MOE_WEIGHTS_BF16": str(B.WEIGHTS_BF16),
+                    "MOE_WEIGHTS_FP8_E4M3": str(B.WEIGHTS_FP8_E4M3)}
+
+
 def test_every_declared_symbol_is_exported(lib):
     for n in declared_functions():
         assert hasattr(lib, n), n
@@ -89,6 +96,9 @@ def _fwd(lib, shape, w, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
     # router bias modes are 0 (none), 1 (in the logits), 2 (selection only)
     (dict(has_router_bias=3), B.MOE_ERR_INVALID_ARG),
     (dict(has_router_bias=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(weight_format=2), B.MOE_ERR_INVALID_ARG),
+    # E4M3 weights: decode-sized row tiles only (T*k / E <= 48 rows per expert)
+    (dict(weight_format=1, T=4096), B.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 30, k=8), B.MOE_ERR_UNSUPPORTED)])
 def test_shape_errors(lib, kw, code):
     assert _fwd(lib, _shape(**kw), _weights()) == code
@@ -139,8 +149,18 @@ def test_align_argument_errors(lib):
     assert lib.moe_align(P, 10, 2, 8, 16, 0, None, P, P, P, P, P, P, P, None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_weights_struct_matches_header():
+    """moe_weights is pointers only, in the header's order."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct moe_weights \{(.*?)\} moe_weights;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\*\s*(\w+);", body)
+    assert names == [f[0] for f in B.Weights._fields_]
+    assert ctypes.sizeof(B.Weights) == 8 * len(names)
+
+
 def test_shape_struct_matches_header():
-    """moe_shape is nine int32 fields in the header's order."""
+    """moe_shape is int32 fields in the header's order."""
     text = open(HEADER).read()
     body = re.search(r"typedef struct moe_shape \{(.*?)\} moe_shape;", text, re.S).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
@@ -178,3 +198,14 @@ def test_expert_load_errors(lib):
     assert load(ctypes.byref(s), FAKE, n.value - 1, FAKE, None) == B.MOE_ERR_WORKSPACE
     assert load(ctypes.byref(s), FAKE, n.value, FAKE + 2, None) == B.MOE_ERR_ALIGNMENT
     assert load(ctypes.byref(_shape(k=0)), FAKE, n.value, FAKE, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_fp8_scale_errors(lib):
+    s = _shape(weight_format=1)  # 64*2/8 = 16 rows per expert: decode tiles
+    assert _fwd(lib, s, _weights()) == B.MOE_ERR_INVALID_ARG  # no scales
+    assert _fwd(lib, s, _weights(w_gate_up_scale=FAKE)) == B.MOE_ERR_INVALID_ARG
+    sc = dict(w_gate_up_scale=FAKE, w_down_scale=FAKE + 2)
+    assert _fwd(lib, s, _weights(**sc)) == B.MOE_ERR_ALIGNMENT
+    s2 = _shape(weight_format=1, F_shared=64)
+    sc = dict(w_gate_up_scale=FAKE, w_down_scale=FAKE, ws_gate_up=FAKE, ws_down=FAKE)
+    assert _fwd(lib, s2, _weights(**sc)) == B.MOE_ERR_INVALID_ARG  # no shared scales

@@ -36,9 +36,17 @@ def _forward(inp, **kw):
     ids = torch.empty((T, s.k), dtype=torch.int32, device=DEV)
     w = torch.empty((T, s.k), dtype=torch.float32, device=DEV)
     y = moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias, g.ws_gate_up,
-                        g.ws_down, topk_ids=ids, topk_w=w, bias_select=s.bias_select, **kw)
+                        g.ws_down, topk_ids=ids, topk_w=w, bias_select=s.bias_select,
+                        scales=_scales(g), **kw)
     torch.cuda.synchronize()
     return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _scales(g):
+    """The row scales of E4M3 expert weights (None for bf16 weights)."""
+    if not g.shape.fp8:
+        return None
+    return (g.w_gate_up_scale, g.w_down_scale, g.ws_gate_up_scale, g.ws_down_scale)
 
 
 def _route_oracle(inp, k):
@@ -265,6 +273,78 @@ def test_expert_load_drives_selection_bias_balancing():
     print("max expert share per step:", ["%.3f" % v for v in shares])
     assert shares[0] > 0.3
     assert min(shares[-4:]) < 0.6 * shares[0]
+
+
+FP8_CASES = [
+    (64, 2880, 32, 4, 2880, 0),   # gpt-oss-shaped decode, 16-row tiles
+    (300, 512, 64, 8, 256, 256),  # 32-row tiles, shared expert
+    (40, 200, 8, 2, 136, 0),      # K tails: D and F not multiples of 64 (nor of 16)
+    (5, 128, 8, 2, 256, 64),
+    (1, 1024, 16, 4, 512, 0),
+]
+
+
+@pytest.mark.parametrize("T,D,E,k,F,Fs", FP8_CASES)
+def test_layer_fp8_weights(T, D, E, k, F, Fs):
+    """E4M3 expert weights with per-row scales against the oracle."""
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, fp8=True)
+    assert moe.moe_block_m(moe.make_shape(T, D, E, F, k, Fs, weight_format=1)) in (16, 32)
+    _layer_parity(W.make_inputs(s, seed=T + D))
+
+
+@pytest.mark.parametrize("T,D,E,k,F,Fs", FP8_CASES[:4])
+def test_layer_fp8_power_of_two_scales_equal_bf16_bitwise(T, D, E, k, F, Fs):
+    """With power-of-two row scales every dequantised weight is a bf16 value
+    and the scaling commutes with every rounding, so the E4M3 kernels must give
+    bitwise the bf16 kernels' y on the dequantised weights."""
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, fp8=True)
+    inp = W.make_inputs(s, seed=T + 1)
+    rng = np.random.default_rng(T)
+
+    def p2(t):
+        return torch.tensor(2.0 ** rng.integers(-12, -6, size=tuple(t.shape)), dtype=torch.float32)
+
+    inp.w_gate_up_scale, inp.w_down_scale = p2(inp.w_gate_up_scale), p2(inp.w_down_scale)
+    if Fs:
+        inp.ws_gate_up_scale, inp.ws_down_scale = p2(inp.ws_gate_up_scale), p2(inp.ws_down_scale)
+
+    def deq(q, sc):
+        return (q.view(torch.float8_e4m3fn).to(torch.float32) * sc[..., None]).to(torch.bfloat16)
+
+    bf = dataclasses.replace(inp, shape=dataclasses.replace(s, fp8=False),
+                             w_gate_up=deq(inp.w_gate_up, inp.w_gate_up_scale),
+                             w_down=deq(inp.w_down, inp.w_down_scale),
+                             ws_gate_up=deq(inp.ws_gate_up, inp.ws_gate_up_scale) if Fs else None,
+                             ws_down=deq(inp.ws_down, inp.ws_down_scale) if Fs else None,
+                             w_gate_up_scale=None, w_down_scale=None, ws_gate_up_scale=None,
+                             ws_down_scale=None)
+    y8, ids8, w8 = _forward(inp)
+    yb, idsb, wb = _forward(bf)
+    assert np.array_equal(ids8, idsb) and np.array_equal(w8, wb)
+    assert np.array_equal(y8, yb)
+
+
+def test_layer_fp8_shard_and_routed():
+    """E4M3 weights in an expert-parallel shard and under a given routing."""
+    s = W.Shape(T=64, D=512, E=16, k=4, F=256, Fs=0, fp8=True)
+    inp = W.make_inputs(s, seed=9)
+    g = _gpu(inp)
+    ids_or, p_or, _, _ = oracle.route(inp.x, inp.w_g, None, s.k)
+    a, b = 4, 12
+    sc = (g.w_gate_up_scale[a:b].contiguous(), g.w_down_scale[a:b].contiguous(), None, None)
+    y = moe.moe_forward_routed(g.x, g.w_gate_up[a:b].contiguous(), g.w_down[a:b].contiguous(),
+                               torch.from_numpy(ids_or).to(DEV),
+                               torch.from_numpy(p_or.astype(np.float32)).to(DEV),
+                               n_experts=s.E, expert_begin=a, scales=sc)
+    torch.cuda.synchronize()
+    sh = dataclasses.replace(inp, w_gate_up=inp.w_gate_up[a:b].contiguous(),
+                             w_down=inp.w_down[a:b].contiguous(),
+                             w_gate_up_scale=inp.w_gate_up_scale[a:b].contiguous(),
+                             w_down_scale=inp.w_down_scale[a:b].contiguous())
+    y_ref = oracle.experts(sh, ids_or, p_or.astype(np.float32).astype(np.float64), expert_begin=a,
+                           n_local=b - a)
+    rel, _, _ = y_error(y.cpu().numpy(), y_ref)
+    assert rel <= 2e-2
 
 
 def _split(V, ctas, kmin):

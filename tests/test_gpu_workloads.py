@@ -6,6 +6,7 @@ deterministic sample of tokens (every (T/n)-th token, every near-tie token and
 the tokens owning the first and last row of every expert group), which the
 oracle computes one by one.
 """
+import dataclasses
 import time
 
 import numpy as np
@@ -22,17 +23,20 @@ moe = pytest.importorskip("sparse_mixture_experts_prefix_amd")
 DEV = torch.device("cuda:0")
 
 
-def _run(name, T=None, n_sample=48):
+def _run(name, T=None, n_sample=48, fp8=False):
     wl = W.WORKLOADS[name]
     s = wl.shape if T is None else wl.shape.with_T(T)
+    if fp8:
+        s = dataclasses.replace(s, fp8=True)
     t0 = time.time()
     inp = W.make_inputs(s, seed=0)
     g = inp.to(DEV)
     t_gen = time.time() - t0
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device=DEV)
     w = torch.empty((s.T, s.k), dtype=torch.float32, device=DEV)
+    scales = (g.w_gate_up_scale, g.w_down_scale, g.ws_gate_up_scale, g.ws_down_scale) if fp8 else None
     y = moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias, g.ws_gate_up,
-                        g.ws_down, topk_ids=ids, topk_w=w)
+                        g.ws_down, topk_ids=ids, topk_w=w, scales=scales)
     torch.cuda.synchronize()
     ids_g, w_g, y_g = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
     del g, y
@@ -40,7 +44,8 @@ def _run(name, T=None, n_sample=48):
     ids_or, p_or, margin, logits = oracle.route(inp.x, inp.w_g, inp.router_bias, s.k)
     flipped = check_routing(ids_g, w_g, ids_or, p_or, margin, logits, s.k)
     # grouping of the GPU's own routing, bit-exact against the oracle's grouping
-    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias)
+    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, s.router_bias,
+                           weight_format=moe.WEIGHTS_FP8_E4M3 if fp8 else moe.WEIGHTS_BF16)
     bm = moe.moe_block_m(shape)
     out = moe.moe_align(torch.from_numpy(ids_g).to(DEV), s.E, bm, s.T if s.Fs else 0)
     ref = oracle.align(ids_g, s.E, bm, shared=bool(s.Fs))
@@ -70,6 +75,12 @@ def test_tiny_all_tokens():
 @pytest.mark.parametrize("T", [1, 8, 32, 64])
 def test_gptoss_decode(T):
     _run("gptoss_decode", T=T, n_sample=64)
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_gptoss_decode_fp8_weights(T):
+    """The gpt-oss-shaped decode layer with E4M3 expert weights (per-row scales)."""
+    _run("gptoss_decode", T=T, n_sample=64, fp8=True)
 
 
 def test_mixtral_prefill():
