@@ -13,16 +13,17 @@
 //    its 4 waves split K and their partial sums are added in LDS in a fixed
 //    order (deterministic).  All loads of a trip are issued before its
 //    MFMAs (a scheduling barrier), so each wave keeps two chunks in flight.
-//  - MFMA 16x16x32 bf16.  The K order inside a 64-wide chunk is permuted the
-//    same way for A and B: lane (col c, group g) holds bytes [32g, 32g+32) of
-//    its row for two consecutive MFMAs, so the four lanes of a row read one
-//    full 128-byte line.  Weights go straight from HBM to registers (each
-//    byte is used once); loads of two chunks are in flight per wave.
+//  - MFMA 16x16x32 bf16.  The K order inside a chunk is permuted the same
+//    way for A and B: lane (col c, group g) holds 128 / 4 bytes of weights of
+//    its row (16 bf16 or 32 E4M3 values) for two or four consecutive MFMAs,
+//    so the four lanes of a row read one full 128-byte line.  Weights go
+//    straight from HBM to registers (each byte is used once); the loads of
+//    several chunks are in flight per wave.
 //  - Out-of-range buffer offsets read as zero: padding rows, rows past the
 //    group's count and K tails need no branches.  Weight rows of tiles that
 //    lie wholly in bounds are read with plain global loads instead (faster).
-//  - E4M3 weights (one fp32 scale per weight row): a lane's 16 weights of a
-//    chunk are one 16-byte load, widened to bf16 exactly in registers
+//  - E4M3 weights (one fp32 scale per weight row): a lane's 32 weights of a
+//    chunk are two 16-byte loads, widened to bf16 exactly in registers
 //    (v_cvt_scalef32_pk_bf16_fp8 with scale 1; every E4M3 value is a bf16
 //    value), and each output column's sum is multiplied by its row's scale
 //    after the reduction: sum_k x_k (q_k s) = s sum_k x_k q_k.  Half the
@@ -91,6 +92,8 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
               : make_rsrc(p.A + row0 * p.lda, (uint32_t)(BMD * p.lda * 2));
   // weight bytes per element, and the lane's bytes within a 64-wide K chunk
   constexpr int EB = FP8 ? 1 : 2;
+  // elements of K per lane and chunk (a chunk is CW = 4 * KE), MFMA steps per chunk
+  constexpr int KE = FP8 ? 32 : 16, CW = 4 * KE, NH = KE / 8;
   const int64_t brows = (int64_t)(GATE_UP ? 2 : 1) * N;  // weight rows of this group
   const char* Bbytes = shared ? static_cast<const char*>(p.B_shared)
                               : static_cast<const char*>(p.B_routed) + (int64_t)g * brows * K * EB;
@@ -102,9 +105,9 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
     const int r = i * 16 + c;
     if (GATE_UP) {
       const int t = r < valid_rows ? p.row_token[row0 + r] : -1;
-      offA[i] = t >= 0 ? (uint32_t)t * (uint32_t)(p.lda * 2) + gq * 32 : kOob;
+      offA[i] = t >= 0 ? (uint32_t)t * (uint32_t)(p.lda * 2) + gq * KE * 2 : kOob;
     } else {
-      offA[i] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + gq * 32 : kOob;
+      offA[i] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + gq * KE * 2 : kOob;
     }
   }
 #pragma unroll
@@ -120,7 +123,7 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
       ok = n < N;
       brow = n;
     }
-    offB[j] = ok ? (uint32_t)brow * (uint32_t)(K * EB) + gq * 16 * EB : kOob;
+    offB[j] = ok ? (uint32_t)brow * (uint32_t)(K * EB) + gq * KE * EB : kOob;
   }
 
   f32x4 acc[MT][NG];
@@ -129,63 +132,67 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
 #pragma unroll
     for (int j = 0; j < NG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- K loop: 64-wide chunks q = wave, wave + kWaves, ...; kUnroll chunks per trip.
-  // A tile whose weight rows and K range are all in bounds (the usual case)
-  // reads the weights with plain global loads, which stream faster than
-  // bounds-checked buffer loads; a ragged tile uses the buffer loads, whose
-  // out-of-range offsets read as zero.
-  const int nq = (K + 63) / 64;
-  constexpr int BV = FP8 ? 1 : 2;  // 16-byte registers per weight row and chunk
-  auto run = [&](auto exact_tag) {
+  // ---- K loop: chunks q = wave, wave + kWaves, ...; kUnroll chunks per trip.
+  // A chunk is CW = 4 * KE elements of K: lane (c, gq) takes elements
+  // [KE*gq, KE*gq + KE) of it, 8 per MFMA step, so the four lanes of a row
+  // read 128 contiguous weight bytes (a full line) either way: KE = 16 bf16
+  // or KE = 32 E4M3 weights.
+  // Whole chunks of a tile whose weight rows are all in bounds (the usual
+  // case) read the weights with plain global loads, which stream faster than
+  // bounds-checked buffer loads; the ragged last chunk of K and tiles past
+  // the last weight row use the buffer loads, whose out-of-range offsets read
+  // as zero.  Each wave still takes its chunks in ascending order.
+  constexpr int BV = 2;  // 16-byte weight registers per row and chunk
+  const int nfull = K / CW, nq = (K + CW - 1) / CW;
+  // chunks q_begin <= q < q_end of this wave
+  auto run = [&](auto exact_tag, int q_begin, int q_end) {
     constexpr bool kExact = decltype(exact_tag)::value;
-    auto load_chunk = [&](int q, u32x4 (&a)[MT][2], u32x4 (&b)[NG][BV]) {
-      const int k0 = q * 64;
-      // K tail (K % 64 != 0): a lane's 32 bytes are all in or all out when K % 16 == 0;
-      // otherwise its two 16-byte halves are checked separately
-      const int kk = k0 + gq * 16;
-      const bool in0 = kk < K, in1 = kk + 8 < K;
+    auto load_chunk = [&](int q, u32x4 (&a)[MT][NH], u32x4 (&b)[NG][BV]) {
+      const int k0 = q * CW;
+      // K tail (K % CW != 0): each 8-element group of a lane is checked on its own
+      bool in[NH];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        a[i][0] = bload(rsA, in0 ? offA[i] : kOob, k0 * 2);
-        a[i][1] = bload(rsA, in1 ? offA[i] + 16 : kOob, k0 * 2);
-      }
+      for (int h = 0; h < NH; ++h) in[h] = k0 + gq * KE + 8 * h < K;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) a[i][h] = bload(rsA, in[h] ? offA[i] + 16 * h : kOob, k0 * 2);
 #pragma unroll
       for (int j = 0; j < NG; ++j) {
-        if constexpr (FP8) {
-          if constexpr (kExact) {
-            b[j][0] = *reinterpret_cast<const u32x4*>(Bbytes + offB[j] + k0);
-          } else {  // each 8-byte half checked against K like A's halves
-            const u32x2 lo = bload8(rsB, in0 ? offB[j] : kOob, k0);
-            const u32x2 hi = bload8(rsB, in1 ? offB[j] + 8 : kOob, k0);
-            b[j][0] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          }
-        } else if constexpr (kExact) {
-          const char* pb = Bbytes + offB[j] + k0 * 2;
+        if constexpr (kExact) {
+          const char* pb = Bbytes + offB[j] + k0 * EB;
           b[j][0] = *reinterpret_cast<const u32x4*>(pb);
           b[j][1] = *reinterpret_cast<const u32x4*>(pb + 16);
+        } else if constexpr (FP8) {  // 8-byte pieces, checked like A's groups
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            const u32x2 lo = bload8(rsB, in[2 * v] ? offB[j] + 16 * v : kOob, k0);
+            const u32x2 hi = bload8(rsB, in[2 * v + 1] ? offB[j] + 16 * v + 8 : kOob, k0);
+            b[j][v] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
         } else {
-          b[j][0] = bload(rsB, in0 ? offB[j] : kOob, k0 * 2);
-          b[j][1] = bload(rsB, in1 ? offB[j] + 16 : kOob, k0 * 2);
+          b[j][0] = bload(rsB, in[0] ? offB[j] : kOob, k0 * 2);
+          b[j][1] = bload(rsB, in[1] ? offB[j] + 16 : kOob, k0 * 2);
         }
       }
     };
-    auto mma_chunk = [&](const u32x4 (&a)[MT][2], const u32x4 (&b)[NG][BV]) {
+    auto mma_chunk = [&](const u32x4 (&a)[MT][NH], const u32x4 (&b)[NG][BV]) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
           bf16x8 bv;
           if constexpr (FP8)
-            bv = e4m3x8_to_bf16(b[j][0][2 * h], b[j][0][2 * h + 1]);
+            bv = e4m3x8_to_bf16(b[j][h / 2][2 * (h % 2)], b[j][h / 2][2 * (h % 2) + 1]);
           else
             bv = as_bf16x8(b[j][h]);
 #pragma unroll
           for (int i = 0; i < MT; ++i) acc[i][j] = mfma16(as_bf16x8(a[i][h]), bv, acc[i][j]);
         }
     };
-    int q = wave;
-    for (; q + (kUnroll - 1) * kWaves < nq; q += kUnroll * kWaves) {
-      u32x4 a[kUnroll][MT][2], b[kUnroll][NG][BV];
+    int q = q_begin + (wave - q_begin % kWaves + kWaves) % kWaves;
+    for (; q + (kUnroll - 1) * kWaves < q_end; q += kUnroll * kWaves) {
+      u32x4 a[kUnroll][MT][NH], b[kUnroll][NG][BV];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) load_chunk(q + u * kWaves, a[u], b[u]);
       // every load of the trip goes out before the first MFMA; left alone,
@@ -194,17 +201,19 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) mma_chunk(a[u], b[u]);
     }
-    for (; q < nq; q += kWaves) {
-      u32x4 a0[MT][2], b0[NG][BV];
+    for (; q < q_end; q += kWaves) {
+      u32x4 a0[MT][NH], b0[NG][BV];
       load_chunk(q, a0, b0);
       __builtin_amdgcn_sched_barrier(0);
       mma_chunk(a0, b0);
     }
   };
-  if (K % 64 == 0 && n0 + NOUT <= N)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+  if (n0 + NOUT <= N) {
+    run(std::true_type{}, 0, nfull);
+    if (nq > nfull) run(std::false_type{}, nfull, nq);
+  } else {
+    run(std::false_type{}, 0, nq);
+  }
 
   // ---- fixed-order reduction over the waves: (((w0 + w1) + w2) + ...)
   if (kWaves > 1) {
@@ -274,21 +283,27 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
 // K, and 64-wide K-chunks whose loads are in flight together per wave.
 // Measured on the gpt-oss-shaped decode layer: 32-64 output columns, 4 waves.
 constexpr int kNgGateUp = 4, kNgDown = 4, kKw = 4, kUnr = 2;
+// E4M3 weights: a chunk is half the bytes, so more chunks go out per trip
+constexpr int kNgGateUpFp8 = 4, kNgDownFp8 = 4, kUnrFp8 = 4;
+
+template <bool FP8> constexpr int ng_gate_up() { return FP8 ? kNgGateUpFp8 : kNgGateUp; }
+template <bool FP8> constexpr int ng_down() { return FP8 ? kNgDownFp8 : kNgDown; }
+template <bool FP8> constexpr int unroll() { return FP8 ? kUnrFp8 : kUnr; }
 
 template <int MT, bool FP8>
 __global__ __launch_bounds__(kKw * 64) void moe_gemm_gate_up_decode_kernel(GroupedGemm p) {
-  decode_tile<true, MT, kNgGateUp, kKw, kUnr, FP8>(p);
+  decode_tile<true, MT, ng_gate_up<FP8>(), kKw, unroll<FP8>(), FP8>(p);
 }
 
 template <int MT, bool FP8>
 __global__ __launch_bounds__(kKw * 64) void moe_gemm_down_decode_kernel(GroupedGemm p) {
-  decode_tile<false, MT, kNgDown, kKw, kUnr, FP8>(p);
+  decode_tile<false, MT, ng_down<FP8>(), kKw, unroll<FP8>(), FP8>(p);
 }
 
 template <int MT, bool FP8>
 hipError_t launch_mt(bool gate_up, GroupedGemm g, hipStream_t s) {
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
-  const int nout = gate_up ? kNgGateUp / 2 * 16 : kNgDown * 16;
+  const int nout = gate_up ? ng_gate_up<FP8>() / 2 * 16 : ng_down<FP8>() * 16;
   g.n_tiles_n = (nmax + nout - 1) / nout;
   const int64_t blocks = g.max_tiles * g.n_tiles_n;
   if (blocks == 0) return hipSuccess;

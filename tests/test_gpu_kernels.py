@@ -186,6 +186,7 @@ LAYER_CASES = [
     (1024, 1024, 8, 2, 1024, 0, True),
     (5, 128, 8, 2, 256, 0, False),
     (64, 128, 8, 2, 256, 0, False),
+    (24, 200, 8, 2, 136, 0, False),   # 16-row tiles with ragged K chunks in both GEMMs
 ]
 
 
@@ -293,10 +294,15 @@ def test_layer_fp8_weights(T, D, E, k, F, Fs):
 
 
 @pytest.mark.parametrize("T,D,E,k,F,Fs", FP8_CASES[:4])
-def test_layer_fp8_power_of_two_scales_equal_bf16_bitwise(T, D, E, k, F, Fs):
+def test_layer_fp8_power_of_two_scales_match_bf16(T, D, E, k, F, Fs):
     """With power-of-two row scales every dequantised weight is a bf16 value
-    and the scaling commutes with every rounding, so the E4M3 kernels must give
-    bitwise the bf16 kernels' y on the dequantised weights."""
+    and the scaling commutes with every rounding, so the E4M3 kernels and the
+    bf16 kernels on the dequantised weights compute the same sums; they group
+    K differently (128- vs 64-wide chunks), so y may differ by fp32 summation
+    order and the rare bf16 rounding of an h element that lands on the other
+    side.  With scales up to 2^-7 a weight reaches 3.5, so one such h moves a
+    y element by up to ~0.4% of RMS: bounded at 1e-2 RMS, and the routing
+    must agree bit for bit."""
     s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, fp8=True)
     inp = W.make_inputs(s, seed=T + 1)
     rng = np.random.default_rng(T)
@@ -321,7 +327,9 @@ def test_layer_fp8_power_of_two_scales_equal_bf16_bitwise(T, D, E, k, F, Fs):
     y8, ids8, w8 = _forward(inp)
     yb, idsb, wb = _forward(bf)
     assert np.array_equal(ids8, idsb) and np.array_equal(w8, wb)
-    assert np.array_equal(y8, yb)
+    rel, _, _ = y_error(y8, yb.astype(np.float64))
+    print("E4M3 vs bf16 kernels: max|dy|/RMS = %.3g" % rel)
+    assert rel <= 1e-2
 
 
 def test_layer_fp8_shard_and_routed():
