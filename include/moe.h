@@ -87,7 +87,8 @@ enum {
  * ws_down hold one byte per weight, an OCP FP8 E4M3 code (bias 7, no
  * infinities, NaN codes outside the contract), and the *_scale arrays of
  * moe_weights give one fp32 scale per row: weight = value(code) * scale[row].
- * x, w_g and everything downstream stay as for bf16 weights. */
+ * x, w_g and everything downstream stay as for bf16 weights.  (With D, F or
+ * F_shared not a multiple of 16, moe_block_m returns at most 32 for them.) */
 #define MOE_WEIGHTS_BF16 0
 #define MOE_WEIGHTS_FP8_E4M3 1
 

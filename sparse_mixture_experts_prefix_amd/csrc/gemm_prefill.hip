@@ -22,6 +22,12 @@
 //    their A and B tiles in its L2 and no XCD gets more tiles than another.
 //  - MFMA work of 32-row sub-tiles that hold only padding rows is skipped.
 //  - A short, partial last round of tiles is cut along K (see split_of).
+//  - E4M3 weights (one fp32 scale per weight row): a B stage holds the codes,
+//    64-byte rows of four 16-byte chunks swizzled by (r >> 1) & 3; a lane's
+//    16-byte read carries its weights of two k-substeps (K is permuted the
+//    same way for A), widened to bf16 exactly in registers, and each output
+//    column is multiplied by its row's scale before the epilogue.  Half the
+//    weight bytes and half the B loads of bf16, for the same MFMAs.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -32,6 +38,14 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kABytes = BM * BK * 2;             // 32 KB: one K-stage of A
 constexpr int kBBytes = BN * BK * 2;             // 32 KB: one K-stage of B
 constexpr int kLdsBytes = 2 * kABytes + 3 * kBBytes;  // A double-, B triple-buffered: 160 KB
+constexpr int kB8Bytes = BN * BK;                // 16 KB: one K-stage of E4M3 B
+template <bool FP8> constexpr int b_stage_bytes() { return FP8 ? kB8Bytes : kBBytes; }
+// The gate/up epilogue stages a 256 x (128 + 8) fp32 tile through LDS (139 KB),
+// so every variant gets the whole 160 KB (one workgroup per CU either way).
+constexpr int kEpilogueBytes = BM * (BN / 2 + 8) * 4;
+static_assert(kEpilogueBytes <= kLdsBytes, "gate/up epilogue must fit in the LDS allocation");
+static_assert(2 * kABytes + 3 * kB8Bytes <= kLdsBytes, "E4M3 K stages must fit");
+template <bool FP8> constexpr int lds_bytes() { return kLdsBytes; }
 constexpr int MS = 4, NS = 8;                    // super-tile: MS m-tiles x NS n-tiles
 constexpr int kMaxSplit = 8;                     // pieces per tile of the last round
 constexpr int kMinPieceStages = 4;               // K-stages per piece, at least
@@ -47,6 +61,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// 16-byte chunk swizzle of the 64-byte rows of an E4M3 B stage
+__device__ __forceinline__ int swz4(int r) { return (r >> 1) & 3; }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (bytes 0..7 of two dwords, element i in byte i) widened to bf16.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 // First LDS row of B sub-tile j of wave column wn.
 template <bool GATE_UP>
@@ -69,25 +96,46 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 // The barrier before substep 3 of stage i+1 waits for A(i+2) and B(i+2)
 // only (vmcnt(8): the eight B(i+3) loads issued after them may still fly).
 // Stages s0 .. s0+n-1 (n >= 1); ACT = active 32-row A sub-tiles of this wave.
-template <bool GATE_UP, int ACT, class IssueA, class IssueB>
+// E4M3 B: four loads per wave and stage instead of eight, so B(i+3) takes
+// two per substep and the barrier waits with vmcnt(4).
+template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB>
 __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, int lane,
                                        IssueA& issue_a, IssueB& issue_b, f32x16 (&acc)[4][4]) {
+  constexpr int NBL = FP8 ? 4 : 8;  // B loads per wave and stage
   const int lr = lane & 31, kh = lane >> 5;
-  int rd[4];  // LDS byte offset of this lane's chunk inside a 32-row block, per k-substep
+  // LDS byte offset of this lane's A chunk inside a 32-row block, per k-substep.
+  // bf16: substep ks takes K chunk 2ks + kh.  E4M3: substeps 2m, 2m+1 take
+  // chunks 4m + 2kh and 4m + 2kh + 1, so a lane's B bytes of both are one
+  // 16-byte chunk (2m + kh) of its 64-byte B row.
+  int rd[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) rd[ks] = (lr * 8 + ((2 * ks + kh) ^ swz(lr))) * 16;
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c = FP8 ? 4 * (ks >> 1) + 2 * kh + (ks & 1) : 2 * ks + kh;
+    rd[ks] = (lr * 8 + (c ^ swz(lr))) * 16;
+  }
+  int rd8[2];  // E4M3 B: byte offset of chunk 2m + kh inside a 32-row block
+#pragma unroll
+  for (int m = 0; m < 2; ++m) rd8[m] = lr * 64 + ((2 * m + kh) ^ swz4(lr)) * 16;
 
   bf16x8 fa[2][4], fb[2][4];
+  u32x4 fq[4];  // E4M3 B: the codes of two substeps
   // fragments of k-substep ks of local stage ls (B buffer bb) into register set `slot`
   auto read = [&](int ls, int bb, int ks, int slot) {
     const char* sa = lds + (ls & 1) * kABytes;
-    const char* sb = lds + 2 * kABytes + bb * kBBytes;
+    const char* sb = lds + 2 * kABytes + bb * b_stage_bytes<FP8>();
 #pragma unroll
     for (int i = 0; i < ACT; ++i)
       fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + rd[ks]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + b_row_of<GATE_UP>(wn, j) * 128 + rd[ks]);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (FP8) {
+        if ((ks & 1) == 0)
+          fq[j] = *reinterpret_cast<const u32x4*>(sb + b_row_of<GATE_UP>(wn, j) * 64 + rd8[ks >> 1]);
+        fb[slot][j] = e4m3x8_to_bf16(fq[j][2 * (ks & 1)], fq[j][2 * (ks & 1) + 1]);
+      } else {
+        fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + b_row_of<GATE_UP>(wn, j) * 128 + rd[ks]);
+      }
+    }
   };
   auto mma = [&](int slot) {
 #pragma unroll
@@ -116,9 +164,9 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
 
-  issue_b(s0, 0, 0, 8);
+  issue_b(s0, 0, 0, NBL);
   issue_a(s0, 0, 0, 8);
-  if (n > 1) issue_b(s0 + 1, 1, 0, 8);
+  if (n > 1) issue_b(s0 + 1, 1, 0, NBL);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   if (n > 1) issue_a(s0 + 1, 1, 0, 4);
@@ -131,17 +179,20 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     mma(0);
     pattern();
     read(i, bcur, 2, 0);
-    issue_b(s0 + a2, b2, 0, 4);
+    issue_b(s0 + a2, b2, 0, NBL / 2);
     mma(1);
     pattern();
     read(i, bcur, 3, 1);
-    issue_b(s0 + a2, b2, 4, 8);
+    issue_b(s0 + a2, b2, NBL / 2, NBL);
     mma(0);
     pattern();
-    // vmcnt(8): A(i+1) and B(i+1) landed, B(i+2) may still fly; lgkmcnt(0):
+    // vmcnt(NBL): A(i+1) and B(i+1) landed, B(i+2) may still fly; lgkmcnt(0):
     // this wave's reads of stage i are done.  A plain s_barrier, since the
     // fence of __syncthreads would wait for every load.
-    __builtin_amdgcn_s_waitcnt(0x0078);
+    if constexpr (FP8)
+      __builtin_amdgcn_s_waitcnt(0x0074);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0078);
     __builtin_amdgcn_s_barrier();
     bcur = bcur == 2 ? 0 : bcur + 1;
     b2 = b2 == 2 ? 0 : b2 + 1;
@@ -210,7 +261,7 @@ __device__ __forceinline__ void tile_coords(int64_t L, int64_t mt, int64_t nt_n,
   n_tile = sn * NS + inner / mh;
 }
 
-template <bool GATE_UP>
+template <bool GATE_UP, bool FP8>
 __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   // The V - R whole tiles are cut into 8 equal runs, one per XCD: the
   // hardware deals workgroup b to XCD b % 8, so XCD x executes run x in
@@ -255,11 +306,19 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const __amdgpu_buffer_rsrc_t rsA =
       GATE_UP ? make_rsrc(p.A, (uint32_t)p.a_bytes)
               : make_rsrc(p.A + row0 * p.lda, (uint32_t)(BM * p.lda * 2));
-  const bf16_t* Bg = shared ? static_cast<const bf16_t*>(p.B_shared)
-                            : static_cast<const bf16_t*>(p.B_routed) +
-                                  (int64_t)g * (GATE_UP ? 2 : 1) * (int64_t)N * K;
-  const __amdgpu_buffer_rsrc_t rsB =
-      make_rsrc(Bg, (uint32_t)((int64_t)(GATE_UP ? 2 : 1) * N * K * 2));
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per weight
+  const int64_t brows = (int64_t)(GATE_UP ? 2 : 1) * N;  // weight rows of this group
+  const char* Bg = shared ? static_cast<const char*>(p.B_shared)
+                          : static_cast<const char*>(p.B_routed) + (int64_t)g * brows * K * EB;
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Bg, (uint32_t)(brows * K * EB));
+  // weight row of B-tile row r (0..255), or -1 past the matrix
+  auto b_weight_row = [&](int r) {
+    if (GATE_UP) {
+      const int half = r >> 7, f = n0 + (r & 127);
+      return f < N ? half * N + f : -1;
+    }
+    return n0 + r < N ? n0 + r : -1;
+  };
   uint32_t offA[8], offB[8];
   const int sub = lane >> 3;
 #pragma unroll
@@ -270,35 +329,49 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     if (GATE_UP) {
       const int t = r < valid_rows ? p.row_token[row0 + r] : -1;
       offA[j] = t >= 0 ? (uint32_t)t * (uint32_t)(p.lda * 2) + kb : kOob;
-      const int half = r >> 7, f = n0 + (r & 127);
-      offB[j] = f < N ? (uint32_t)(half * N + f) * (uint32_t)(K * 2) + kb : kOob;
     } else {
       offA[j] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + kb : kOob;
-      const int n = n0 + r;
-      offB[j] = n < N ? (uint32_t)n * (uint32_t)(K * 2) + kb : kOob;
+    }
+    if constexpr (!FP8) {
+      const int wr = b_weight_row(r);
+      offB[j] = wr >= 0 ? (uint32_t)wr * (uint32_t)(K * 2) + kb : kOob;
+    } else if (j < 4) {
+      // E4M3: load j writes 16 rows of 64 bytes; lane i carries row +i/4 and
+      // 16-byte K chunk (i%4) ^ swz4(row)
+      const int r8 = (wave * 4 + j) * 16 + (lane >> 2);
+      const int wr = b_weight_row(r8);
+      const uint32_t kb8 = ((lane & 3) ^ swz4(r8)) * 16;
+      offB[j] = wr >= 0 ? (uint32_t)wr * (uint32_t)K + kb8 : kOob;
     }
   }
   const int kcl = (lane & 7);  // chunk position within the 8 of a row, before the swizzle
 
   // loads j in [j0, j1) of the A (or B) rows of K-stage `stage` into A (or B)
   // buffer `buf`; chunks at or past K (only in the last stage when
-  // K % 64 != 0) read as zero
+  // K % 64 != 0) read as zero.  An E4M3 chunk of 16 codes that straddles K
+  // (K % 16 == 8) brings 8 codes past K, which meet zero A.
   auto issue = [&](bool isB, int stage, int buf, int j0, int j1) {
     const int k0 = stage * BK;
-    char* base = isB ? lds + 2 * kABytes + buf * kBBytes : lds + buf * kABytes;
+    const bool b8 = FP8 && isB;
+    char* base = isB ? lds + 2 * kABytes + buf * b_stage_bytes<FP8>() : lds + buf * kABytes;
     const bool tail = k0 + BK > K;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < j0 || j >= j1) continue;
       uint32_t o = isB ? offB[j] : offA[j];
       if (tail) {
-        const int r = (wave * 8 + j) * 8 + sub;
-        const int kc = kcl ^ swz(r);
-        if (k0 + kc * 8 >= K) o = kOob;
+        if (b8) {
+          const int r8 = (wave * 4 + j) * 16 + (lane >> 2);
+          if (k0 + ((lane & 3) ^ swz4(r8)) * 16 >= K) o = kOob;
+        } else {
+          const int r = (wave * 8 + j) * 8 + sub;
+          const int kc = kcl ^ swz(r);
+          if (k0 + kc * 8 >= K) o = kOob;
+        }
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA,
-                                               (lds_void*)(base + (wave * 8 + j) * 1024), 16, o,
-                                               k0 * 2, 0, 0);
+      const int blk = b8 ? wave * 4 + j : wave * 8 + j;  // 1-KB block of the stage
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA, (lds_void*)(base + blk * 1024), 16,
+                                               o, k0 * (isB ? EB : 2), 0, 0);
     }
   };
   auto issue_a = [&](int stage, int buf, int j0, int j1) { issue(false, stage, buf, j0, j1); };
@@ -320,13 +393,28 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int s0 = piece ? (int)((int64_t)part * nk / S) : 0;
   const int s1 = piece ? (int)((int64_t)(part + 1) * nk / S) : nk;
   switch (act) {
-    case 4: k_loop<GATE_UP, 4>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 3: k_loop<GATE_UP, 3>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 2: k_loop<GATE_UP, 2>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 1: k_loop<GATE_UP, 1>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    default: k_loop<GATE_UP, 0>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 4: k_loop<GATE_UP, 4, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 3: k_loop<GATE_UP, 3, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 2: k_loop<GATE_UP, 2, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 1: k_loop<GATE_UP, 1, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    default: k_loop<GATE_UP, 0, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
   }
   auto a_row = [&](int i) { return wm * 128 + i * 32; };
+
+  // E4M3: every output column times the scale of its weight row
+  if constexpr (FP8) {
+    const float* Sg = shared ? p.S_shared : p.S_routed + (int64_t)g * brows;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int wr = b_weight_row(b_row_of<GATE_UP>(wn, j) + lr);
+      const float sc = wr >= 0 ? Sg[wr] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= act) continue;
+        acc[i][j] *= sc;
+      }
+    }
+  }
 
   // ------------------------------------------------ pieces of a split tile
   if (piece) {  // row-major fp32 partial tile, columns in LDS B-row order
@@ -358,7 +446,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     // idle) LDS so that each lane writes 16 bytes of H at a time, and padding
     // rows are not written.  Rows are padded to 136 floats so the two row
     // groups of a 64-lane write land on different banks.
-    constexpr int kHs = BN / 2 + 8;
+    constexpr int kHs = BN / 2 + 8;  // kEpilogueBytes = BM * kHs * 4
     float* hs = reinterpret_cast<float*>(lds);
     __syncthreads();  // every wave is done reading the K stages
 #pragma unroll
@@ -405,14 +493,16 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void moe_gemm_gate_up_prefill_kernel(GroupedGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  prefill_tile<true>(p, lds);
+  prefill_tile<true, FP8>(p, lds);
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void moe_gemm_down_prefill_kernel(GroupedGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  prefill_tile<false>(p, lds);
+  prefill_tile<false, FP8>(p, lds);
 }
 
 // Finishes the cut tiles of the last round: block b owns rows
@@ -479,14 +569,16 @@ __global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p
   }
 }
 
-hipError_t launch(bool gate_up, GroupedGemm g, hipStream_t s) {
+template <bool FP8>
+hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
+  constexpr int lds = lds_bytes<FP8>();
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      e = hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel<FP8>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -506,10 +598,10 @@ hipError_t launch(bool gate_up, GroupedGemm g, hipStream_t s) {
   const int64_t blocks = (g.max_tiles * g.n_tiles_n + 7) / 8 * 8 + (g.ctas > 0 ? g.ctas : 0);
   if (blocks == 0) return hipSuccess;
   if (gate_up)
-    hipLaunchKernelGGL(moe_gemm_gate_up_prefill_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes,
+    hipLaunchKernelGGL(moe_gemm_gate_up_prefill_kernel<FP8>, dim3((unsigned)blocks), dim3(256), lds,
                        s, g);
   else
-    hipLaunchKernelGGL(moe_gemm_down_prefill_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes, s,
+    hipLaunchKernelGGL(moe_gemm_down_prefill_kernel<FP8>, dim3((unsigned)blocks), dim3(256), lds, s,
                        g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.ctas <= 0) return e;
@@ -519,6 +611,10 @@ hipError_t launch(bool gate_up, GroupedGemm g, hipStream_t s) {
   else
     hipLaunchKernelGGL(moe_gemm_split_fixup_kernel<false>, dim3(fix_blocks), dim3(256), 0, s, g);
   return hipGetLastError();
+}
+
+hipError_t launch(bool gate_up, const GroupedGemm& g, hipStream_t s) {
+  return g.fp8 ? launch_fmt<true>(gate_up, g, s) : launch_fmt<false>(gate_up, g, s);
 }
 
 }  // namespace

@@ -43,6 +43,12 @@ int choose_block_m(const moe_shape* s) {
   const int64_t rows = (int64_t)s->T * s->k;
   if (rows <= (int64_t)20 * s->E) return 16;
   if (rows <= (int64_t)48 * s->E) return 32;
+  // The 256-row tiles move E4M3 weights in 16-code chunks, which must not
+  // straddle the end of a row; other widths keep the 32-row tiles, whose
+  // loads check K in 8-element steps.
+  if (s->weight_format == MOE_WEIGHTS_FP8_E4M3 &&
+      (s->D % 16 || s->F % 16 || s->F_shared % 16))
+    return 32;
   return 256;
 }
 
@@ -64,7 +70,6 @@ int make_plan(const moe_shape* s, Plan* p) {
   p->max_tiles = p->cap_rows / p->BM + 1;
   p->ldh = p->F > p->Fs ? p->F : p->Fs;
   p->fp8 = s->weight_format == MOE_WEIGHTS_FP8_E4M3;
-  if (p->fp8 && p->BM == 256) return MOE_ERR_UNSUPPORTED;  // decode-sized tiles only
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;

@@ -97,8 +97,6 @@ def _fwd(lib, shape, w, y=FAKE, ws=FAKE, ws_bytes=1 << 40):
     (dict(has_router_bias=3), B.MOE_ERR_INVALID_ARG),
     (dict(has_router_bias=-1), B.MOE_ERR_INVALID_ARG),
     (dict(weight_format=2), B.MOE_ERR_INVALID_ARG),
-    # E4M3 weights: decode-sized row tiles only (T*k / E <= 48 rows per expert)
-    (dict(weight_format=1, T=4096), B.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 30, k=8), B.MOE_ERR_UNSUPPORTED)])
 def test_shape_errors(lib, kw, code):
     assert _fwd(lib, _shape(**kw), _weights()) == code
@@ -209,3 +207,15 @@ def test_fp8_scale_errors(lib):
     s2 = _shape(weight_format=1, F_shared=64)
     sc = dict(w_gate_up_scale=FAKE, w_down_scale=FAKE, ws_gate_up=FAKE, ws_down=FAKE)
     assert _fwd(lib, s2, _weights(**sc)) == B.MOE_ERR_INVALID_ARG  # no shared scales
+
+
+def test_block_m_for_e4m3_widths(lib):
+    """E4M3 weights keep the 32-row tiles when a width is not a multiple of 16."""
+    def bm(**kw):
+        return lib.moe_block_m(ctypes.byref(_shape(**kw)))
+    assert bm(T=4096, D=4096, E=8, F=14336, k=2, weight_format=1) == 256
+    assert bm(T=4096, D=4096, E=8, F=14344, k=2, weight_format=1) == 32
+    assert bm(T=4096, D=4104, E=8, F=14336, k=2, weight_format=1) == 32
+    assert bm(T=4096, D=4096, E=8, F=14336, k=2, F_shared=8, weight_format=1) == 32
+    assert bm(T=4096, D=4104, E=8, F=14336, k=2, weight_format=0) == 256
+    assert bm(T=16, D=4104, E=8, F=14336, k=2, weight_format=1) == 16

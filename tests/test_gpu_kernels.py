@@ -282,6 +282,11 @@ FP8_CASES = [
     (40, 200, 8, 2, 136, 0),      # K tails: D and F not multiples of 64 (nor of 16)
     (5, 128, 8, 2, 256, 64),
     (1, 1024, 16, 4, 512, 0),
+    (2048, 256, 8, 2, 512, 0),    # 256-row tiles
+    (1500, 320, 8, 2, 208, 0),    # 256-row tiles, ragged M, N and K (F % 64 == 16)
+    (1500, 320, 8, 2, 200, 0),    # F % 16 == 8: E4M3 keeps the 32-row tiles at any T
+    (700, 512, 16, 4, 256, 256),  # 256-row tiles with the shared expert
+    (512, 512, 8, 2, 512, 0),     # both GEMMs cut along K in their last round
 ]
 
 
@@ -289,11 +294,16 @@ FP8_CASES = [
 def test_layer_fp8_weights(T, D, E, k, F, Fs):
     """E4M3 expert weights with per-row scales against the oracle."""
     s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, fp8=True)
-    assert moe.moe_block_m(moe.make_shape(T, D, E, F, k, Fs, weight_format=1)) in (16, 32)
+    bm = moe.moe_block_m(moe.make_shape(T, D, E, F, k, Fs, weight_format=1))
+    print("BM =", bm)
+    if F % 16 or D % 16:
+        assert bm in (16, 32)
+    elif T * k > 48 * E:
+        assert bm == 256
     _layer_parity(W.make_inputs(s, seed=T + D))
 
 
-@pytest.mark.parametrize("T,D,E,k,F,Fs", FP8_CASES[:4])
+@pytest.mark.parametrize("T,D,E,k,F,Fs", FP8_CASES[:4] + FP8_CASES[5:8])
 def test_layer_fp8_power_of_two_scales_match_bf16(T, D, E, k, F, Fs):
     """With power-of-two row scales every dequantised weight is a bf16 value
     and the scaling commutes with every rounding, so the E4M3 kernels and the

@@ -87,6 +87,11 @@ def test_mixtral_prefill():
     _run("mixtral_prefill")
 
 
+def test_mixtral_prefill_fp8_weights():
+    """The Mixtral-shaped prefill layer with E4M3 expert weights."""
+    _run("mixtral_prefill", fp8=True)
+
+
 def test_mixtral_skewed():
     loads = _run("mixtral_skewed")
     assert loads[0] > 0.4 * loads.sum()
