@@ -71,6 +71,9 @@ def _load():
             lib.oracle_experts_q.restype = ctypes.c_int
             lib.oracle_experts_q.argtypes = [_p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32,
                                              _i32, _i32, _i32, _i32, _i32, _p, _p, _p, _i64, _p, _p]
+            lib.oracle_backward.restype = ctypes.c_int
+            lib.oracle_backward.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]
             lib.oracle_e4m3_decode.restype = None
             lib.oracle_e4m3_decode.argtypes = [_p, _i64, _p]
             lib.oracle_align.restype = ctypes.c_int
@@ -211,6 +214,48 @@ def forward(inp):
     ids, p, margin, _ = route(inp.x, inp.w_g, inp.router_bias, inp.shape.k,
                               select_only=inp.shape.bias_select)
     return experts(inp, ids, p), ids, p, margin
+
+
+def backward(inp, ids, p, dy):
+    """Gradients of sum_t <dy[t], y[t]> for the routing (ids [T,k], p [T,k]):
+    a dict of float64 arrays dx [T,D], dw_g [E,D], d_bias [E] (zero unless the
+    bias is part of the logits), dw_gate_up [E,2F,D], dw_down [E,D,F],
+    dws_gate_up [2Fs,D] / dws_down [D,Fs] (shared expert only) and dp [T,k]
+    (<dy, expert output> per slot).  bf16 expert weights only."""
+    lib = _load()
+    s = inp.shape
+    T = inp.x.shape[0]
+    if inp.w_gate_up.dtype != torch.bfloat16:
+        raise TypeError("the backward oracle takes bf16 expert weights")
+    px, kx = _bf16_ptr(inp.x)
+    pg, kg = _bf16_ptr(inp.w_g)
+    pgu, k1 = _bf16_ptr(inp.w_gate_up)
+    pdn, k2 = _bf16_ptr(inp.w_down)
+    psgu, k3 = _bf16_ptr(inp.ws_gate_up)
+    psdn, k4 = _bf16_ptr(inp.ws_down)
+    ids = np.ascontiguousarray(ids, np.int32)
+    p = np.ascontiguousarray(p, np.float64)
+    dyf = np.ascontiguousarray(dy, np.float32)
+    if ids.shape != (T, s.k) or p.shape != (T, s.k) or dyf.shape != (T, s.D):
+        raise ValueError("shape mismatch")
+    out = dict(dx=np.empty((T, s.D)), dw_g=np.empty((s.E, s.D)), d_bias=np.empty(s.E),
+               dw_gate_up=np.empty((s.E, 2 * s.F, s.D)), dw_down=np.empty((s.E, s.D, s.F)),
+               dp=np.empty((T, s.k)))
+    if s.Fs:
+        out["dws_gate_up"] = np.empty((2 * s.Fs, s.D))
+        out["dws_down"] = np.empty((s.D, s.Fs))
+    mode = 1 if (inp.router_bias is not None and not s.bias_select) else 0
+
+    def ptr(name):
+        return out[name].ctypes.data if name in out else None
+
+    rc = lib.oracle_backward(px, pg, pgu, pdn, psgu, psdn, T, s.D, s.E, s.F, s.k, s.Fs, mode,
+                             ids.ctypes.data, p.ctypes.data, dyf.ctypes.data, ptr("dx"),
+                             ptr("dw_g"), ptr("d_bias"), ptr("dw_gate_up"), ptr("dw_down"),
+                             ptr("dws_gate_up"), ptr("dws_down"), ptr("dp"))
+    if rc:
+        raise ValueError("oracle_backward failed: %d" % rc)
+    return out
 
 
 def align(ids, E: int, block_m: int, shared: bool = False):

@@ -329,6 +329,189 @@ int oracle_experts(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t*
                               p, tokens, n_tokens, y, macs);
 }
 
+/* ---------------------------------------------------------------- backward */
+
+/*
+ * Backward pass of the layer for a given routing: the gradients of the scalar
+ * sum_t <dy[t], y[t]> with respect to x, the router weight (and a bias inside
+ * the logits), and every expert weight.  The pages' training sections ("Mixture
+ * of Experts optimiza Transformers y LLMs", section on training; "Transformers
+ * v5 El Secreto Detrás de los Modelos MoE Más Rápidos", section "Entrenamiento
+ * MoE") give no formulas, so this is the chain rule of the forward pass above:
+ *   O_j = W_down[e_j] h_j,  y = sum_j p_j O_j (+ shared),  p = softmax over the
+ *   chosen logits.  The top-k choice is piecewise constant and passes no
+ *   gradient; the softmax gives dl_j = p_j (dp_j - sum_i p_i dp_i) with
+ *   dp_j = <dy, O_j> on the chosen logits, 0 on the others.
+ *   SwiGLU: h = SiLU(g) u, SiLU'(g) = s (1 + g (1 - s)), s = 1 / (1 + e^-g).
+ * Inputs: bf16 x [T,D], w_g [E,D], w_gate_up [E,2F,D], w_down [E,D,F], shared
+ * ws_gate_up [2Fs,D], ws_down [D,Fs] (or NULL); ids/p [T,k] (the routing);
+ * dy fp32 [T,D].  bias_mode: 1 when a bias is part of the logits (then dbias
+ * gets sum_t dl[t,e]); otherwise dbias is zero (a selection-only bias passes
+ * no gradient).  Outputs (double, overwritten): dx [T,D], dwg [E,D], dbias [E]
+ * (or NULL), dwgu [E,2F,D], dwdn [E,D,F], dwsgu [2Fs,D], dwsdn [D,Fs] (NULL
+ * without a shared expert), dp [T,k] (or NULL).  Weight gradients are summed
+ * over tokens in ascending order.  Returns 0, -1 on invalid sizes, -2 on
+ * allocation failure.
+ */
+int oracle_backward(const uint16_t* x, const uint16_t* w_g, const uint16_t* w_gate_up,
+                    const uint16_t* w_down, const uint16_t* ws_gate_up, const uint16_t* ws_down,
+                    int64_t T, int32_t D, int32_t E, int32_t F, int32_t k, int32_t Fs,
+                    int32_t bias_mode, const int32_t* ids, const double* p, const float* dy,
+                    double* dx, double* dwg, double* dbias, double* dwgu, double* dwdn,
+                    double* dwsgu, double* dwsdn, double* dp_out) {
+  if (T < 0 || D <= 0 || E <= 0 || F <= 0 || k <= 0 || k > E || Fs < 0) return -1;
+  if (Fs > 0 && (!ws_gate_up || !ws_down || !dwsgu || !dwsdn)) return -1;
+  for (int64_t a = 0; a < T * k; ++a)
+    if (ids[a] < 0 || ids[a] >= E) return -1;
+  const int64_t S = k + (Fs > 0 ? 1 : 0); /* slots per token, the shared expert last */
+  const int32_t Fm = F > Fs ? F : Fs;
+  /* per (token, slot): h, dg, du (Fm each), and the slot's dO scale and dl */
+  double* hs = (double*)malloc(sizeof(double) * (size_t)(T * S * Fm + 1));
+  double* dgs = (double*)malloc(sizeof(double) * (size_t)(T * S * Fm + 1));
+  double* dus = (double*)malloc(sizeof(double) * (size_t)(T * S * Fm + 1));
+  double* dls = (double*)malloc(sizeof(double) * (size_t)(T * k + 1));
+  if (!hs || !dgs || !dus || !dls) {
+    free(hs); free(dgs); free(dus); free(dls);
+    return -2;
+  }
+  int err = 0;
+  /* pass 1, per token: forward recomputation, dp, dl, SwiGLU backward, dx */
+#pragma omp parallel
+  {
+    double* xd = (double*)malloc(sizeof(double) * (size_t)D);
+    double* g = (double*)malloc(sizeof(double) * (size_t)Fm);
+    double* u = (double*)malloc(sizeof(double) * (size_t)Fm);
+    double* dpv = (double*)malloc(sizeof(double) * (size_t)k);
+    if (!xd || !g || !u || !dpv) {
+#pragma omp atomic write
+      err = -2;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t t = 0; t < T; ++t) {
+        for (int32_t d = 0; d < D; ++d) xd[d] = bf(x[t * D + d]);
+        const float* dyt = dy + t * D;
+        double* dxt = dx + t * D;
+        for (int32_t d = 0; d < D; ++d) dxt[d] = 0.0;
+        for (int64_t j = 0; j < S; ++j) {
+          const int shared_slot = j == k;
+          const int32_t e = shared_slot ? 0 : ids[t * k + j];
+          const int32_t Fj = shared_slot ? Fs : F;
+          const uint16_t* gu = shared_slot ? ws_gate_up : w_gate_up + (int64_t)e * 2 * F * D;
+          const uint16_t* dn = shared_slot ? ws_down : w_down + (int64_t)e * D * F;
+          const double coef = shared_slot ? 1.0 : p[t * k + j];
+          double* h = hs + (t * S + j) * Fm;
+          double* dg = dgs + (t * S + j) * Fm;
+          double* du = dus + (t * S + j) * Fm;
+          for (int32_t f = 0; f < Fj; ++f) {
+            double a = 0.0, b = 0.0;
+            for (int32_t d = 0; d < D; ++d) a += bf(gu[(int64_t)f * D + d]) * xd[d];
+            for (int32_t d = 0; d < D; ++d) b += bf(gu[(int64_t)(Fj + f) * D + d]) * xd[d];
+            g[f] = a;
+            u[f] = b;
+            h[f] = a / (1.0 + exp(-a)) * b;
+          }
+          /* dp_j = <dy, O_j> and dh = W_down^T (coef dy) */
+          if (!shared_slot) {
+            double s = 0.0;
+            for (int32_t d = 0; d < D; ++d) {
+              double o = 0.0;
+              for (int32_t f = 0; f < Fj; ++f) o += bf(dn[(int64_t)d * Fj + f]) * h[f];
+              s += (double)dyt[d] * o;
+            }
+            dpv[j] = s;
+          }
+          for (int32_t f = 0; f < Fj; ++f) {
+            double dh = 0.0;
+            for (int32_t d = 0; d < D; ++d) dh += coef * (double)dyt[d] * bf(dn[(int64_t)d * Fj + f]);
+            const double sg = 1.0 / (1.0 + exp(-g[f]));
+            dg[f] = dh * u[f] * sg * (1.0 + g[f] * (1.0 - sg));
+            du[f] = dh * g[f] * sg;
+          }
+          for (int32_t d = 0; d < D; ++d) {
+            double v = 0.0;
+            for (int32_t f = 0; f < Fj; ++f)
+              v += dg[f] * bf(gu[(int64_t)f * D + d]) + du[f] * bf(gu[(int64_t)(Fj + f) * D + d]);
+            dxt[d] += v;
+          }
+        }
+        /* softmax over the chosen logits */
+        double sp = 0.0;
+        for (int32_t j = 0; j < k; ++j) sp += p[t * k + j] * dpv[j];
+        for (int32_t j = 0; j < k; ++j) {
+          const double dl = p[t * k + j] * (dpv[j] - sp);
+          dls[t * k + j] = dl;
+          if (dp_out) dp_out[t * k + j] = dpv[j];
+          const uint16_t* wr = w_g + (int64_t)ids[t * k + j] * D;
+          for (int32_t d = 0; d < D; ++d) dxt[d] += dl * bf(wr[d]);
+        }
+      }
+    }
+    free(xd); free(g); free(u); free(dpv);
+  }
+  /* pass 2: weight gradients, one output row per iteration, tokens in order */
+  if (!err) {
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < (int64_t)E * D; ++r) { /* dW_g[e,d], dW_down[e,d,:] */
+      const int32_t e = (int32_t)(r / D), d = (int32_t)(r % D);
+      double gsum = 0.0;
+      double* dwr = dwdn + r * F;
+      for (int32_t f = 0; f < F; ++f) dwr[f] = 0.0;
+      for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+          if (ids[t * k + j] != e) continue;
+          gsum += dls[t * k + j] * bf(x[t * D + d]);
+          const double c = p[t * k + j] * (double)dy[t * D + d];
+          const double* h = hs + (t * S + j) * Fm;
+          for (int32_t f = 0; f < F; ++f) dwr[f] += c * h[f];
+        }
+      dwg[r] = gsum;
+    }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < (int64_t)E * 2 * F; ++r) { /* dW_gate_up[e,r',:] */
+      const int32_t e = (int32_t)(r / (2 * F)), q = (int32_t)(r % (2 * F));
+      double* dwr = dwgu + r * D;
+      for (int32_t d = 0; d < D; ++d) dwr[d] = 0.0;
+      for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+          if (ids[t * k + j] != e) continue;
+          const double c = q < F ? dgs[(t * S + j) * Fm + q] : dus[(t * S + j) * Fm + q - F];
+          for (int32_t d = 0; d < D; ++d) dwr[d] += c * bf(x[t * D + d]);
+        }
+    }
+    if (dbias)
+      for (int32_t e = 0; e < E; ++e) {
+        double s = 0.0;
+        if (bias_mode == 1)
+          for (int64_t a = 0; a < T * k; ++a)
+            if (ids[a] == e) s += dls[a];
+        dbias[e] = s;
+      }
+    if (Fs > 0) {
+#pragma omp parallel for schedule(dynamic, 4)
+      for (int32_t d = 0; d < D; ++d) {
+        double* dwr = dwsdn + (int64_t)d * Fs;
+        for (int32_t f = 0; f < Fs; ++f) dwr[f] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+          const double c = (double)dy[t * D + d];
+          const double* h = hs + (t * S + k) * Fm;
+          for (int32_t f = 0; f < Fs; ++f) dwr[f] += c * h[f];
+        }
+      }
+#pragma omp parallel for schedule(dynamic, 4)
+      for (int32_t q = 0; q < 2 * Fs; ++q) {
+        double* dwr = dwsgu + (int64_t)q * D;
+        for (int32_t d = 0; d < D; ++d) dwr[d] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+          const double c = q < Fs ? dgs[(t * S + k) * Fm + q] : dus[(t * S + k) * Fm + q - Fs];
+          for (int32_t d = 0; d < D; ++d) dwr[d] += c * bf(x[t * D + d]);
+        }
+      }
+    }
+  }
+  free(hs); free(dgs); free(dus); free(dls);
+  return err;
+}
+
 /* ------------------------------------------------------------------- align */
 
 /*
