@@ -238,6 +238,47 @@ int moe_forward_timed(const moe_shape* shape, const moe_weights* w, float* y, in
 int moe_expert_load(const moe_shape* shape, const void* workspace, size_t ws_bytes,
                     int32_t* counts, void* stream);
 
+/*
+ * Backward pass: the gradients of sum_t <dy[t], y[t]> for the routing a
+ * moe_forward call returned, by the chain rule of the forward pass.  The
+ * pages' training sections ("Mixture of Experts optimiza Transformers y
+ * LLMs", section on training; "Transformers v5 El Secreto Detrás de los
+ * Modelos MoE Más Rápidos", section "Entrenamiento MoE") run training on
+ * grouped-GEMM kernels; the gradients themselves are those of the function:
+ *  - the top-k choice is piecewise constant and passes no gradient; the
+ *    softmax over the chosen gives dl_j = p_j (dp_j - sum_i p_i dp_i),
+ *    dp_j = <dy, O_j> (O_j: slot j's expert output); other logits get 0;
+ *  - SwiGLU: dg = dh u SiLU'(g), du = dh SiLU(g), dh = W_down^T (p_j dy);
+ *  - dx = sum_j W_gate_up^T [dg du] (+ shared) + sum_j dl_j W_g[e_j];
+ *  - dW_down[e] = sum over e's rows of (p dy) h^T, dW_gate_up[e] = [dg du] x^T,
+ *    dW_g[e] = sum dl x, d_bias[e] = sum dl (a bias inside the logits only; a
+ *    selection-only bias or none: d_bias is zero), the shared expert with weight 1.
+ * bf16 expert weights and no shard (MOE_ERR_UNSUPPORTED otherwise).
+ *   shape, w       as for the moe_forward call (w->x, w->w_g, the expert
+ *                  weights; the bias is not read)
+ *   topk_ids, topk_w  that call's routing [T, k]
+ *   dy             fp32 [T, D]
+ *   grads          outputs, fp32, overwritten
+ *   workspace      device buffer of ws_bytes >= moe_backward_workspace_size(shape)
+ * The dx rows and every sum run in a fixed order: the gradients are bitwise
+ * reproducible.  Gradient products take bf16 operands (dy, h, dg, du, x are
+ * rounded to bf16 for the MFMAs) with fp32 accumulation.
+ */
+typedef struct moe_grads {
+  float* dx;          /* [T, D] */
+  float* dw_g;        /* [E, D] */
+  float* d_bias;      /* [E], or NULL */
+  float* dw_gate_up;  /* [E, 2F, D] */
+  float* dw_down;     /* [E, D, F] */
+  float* dws_gate_up; /* [2*F_shared, D], or NULL when F_shared == 0 */
+  float* dws_down;    /* [D, F_shared], or NULL when F_shared == 0 */
+} moe_grads;
+
+int moe_backward_workspace_size(const moe_shape* shape, size_t* bytes);
+int moe_backward(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
+                 const float* topk_w, const float* dy, const moe_grads* grads, void* workspace,
+                 size_t ws_bytes, void* stream);
+
 /* Static text for an error code (for MOE_ERR_HIP: the last HIP error seen by
  * this thread).  Never NULL. */
 const char* moe_strerror(int code);

@@ -24,7 +24,8 @@ MOE_ERR_ALIGNMENT = -4
 MOE_ERR_HIP = -5
 
 EXPORTS = ("moe_workspace_size", "moe_block_m", "moe_forward", "moe_route", "moe_align",
-           "moe_forward_routed", "moe_forward_timed", "moe_expert_load", "moe_strerror")
+           "moe_forward_routed", "moe_forward_timed", "moe_expert_load",
+           "moe_backward_workspace_size", "moe_backward", "moe_strerror")
 
 
 class MoEError(RuntimeError):
@@ -46,6 +47,12 @@ class Weights(ctypes.Structure):
                 ("ws_gate_up", ctypes.c_void_p), ("ws_down", ctypes.c_void_p),
                 ("w_gate_up_scale", ctypes.c_void_p), ("w_down_scale", ctypes.c_void_p),
                 ("ws_gate_up_scale", ctypes.c_void_p), ("ws_down_scale", ctypes.c_void_p)]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [("dx", ctypes.c_void_p), ("dw_g", ctypes.c_void_p), ("d_bias", ctypes.c_void_p),
+                ("dw_gate_up", ctypes.c_void_p), ("dw_down", ctypes.c_void_p),
+                ("dws_gate_up", ctypes.c_void_p), ("dws_down", ctypes.c_void_p)]
 
 
 _lib = None
@@ -73,6 +80,10 @@ def load_library(path: str = LIB_PATH):
             lib.moe_forward_timed.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P,
                                               P, P, ctypes.c_size_t, P, P]
             lib.moe_expert_load.argtypes = [ctypes.POINTER(Shape), P, ctypes.c_size_t, P, P]
+            lib.moe_backward_workspace_size.argtypes = [ctypes.POINTER(Shape),
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+            lib.moe_backward.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P, P,
+                                         ctypes.POINTER(Grads), P, ctypes.c_size_t, P]
             lib.moe_strerror.argtypes = [ctypes.c_int]
             lib.moe_strerror.restype = ctypes.c_char_p
             for name in EXPORTS[:-1]:
@@ -353,8 +364,50 @@ def moe_expert_load(shape: Shape, workspace, counts=None):
     return counts
 
 
+def backward_workspace_size(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_backward_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def moe_backward(x, w_g, w_gate_up, w_down, k, topk_ids, topk_w, dy, router_bias=None,
+                 ws_gate_up=None, ws_down=None, *, bias_select=False, workspace=None, grads=None):
+    """Gradients of sum <dy, y> for the routing (topk_ids, topk_w) of a forward
+    call with the same tensors.  Returns a dict of fp32 tensors dx, dw_g,
+    d_bias, dw_gate_up, dw_down (and dws_gate_up, dws_down with a shared
+    expert); ``grads`` may hold preallocated ones."""
+    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    _dev(w_g, "w_g", torch.bfloat16, (E, D))
+    _dev(topk_ids, "topk_ids", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    _dev(dy, "dy", torch.float32, (T, D))
+    if router_bias is not None:
+        _dev(router_bias, "router_bias", torch.float32, (E,))
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, bias_mode(router_bias, bias_select))
+    Fs = shape.F_shared
+    dev = x.device
+    sizes = dict(dx=(T, D), dw_g=(E, D), d_bias=(E,), dw_gate_up=(E, 2 * F, D), dw_down=(E, D, F))
+    if Fs:
+        sizes.update(dws_gate_up=(2 * Fs, D), dws_down=(D, Fs))
+    out = dict(grads or {})
+    for name, shp in sizes.items():
+        if name not in out:
+            out[name] = torch.empty(shp, dtype=torch.float32, device=dev)
+        _dev(out[name], name, torch.float32, shp)
+    if workspace is None:
+        workspace = torch.empty(max(backward_workspace_size(shape), 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    gr = Grads(*[_ptr(out.get(n)) for n, _ in Grads._fields_])
+    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
+    _check(load_library().moe_backward(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids),
+                                       _ptr(topk_w), _ptr(dy), ctypes.byref(gr), _ptr(workspace),
+                                       workspace.numel(), _stream(dev)))
+    return out
+
+
 # the C names, one to one
 moe_workspace_size = workspace_size
+moe_backward_workspace_size = backward_workspace_size
 moe_block_m = block_m
 moe_strerror = strerror
 

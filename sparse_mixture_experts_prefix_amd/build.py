@@ -15,7 +15,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["router.hip", "align.hip", "gemm_prefill.hip", "gemm_decode.hip", "combine.hip",
-           "api.cpp", "plan.cpp"]
+           "backward.hip", "api.cpp", "plan.cpp"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

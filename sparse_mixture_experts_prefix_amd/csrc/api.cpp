@@ -134,6 +134,127 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   return MOE_OK;
 }
 
+// Backward pass for a given routing (see moe_backward in moe.h).
+int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weights* w,
+                 const int32_t* ids, const float* wts, const float* dy, const moe_grads* gr,
+                 void* ws, hipStream_t s) {
+  using namespace moe;
+  const Plan& P = B.P;
+  int32_t* counts = at<int32_t>(ws, P.off_counts);
+  int32_t* offsets = at<int32_t>(ws, P.off_offsets);
+  int32_t* padded = at<int32_t>(ws, P.off_padded);
+  int32_t* n_tiles = at<int32_t>(ws, P.off_ntiles);
+  int32_t* sorted = at<int32_t>(ws, P.off_sorted);
+  int32_t* row_of = at<int32_t>(ws, P.off_rowof);
+  int32_t* row_token = at<int32_t>(ws, P.off_rowtoken);
+  int32_t* tile_group = at<int32_t>(ws, P.off_tilegroup);
+  int32_t* row_assign = at<int32_t>(ws, B.off_rowa);
+  uint16_t* xr = at<uint16_t>(ws, B.off_xr);
+  uint16_t* dyr = at<uint16_t>(ws, B.off_dyr);
+  float* gu = at<float>(ws, B.off_gu);
+  float* dhp = at<float>(ws, B.off_dhp);
+  uint16_t* dgu = at<uint16_t>(ws, B.off_dgu);
+  float* dxr = at<float>(ws, P.off_yp);
+  float* dp = at<float>(ws, B.off_dp);
+  float* dl = at<float>(ws, B.off_dl);
+  uint16_t* wdt = at<uint16_t>(ws, B.off_wdt);
+  uint16_t* wdts = at<uint16_t>(ws, B.off_wdts);
+  uint16_t* wgut = at<uint16_t>(ws, B.off_wgut);
+  uint16_t* wguts = at<uint16_t>(ws, B.off_wguts);
+  const int E = (int)P.E_loc, D = (int)P.D, F = (int)P.F, Fs = (int)P.Fs, T = (int)P.T,
+            k = (int)P.k, ldh = (int)P.ldh;
+  const int64_t cap = P.cap_rows;
+  const int G = P.G;
+  const bool prefill = P.BM == 256;
+  int ctas = 0;
+  if (prefill) {
+    hipError_t e0 = split_ctas(&ctas);
+    if (e0 != hipSuccess) return hip_fail(e0);
+  }
+  hipError_t e = launch_align(ids, T, k, E, 0, P.BM, Fs > 0 ? T : 0, counts, offsets, padded, sorted,
+                              row_of, row_token, tile_group, n_tiles, nullptr, s);
+  if (e == hipSuccess) e = launch_row_assign(row_of, (int)P.A, cap, row_assign, s);
+  const int32_t* total = padded + G;  // rows in use
+  if (e == hipSuccess) e = launch_gather_rows(w->x, false, row_token, total, cap, D, xr, s);
+  if (e == hipSuccess) e = launch_gather_rows(dy, true, row_token, total, cap, D, dyr, s);
+  const uint16_t* wgu = static_cast<const uint16_t*>(w->w_gate_up);
+  const uint16_t* wdn = static_cast<const uint16_t*>(w->w_down);
+  if (e == hipSuccess) e = launch_transpose(wdn, wdt, E, D, F, s);
+  if (e == hipSuccess) e = launch_transpose(wgu, wgut, E, 2 * F, D, s);
+  if (Fs > 0) {
+    if (e == hipSuccess)
+      e = launch_transpose(static_cast<const uint16_t*>(w->ws_down), wdts, 1, D, Fs, s);
+    if (e == hipSuccess)
+      e = launch_transpose(static_cast<const uint16_t*>(w->ws_gate_up), wguts, 1, 2 * Fs, D, s);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+
+  // row-space products on the forward's grouped GEMM (rows x weight^T)
+  GroupedGemm g{};
+  g.E = E;
+  g.tile_group = tile_group;
+  g.n_tiles = n_tiles;
+  g.max_tiles = P.max_tiles;
+  g.min_tiles = (P.A + P.BM - 1) / P.BM + (Fs > 0 ? (P.T + P.BM - 1) / P.BM : 0);
+  g.BM = P.BM;
+  g.group_count = counts;
+  g.group_padded = padded;
+  g.ctas = ctas;
+  g.partial = prefill ? at<float>(ws, P.off_partial) : nullptr;
+  auto gemm = [&](const uint16_t* A, int64_t lda, const void* Br, const void* Bs, int Nr, int Ns,
+                  int Kr, int Ks, float* C, int64_t ldc) {
+    GroupedGemm q = g;
+    q.A = A;
+    q.lda = lda;
+    q.a_bytes = cap * lda * 2;
+    q.B_routed = Br;
+    q.B_shared = Fs > 0 ? Bs : nullptr;
+    q.N_routed = Nr;
+    q.N_shared = Ns;
+    q.K_routed = Kr;
+    q.K_shared = Ks;
+    q.C = C;
+    q.ldc = ldc;
+    return prefill ? launch_gemm_down_prefill(q, s) : launch_gemm_down_decode(q, s);
+  };
+  // g | u again, then dh' = W_down^T dy
+  e = gemm(xr, D, w->w_gate_up, w->ws_gate_up, 2 * F, 2 * Fs, D, D, gu, 2 * ldh);
+  if (e == hipSuccess) e = gemm(dyr, D, wdt, wdts, F, Fs, D, D, dhp, ldh);
+  BwdRows rows{cap, total, row_token, row_assign, padded, tile_group, wts, dy, E, P.BM, D, F, Fs, ldh,
+               gu, dgu, dgu, xr};
+  if (e == hipSuccess) e = launch_swiglu_bwd(rows, dhp, dp, s);
+  if (e == hipSuccess) e = launch_router_bwd(wts, dp, T, k, dl, s);
+  // per-row dx = [dg du] W_gate_up, then dx
+  if (e == hipSuccess) e = gemm(dgu, 2 * ldh, wgut, wguts, D, D, 2 * F, 2 * Fs, dxr, D);
+  if (e == hipSuccess)
+    e = launch_combine_bwd(dxr, row_of, ids, dl, static_cast<const uint16_t*>(w->w_g), padded, T, D, k,
+                           E, Fs > 0 ? 1 : 0, gr->dx, s);
+  if (e == hipSuccess)
+    e = launch_router_wgrad(dl, static_cast<const uint16_t*>(w->x), offsets, sorted, E, k, D,
+                            shape->has_router_bias == MOE_ROUTER_BIAS_LOGITS ? 1 : 0, gr->dw_g,
+                            gr->d_bias, s);
+  if (e != hipSuccess) return hip_fail(e);
+
+  // weight gradients over transposed row buffers
+  uint16_t* dot = at<uint16_t>(ws, B.off_dot);
+  uint16_t* ht = at<uint16_t>(ws, B.off_ht);
+  uint16_t* dgut = at<uint16_t>(ws, B.off_dgut);
+  uint16_t* xt = at<uint16_t>(ws, B.off_xt);
+  e = launch_rows_transpose(rows, 0, D, dot, s);
+  if (e == hipSuccess) e = launch_rows_transpose(rows, 1, ldh, ht, s);
+  if (e == hipSuccess) e = launch_rows_transpose(rows, 2, 2 * ldh, dgut, s);
+  if (e == hipSuccess) e = launch_rows_transpose(rows, 3, D, xt, s);
+  auto tiles = [](int64_t n) { return (n + 255) / 256; };
+  WgradGemm wd{dot, ht, cap, D, ldh, D, F, D, Fs, E, G, padded, gr->dw_down, gr->dws_down,
+               tiles(D), tiles(F > Fs ? F : Fs)};
+  if (e == hipSuccess) e = launch_gemm_wgrad(wd, s);
+  WgradGemm wu{dgut, xt, cap, 2 * ldh, D, 2 * F, D, 2 * Fs, D, E, G, padded, gr->dw_gate_up,
+               gr->dws_gate_up, tiles(2 * ldh), tiles(D)};
+  if (e == hipSuccess) e = launch_gemm_wgrad(wu, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -284,6 +405,49 @@ int moe_expert_load(const moe_shape* shape, const void* workspace, size_t ws_byt
     e = hipMemcpyAsync(counts, src, sizeof(int32_t) * (size_t)P.G, hipMemcpyDeviceToDevice, s);
   }
   return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_backward_workspace_size(const moe_shape* shape, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe::BwdPlan B;
+  int rc = moe::make_backward_plan(shape, &B);
+  if (rc) return rc;
+  *bytes = B.total;
+  return MOE_OK;
+}
+
+int moe_backward(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
+                 const float* topk_w, const float* dy, const moe_grads* grads, void* workspace,
+                 size_t ws_bytes, void* stream) {
+  moe::BwdPlan B;
+  int rc = moe::make_backward_plan(shape, &B);
+  if (rc) return rc;
+  rc = moe::check_weights(shape, w, true);
+  if (rc) return rc;
+  const moe::Plan& P = B.P;
+  if (!grads || !grads->dw_g || !grads->dw_gate_up || !grads->dw_down) return MOE_ERR_INVALID_ARG;
+  if (P.Fs > 0 && (!grads->dws_gate_up || !grads->dws_down)) return MOE_ERR_INVALID_ARG;
+  const void* outs[] = {grads->dx, grads->dw_g, grads->d_bias, grads->dw_gate_up, grads->dw_down,
+                        grads->dws_gate_up, grads->dws_down};
+  for (const void* q : outs)
+    if (q && !moe::aligned16(q)) return MOE_ERR_ALIGNMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (P.T == 0) {  // no tokens: every weight gradient is zero
+    const int64_t E = P.E_loc, D = P.D, F = P.F, Fs = P.Fs;
+    hipError_t e = moe::launch_fill_f32(grads->dw_g, E * D, s);
+    if (e == hipSuccess && grads->d_bias) e = moe::launch_fill_f32(grads->d_bias, E, s);
+    if (e == hipSuccess) e = moe::launch_fill_f32(grads->dw_gate_up, E * 2 * F * D, s);
+    if (e == hipSuccess) e = moe::launch_fill_f32(grads->dw_down, E * D * F, s);
+    if (e == hipSuccess && Fs > 0) e = moe::launch_fill_f32(grads->dws_gate_up, 2 * Fs * D, s);
+    if (e == hipSuccess && Fs > 0) e = moe::launch_fill_f32(grads->dws_down, D * Fs, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+  }
+  if (!topk_ids || !topk_w || !dy || !grads->dx || !workspace) return MOE_ERR_INVALID_ARG;
+  if (!moe::aligned16(topk_ids) || !moe::aligned16(topk_w) || !moe::aligned16(dy) ||
+      !moe::aligned16(workspace))
+    return MOE_ERR_ALIGNMENT;
+  if (ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+  return run_backward(B, shape, w, topk_ids, topk_w, dy, grads, workspace, s);
 }
 
 const char* moe_strerror(int code) {

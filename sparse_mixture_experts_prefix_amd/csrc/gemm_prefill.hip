@@ -617,7 +617,101 @@ hipError_t launch(bool gate_up, const GroupedGemm& g, hipStream_t s) {
   return g.fp8 ? launch_fmt<true>(gate_up, g, s) : launch_fmt<false>(gate_up, g, s);
 }
 
+// ------------------------------------------------------------ weight gradients
+// Group g: C_g[m][n] = sum_k A[m][k0 + k] * B[n][k0 + k] over the group's
+// rows k0 = padded[g] .. padded[g+1] - 1 (read on the device), with the same
+// 256 x 256 x 64 tiles and K loop as the forward.  A and B are transposed
+// row buffers (one row per output row / column, the layer's rows along K),
+// whose padding rows hold zeros.  A group with no rows stores zeros.
+__global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int64_t per_group = p.tiles_m * p.tiles_n;
+  const int g = (int)(blockIdx.x / per_group);
+  const int64_t rem = blockIdx.x - (int64_t)g * per_group;
+  const int mt = (int)(rem / p.tiles_n), nt = (int)(rem % p.tiles_n);
+  const bool shared = g >= p.E;
+  const int M = shared ? p.M_shared : p.M_routed;
+  const int N = shared ? p.N_shared : p.N_routed;
+  const int m0 = mt * BM, n0 = nt * BN;
+  if (m0 >= M || n0 >= N) return;
+  float* C = shared ? p.C_shared : p.C_routed + (int64_t)g * M * N;
+  const int k0g = p.padded[g];
+  const int K = p.padded[g + 1] - k0g;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, kh = lane >> 5;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (K > 0) {
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, (uint32_t)(p.rows_a * p.ld * 2));
+    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.B, (uint32_t)(p.rows_b * p.ld * 2));
+    uint32_t offA[8], offB[8];
+    const int sub = lane >> 3;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (wave * 8 + j) * 8 + sub;
+      const uint32_t kb = ((lane & 7) ^ swz(r)) * 16 + (uint32_t)k0g * 2;
+      offA[j] = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)(p.ld * 2) + kb : kOob;
+      offB[j] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(p.ld * 2) + kb : kOob;
+    }
+    auto issue = [&](bool isB, int stage, int buf, int j0, int j1) {
+      const int k0 = stage * BK;
+      char* base = isB ? lds + 2 * kABytes + buf * kBBytes : lds + buf * kABytes;
+      const bool tail = k0 + BK > K;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < j0 || j >= j1) continue;
+        uint32_t o = isB ? offB[j] : offA[j];
+        if (tail) {
+          const int r = (wave * 8 + j) * 8 + sub;
+          if (k0 + ((lane & 7) ^ swz(r)) * 8 >= K) o = kOob;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA,
+                                                 (lds_void*)(base + (wave * 8 + j) * 1024), 16, o,
+                                                 k0 * 2, 0, 0);
+      }
+    };
+    auto issue_a = [&](int stage, int buf, int j0, int j1) { issue(false, stage, buf, j0, j1); };
+    auto issue_b = [&](int stage, int buf, int j0, int j1) { issue(true, stage, buf, j0, j1); };
+    k_loop<false, 4, false>(lds, 0, (K + BK - 1) / BK, wm, wn, lane, issue_a, issue_b, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + b_row_of<false>(wn, j) + lr;
+        if (n < N) C[(int64_t)m * N + n] = acc[i][j][r];
+      }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gemm_wgrad(const WgradGemm& g, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_wgrad_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t blocks = (int64_t)g.G * g.tiles_m * g.tiles_n;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_gemm_wgrad_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes, s, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_gate_up_prefill(const GroupedGemm& g, hipStream_t s) {
   return launch(true, g, s);

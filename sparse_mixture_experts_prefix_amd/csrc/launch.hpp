@@ -77,6 +77,60 @@ hipError_t launch_gemm_down_prefill(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_gemm_gate_up_decode(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_gemm_down_decode(const GroupedGemm& g, hipStream_t s);
 
+// Weight gradients of the grouped GEMMs: for each group g (E routed, then
+// the shared one when G > E), C_g[m][n] = sum over the group's rows r in
+// [padded[g], padded[g+1]) of A[m][r] * B[n][r].  A: rows_a rows, B: rows_b
+// rows, both bf16 with row stride ld; rows past the group's count are zero.
+struct WgradGemm {
+  const uint16_t* A;
+  const uint16_t* B;
+  int64_t ld, rows_a, rows_b;
+  int M_routed, N_routed, M_shared, N_shared;
+  int E, G;
+  const int32_t* padded;
+  float* C_routed;  // [E][M_routed][N_routed]
+  float* C_shared;  // [M_shared][N_shared]
+  int64_t tiles_m, tiles_n;  // 256 x 256 tiles per group (max over both kinds)
+};
+hipError_t launch_gemm_wgrad(const WgradGemm& g, hipStream_t s);
+
+// ---- backward pass (backward.hip)
+// The rows of one backward call: align outputs and per-row buffers.
+struct BwdRows {
+  int64_t cap;                 // allocated rows
+  const int32_t* total;        // padded[G] on the device: rows in use
+  const int32_t* row_token;
+  const int32_t* row_assign;
+  const int32_t* padded;
+  const int32_t* tile_group;
+  const float* topk_w;         // [T k]
+  const float* dy;             // [T][D]
+  int E, BM, D, F, Fs, ldh;
+  const float* gu;             // [cap][2 ldh]
+  const uint16_t* dgu;         // [cap][2 ldh]
+  uint16_t* dgu_w;             // the same buffer, written by the SwiGLU backward
+  const uint16_t* xr;          // [cap][D]
+};
+hipError_t launch_gather_rows(const void* src, bool src_f32, const int32_t* row_token,
+                              const int32_t* total, int64_t cap, int D, uint16_t* dst, hipStream_t s);
+hipError_t launch_row_assign(const int32_t* row_of, int A, int64_t cap, int32_t* row_assign,
+                             hipStream_t s);
+hipError_t launch_fill_f32(float* out, int64_t n, hipStream_t s);
+// dst[b][c][r] = src[b][r][c] (bf16)
+hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t s);
+// dst[c][r] (row stride cap) of rows r in use; kind 0: p_r dy[t_r], 1: bf16(SiLU(g) u),
+// 2: dGU rows, 3: x rows
+hipError_t launch_rows_transpose(const BwdRows& b, int kind, int C, uint16_t* dst, hipStream_t s);
+hipError_t launch_swiglu_bwd(const BwdRows& b, const float* dhp, float* dp, hipStream_t s);
+hipError_t launch_router_bwd(const float* topk_w, const float* dp, int T, int k, float* dl,
+                             hipStream_t s);
+hipError_t launch_router_wgrad(const float* dl, const uint16_t* x, const int32_t* offsets,
+                               const int32_t* sorted_assign, int E, int k, int D, int bias_grad,
+                               float* dwg, float* dbias, hipStream_t s);
+hipError_t launch_combine_bwd(const float* dxr, const int32_t* row_of, const int32_t* ids,
+                              const float* dl, const uint16_t* w_g, const int32_t* padded, int T, int D,
+                              int k, int E, int has_shared, float* dx, hipStream_t s);
+
 // y[t] = sum_j w[t,j] * Yp[row_of[t*k+j]] (+ Yp[shared_base + t]) in fixed order.
 hipError_t launch_combine(const float* Yp, const int32_t* row_of, const float* wts,
                           const int32_t* padded, int T, int D, int k, int E, int has_shared,

@@ -98,6 +98,42 @@ int make_plan(const moe_shape* s, Plan* p) {
   return MOE_OK;
 }
 
+int make_backward_plan(const moe_shape* s, BwdPlan* b) {
+  int rc = make_plan(s, &b->P);
+  if (rc) return rc;
+  const Plan& P = b->P;
+  if (P.fp8) return MOE_ERR_UNSUPPORTED;                       // bf16 expert weights only
+  if (s->num_local_experts > 0 && s->num_local_experts != s->E) return MOE_ERR_UNSUPPORTED;
+  // the transposed row buffers are addressed through 32-bit buffer offsets
+  const int64_t widest = P.D > 2 * P.ldh ? P.D : 2 * P.ldh;
+  if (P.cap_rows * widest * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  size_t o = P.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  const size_t cap = (size_t)P.cap_rows;
+  b->off_rowa = take(sizeof(int32_t) * cap);
+  b->off_xr = take(2 * cap * P.D);
+  b->off_dyr = take(2 * cap * P.D);
+  b->off_gu = take(4 * cap * 2 * P.ldh);
+  b->off_dhp = take(4 * cap * P.ldh);
+  b->off_dgu = take(2 * cap * 2 * P.ldh);
+  b->off_dp = take(4 * (size_t)P.A);
+  b->off_dl = take(4 * (size_t)P.A);
+  b->off_wdt = take(2 * (size_t)P.E_loc * P.F * P.D);
+  b->off_wdts = take(2 * (size_t)P.Fs * P.D);
+  b->off_wgut = take(2 * (size_t)P.E_loc * P.D * 2 * P.F);
+  b->off_wguts = take(2 * (size_t)P.D * 2 * P.Fs);
+  b->off_dot = take(2 * (size_t)P.D * cap);
+  b->off_ht = take(2 * (size_t)P.ldh * cap);
+  b->off_dgut = take(2 * (size_t)2 * P.ldh * cap);
+  b->off_xt = take(2 * (size_t)P.D * cap);
+  b->total = o;
+  return MOE_OK;
+}
+
 int check_weights(const moe_shape* s, const moe_weights* w, bool need_router) {
   if (!w) return MOE_ERR_INVALID_ARG;
   if (s->T > 0 && !w->x) return MOE_ERR_INVALID_ARG;

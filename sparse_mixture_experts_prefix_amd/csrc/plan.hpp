@@ -38,6 +38,24 @@ struct Plan {
       off_rowtoken, off_tilegroup, off_h, off_yp, off_partial, off_rpart, total;
 };
 
+// Backward-pass workspace: the forward's layout (align outputs, split
+// partials; Yp holds the per-row dx) followed by the backward's buffers.
+// cap = P.cap_rows.
+struct BwdPlan {
+  Plan P;
+  size_t off_rowa;          // int32 [cap]: assignment of each row, -1 elsewhere
+  size_t off_xr, off_dyr;   // bf16 [cap][D]: x and dy rows in expert order
+  size_t off_gu;            // fp32 [cap][2 ldh]: g | u recomputed
+  size_t off_dhp;           // fp32 [cap][ldh]: W_down^T dy
+  size_t off_dgu;           // bf16 [cap][2 ldh]: dg | du
+  size_t off_dp, off_dl;    // fp32 [T k]
+  size_t off_wdt, off_wdts; // bf16 [E][F][D], [Fs][D]: W_down transposed
+  size_t off_wgut, off_wguts;  // bf16 [E][D][2F], [D][2Fs]: W_gate_up transposed
+  size_t off_dot, off_ht, off_dgut, off_xt;  // bf16 [D | ldh | 2 ldh | D][cap]
+  size_t total;
+};
+int make_backward_plan(const moe_shape* s, BwdPlan* b);
+
 // Shape checks shared by every entry point (MOE_OK or an error code).
 int check_shape(const moe_shape* s);
 

@@ -219,3 +219,40 @@ def test_block_m_for_e4m3_widths(lib):
     assert bm(T=4096, D=4096, E=8, F=14336, k=2, F_shared=8, weight_format=1) == 32
     assert bm(T=4096, D=4104, E=8, F=14336, k=2, weight_format=0) == 256
     assert bm(T=16, D=4104, E=8, F=14336, k=2, weight_format=1) == 16
+
+
+def test_grads_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct moe_grads \{(.*?)\} moe_grads;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\*\s*(\w+);", body)
+    assert names == [f[0] for f in B.Grads._fields_]
+
+
+def test_backward_errors(lib):
+    n = ctypes.c_size_t(0)
+    size = lib.moe_backward_workspace_size
+    assert size(ctypes.byref(_shape()), ctypes.byref(n)) == B.MOE_OK and n.value > 0
+    assert size(ctypes.byref(_shape(weight_format=1)), ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED
+    assert size(ctypes.byref(_shape(expert_begin=2, num_local_experts=4)),
+                ctypes.byref(n)) == B.MOE_ERR_UNSUPPORTED
+    assert size(ctypes.byref(_shape(k=0)), ctypes.byref(n)) == B.MOE_ERR_INVALID_ARG
+    size(ctypes.byref(_shape()), ctypes.byref(n))
+    s = _shape()
+    g = B.Grads(FAKE, FAKE, None, FAKE, FAKE, None, None)
+
+    def bwd(shape=s, w=None, grads=g, ids=FAKE, wts=FAKE, dy=FAKE, ws=FAKE, nb=n.value):
+        return lib.moe_backward(ctypes.byref(shape), ctypes.byref(w or _weights()), ids, wts, dy,
+                                ctypes.byref(grads) if grads is not None else None, ws, nb, None)
+
+    assert bwd(grads=None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(grads=B.Grads(FAKE, FAKE, None, None, FAKE, None, None)) == B.MOE_ERR_INVALID_ARG
+    assert bwd(dy=None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(dy=FAKE + 4) == B.MOE_ERR_ALIGNMENT
+    assert bwd(grads=B.Grads(FAKE, FAKE + 8, None, FAKE, FAKE, None, None)) == B.MOE_ERR_ALIGNMENT
+    assert bwd(nb=n.value - 1) == B.MOE_ERR_WORKSPACE
+    assert bwd(w=_weights(w_g=None)) == B.MOE_ERR_INVALID_ARG
+    # a shared expert needs its two gradient outputs
+    s2 = _shape(F_shared=64)
+    size(ctypes.byref(s2), ctypes.byref(n))
+    assert bwd(shape=s2, w=_weights(ws_gate_up=FAKE, ws_down=FAKE), nb=n.value) == B.MOE_ERR_INVALID_ARG
