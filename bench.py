@@ -75,6 +75,59 @@ def _cpu_baseline(inp, target_s):
                       "%.1f s wall" % (n, s.T, "same", s.k, " + shared expert" if s.Fs else "", t)}
 
 
+def _bench_backward(args, s, wl, g, moe, torch, W, dev):
+    """Backward pass timing: gradients of sum <dy, y> for the routing of one
+    forward call, on the same inputs; dy ~ N(0, 1) fp32."""
+    if s.fp8 or args.ep != 1:
+        raise SystemExit("--backward takes bf16 weights and the whole layer")
+    ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+    moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias, g.ws_gate_up, g.ws_down,
+                    topk_ids=ids, topk_w=wts, bias_select=s.bias_select)
+    dy = W.normal_f32((s.T, s.D), 0, 99, 1.0).to(dev)
+    shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, moe.bias_mode(g.router_bias, s.bias_select))
+    ws = torch.empty(moe.backward_workspace_size(shape), dtype=torch.uint8, device=dev)
+    grads = moe.moe_backward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, ids, wts, dy, g.router_bias,
+                             g.ws_gate_up, g.ws_down, bias_select=s.bias_select, workspace=ws)
+
+    def step():
+        moe.moe_backward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, ids, wts, dy, g.router_bias,
+                         g.ws_gate_up, g.ws_down, bias_select=s.bias_select, workspace=ws, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    _log("timed %d backward steps: %.3f ms/step" % (args.steps, ms))
+    # algorithmic work: dgrad and wgrad of the three expert products (6 each
+    # per routed row and unit of D*F, likewise for the shared expert) and the
+    # router's two products; the recomputation of g and u is not counted
+    rows = s.T * s.k
+    flops = 12 * rows * s.D * s.F + 12 * s.T * s.D * s.Fs + 4 * s.T * s.D * s.E
+    achieved = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "MoE-layer backward tokens/s",
+        "value": round(s.T * args.steps / elapsed, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded counter-based normal draws: x ~ N(0,1), weights ~ N(0,0.02), "
+                "dy ~ N(0,1), bf16 weights)",
+        "config": {"workload": wl.name, "pass": "backward", "T": s.T, "D": s.D, "E": s.E, "k": s.k,
+                   "d_ff": s.F, "shared_d_ff": s.Fs, "router_bias": bool(s.router_bias)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "moe_backward (whole call)", "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +146,9 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="expert weights as E4M3 codes with one fp32 scale per row (the same "
                          "draws quantised per row)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (moe_backward) for the routing of one forward "
+                         "call instead of the forward pass")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="run one plain device copy of this many GiB first (a known-size kernel "
                          "for calibrating rocprofv3 byte counters)")
@@ -181,6 +237,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         _log("copy calibration: %d bytes read, %d bytes written" % (n, n))
+
+    if args.backward:
+        _bench_backward(args, s, wl, g, moe, torch, W, dev)
+        return
 
     def step(i):
         q = sets[i % len(sets)]

@@ -220,8 +220,8 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   // g | u again, then dh' = W_down^T dy
   e = gemm(xr, D, w->w_gate_up, w->ws_gate_up, 2 * F, 2 * Fs, D, D, gu, 2 * ldh);
   if (e == hipSuccess) e = gemm(dyr, D, wdt, wdts, F, Fs, D, D, dhp, ldh);
-  BwdRows rows{cap, total, row_token, row_assign, padded, tile_group, wts, dy, E, P.BM, D, F, Fs, ldh,
-               gu, dgu, dgu, xr};
+  BwdRows rows{cap, B.ldt, total, row_token, row_assign, padded, tile_group, wts, dy, E, P.BM, D, F, Fs,
+               ldh, gu, dgu, dgu, xr};
   if (e == hipSuccess) e = launch_swiglu_bwd(rows, dhp, dp, s);
   if (e == hipSuccess) e = launch_router_bwd(wts, dp, T, k, dl, s);
   // per-row dx = [dg du] W_gate_up, then dx
@@ -245,10 +245,10 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   if (e == hipSuccess) e = launch_rows_transpose(rows, 2, 2 * ldh, dgut, s);
   if (e == hipSuccess) e = launch_rows_transpose(rows, 3, D, xt, s);
   auto tiles = [](int64_t n) { return (n + 255) / 256; };
-  WgradGemm wd{dot, ht, cap, D, ldh, D, F, D, Fs, E, G, padded, gr->dw_down, gr->dws_down,
+  WgradGemm wd{dot, ht, B.ldt, D, ldh, D, F, D, Fs, E, G, padded, counts, gr->dw_down, gr->dws_down,
                tiles(D), tiles(F > Fs ? F : Fs)};
   if (e == hipSuccess) e = launch_gemm_wgrad(wd, s);
-  WgradGemm wu{dgut, xt, cap, 2 * ldh, D, 2 * F, D, 2 * Fs, D, E, G, padded, gr->dw_gate_up,
+  WgradGemm wu{dgut, xt, B.ldt, 2 * ldh, D, 2 * F, D, 2 * Fs, D, E, G, padded, counts, gr->dw_gate_up,
                gr->dws_gate_up, tiles(2 * ldh), tiles(D)};
   if (e == hipSuccess) e = launch_gemm_wgrad(wu, s);
   if (e != hipSuccess) return hip_fail(e);

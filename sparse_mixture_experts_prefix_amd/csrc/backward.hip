@@ -59,24 +59,50 @@ __global__ void moe_row_assign_kernel(const int32_t* __restrict__ row_of, int A,
   if (a < A) row_assign[row_of[a]] = a;
 }
 
-// Batched transpose: dst[b][c][r] = src[b][r][c], bf16, 64 x 64 tiles through LDS.
+// 64 x 64 bf16 tiles through LDS: 16-byte loads along the source rows and
+// 16-byte stores along the destination rows.  LDS rows are 72 elements (144
+// bytes), so the eight rows a store gathers from one column sit on distinct
+// banks.  Needs R and C multiples of 8 (every width here is).
+typedef bf16_t tile_t[64][72];
+
+__device__ __forceinline__ u32x4 pack8(const bf16_t (&e)[8]) {
+  u32x4 v;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = (uint32_t)e[2 * u] | ((uint32_t)e[2 * u + 1] << 16);
+  return v;
+}
+
+// tile rows i (source rows r0 + i) are in the tile; write dst[c][r0 + ...] for
+// c in [c0, c0 + 64) and rows < R, row stride ld
+__device__ __forceinline__ void store_tile_t(const tile_t& tile, bf16_t* dst, int64_t ld, int64_t r0,
+                                             int c0, int64_t R, int C) {
+  for (int q = threadIdx.x; q < 512; q += blockDim.x) {
+    const int j = q >> 3, r8 = (q & 7) * 8;
+    const int c = c0 + j;
+    const int64_t r = r0 + r8;
+    if (c >= C || r >= R) continue;
+    bf16_t e[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) e[u] = tile[r8 + u][j];
+    st16(dst + (int64_t)c * ld + r, pack8(e));
+  }
+}
+
+// Batched transpose: dst[b][c][r] = src[b][r][c].
 __global__ __launch_bounds__(256) void moe_transpose_kernel(const bf16_t* __restrict__ src,
                                                             bf16_t* __restrict__ dst, int R, int C) {
-  __shared__ bf16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) tile_t tile;
   const int64_t b = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const bf16_t* s = src + b * (int64_t)R * C;
-  bf16_t* d = dst + b * (int64_t)R * C;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < R && c < C) tile[i][tx] = s[(int64_t)r * C + c];
+  for (int q = threadIdx.x; q < 512; q += blockDim.x) {
+    const int i = q >> 3, c8 = (q & 7) * 8;
+    const int r = r0 + i, c = c0 + c8;
+    const u32x4 v = (r < R && c < C) ? ld16(s + (int64_t)r * C + c) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(&tile[i][c8]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (r < R && c < C) d[(int64_t)c * R + r] = tile[tx][i];
-  }
+  store_tile_t(tile, dst + b * (int64_t)R * C, R, r0, c0, R, C);
 }
 
 // The row-space operands of the weight gradients, transposed: dst[c][r]
@@ -94,46 +120,56 @@ struct RowSource {
   const bf16_t* rows16;       // [rows][cols] (kind 2: stride 2 ldh; kind 3: stride D)
 };
 
-__device__ __forceinline__ float row_value(const RowSource& q, int64_t r, int c) {
+// columns c .. c + 7 (c % 8 == 0) of row r, as bf16
+__device__ __forceinline__ u32x4 row_values8(const RowSource& q, int64_t r, int c) {
   const int t = q.row_token[r];
-  if (t < 0) return 0.f;
+  if (t < 0) return u32x4{0, 0, 0, 0};
+  bf16_t e[8];
   switch (q.kind) {
     case 0: {
       const int a = q.row_assign[r];
       const float p = a >= 0 ? q.topk_w[a] : 1.f;  // the shared expert's rows: weight 1
-      return p * q.dy[(int64_t)t * q.D + c];
+      const float4* src = reinterpret_cast<const float4*>(q.dy + (int64_t)t * q.D + c);
+      const float4 v0 = src[0], v1 = src[1];
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) e[u] = f32_to_bf16(p * f[u]);
+      return pack8(e);
     }
     case 1: {
       const int Fg = q.tile_group[r / q.BM] >= q.E ? q.Fs : q.F;
-      if (c >= Fg) return 0.f;
-      const float g = q.gu[r * 2 * q.ldh + c], u = q.gu[r * 2 * q.ldh + Fg + c];
-      return bf16_to_f32(f32_to_bf16(silu(g) * u));
+      if (c >= Fg) return u32x4{0, 0, 0, 0};  // Fg % 8 == 0: a chunk is all in or all out
+      const float4* gp = reinterpret_cast<const float4*>(q.gu + r * 2 * q.ldh + c);
+      const float4* up = reinterpret_cast<const float4*>(q.gu + r * 2 * q.ldh + Fg + c);
+      const float4 g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
+      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int w = 0; w < 8; ++w) e[w] = f32_to_bf16(silu(g[w]) * u[w]);
+      return pack8(e);
     }
-    case 2: return bf16_to_f32(q.rows16[r * 2 * q.ldh + c]);
-    default: return bf16_to_f32(q.rows16[r * q.D + c]);
+    case 2: return ld16(q.rows16 + r * 2 * q.ldh + c);
+    default: return ld16(q.rows16 + r * q.D + c);
   }
 }
 
 __global__ __launch_bounds__(256) void moe_rows_transpose_kernel(RowSource q, const int32_t* total,
                                                                  int C, int64_t ld,
                                                                  bf16_t* __restrict__ dst) {
-  __shared__ bf16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) tile_t tile;
   const int64_t r0 = (int64_t)blockIdx.x * 64;  // rows on x: their count is the large one
   const int c0 = blockIdx.y * 64;
   const int64_t R = total[0];
   if (r0 >= R) return;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
+  for (int i8 = threadIdx.x; i8 < 512; i8 += blockDim.x) {
+    const int i = i8 >> 3, c8 = (i8 & 7) * 8;
     const int64_t r = r0 + i;
-    const int c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? f32_to_bf16(row_value(q, r, c)) : (bf16_t)0;
+    const int c = c0 + c8;
+    *reinterpret_cast<u32x4*>(&tile[i][c8]) =
+        (r < R && c < C) ? row_values8(q, r, c) : u32x4{0, 0, 0, 0};
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i;
-    const int64_t r = r0 + tx;
-    if (r < R && c < C) dst[(int64_t)c * ld + r] = tile[tx][i];
-  }
+  store_tile_t(tile, dst, ld, r0, c0, R, C);
 }
 
 // One wave per row: SwiGLU backward.  dh' = W_down^T dy (fp32 rows), p the
@@ -195,28 +231,34 @@ __global__ void moe_router_bwd_kernel(const float* __restrict__ topk_w, const fl
   for (int j = 0; j < k; ++j) dl[t * k + j] = topk_w[t * k + j] * (dp[t * k + j] - s);
 }
 
-// dW_g[e][d] = sum over expert e's assignments (ascending a) of dl_a x[t_a][d];
-// dbias[e] = the same sum of dl_a (bias inside the logits) or 0.
+// dW_g[e][d] = sum over expert e's assignments of dl_a x[t_a][d]: workgroup
+// (64 columns, e); wave w adds assignments i = i0 + w, i0 + w + 4, ... (in
+// order) and the four partial sums are added in wave order.  dbias[e] = the
+// same sum of dl_a (bias inside the logits) or 0.
 __global__ __launch_bounds__(256) void moe_router_wgrad_kernel(
     const float* __restrict__ dl, const bf16_t* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_assign, int k, int D, int bias_grad, float* __restrict__ dwg,
     float* __restrict__ dbias) {
+  __shared__ float part[4][64];
   const int e = blockIdx.y;
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int d = blockIdx.x * 64 + lane;
   const int i0 = offsets[e], i1 = offsets[e + 1];
-  if (d < D) {
-    float acc = 0.f;
-    for (int i = i0; i < i1; ++i) {
+  float acc = 0.f;
+  if (d < D)
+    for (int i = i0 + wave; i < i1; i += 4) {
       const int a = sorted_assign[i];
       acc += dl[a] * bf16_to_f32(x[(int64_t)(a / k) * D + d]);
     }
-    dwg[(int64_t)e * D + d] = acc;
-  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && d < D)
+    dwg[(int64_t)e * D + d] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
   if (dbias && blockIdx.x == 0 && threadIdx.x == 0) {
-    float s = 0.f;
+    float sb = 0.f;
     if (bias_grad)
-      for (int i = i0; i < i1; ++i) s += dl[sorted_assign[i]];
-    dbias[e] = s;
+      for (int i = i0; i < i1; ++i) sb += dl[sorted_assign[i]];
+    dbias[e] = sb;
   }
 }
 
@@ -279,7 +321,7 @@ hipError_t launch_rows_transpose(const BwdRows& b, int kind, int C, uint16_t* ds
   RowSource q{kind, b.dy, b.topk_w, b.row_token, b.row_assign, b.padded, b.tile_group, b.E, b.BM,
               b.D, b.F, b.Fs, b.ldh, b.gu, kind == 2 ? b.dgu : b.xr};
   hipLaunchKernelGGL(moe_rows_transpose_kernel, dim3((unsigned)((b.cap + 63) / 64), (C + 63) / 64),
-                     dim3(256), 0, s, q, b.total, C, b.cap, dst);
+                     dim3(256), 0, s, q, b.total, C, b.ldt, dst);
   return hipGetLastError();
 }
 
@@ -302,7 +344,7 @@ hipError_t launch_router_bwd(const float* topk_w, const float* dp, int T, int k,
 hipError_t launch_router_wgrad(const float* dl, const uint16_t* x, const int32_t* offsets,
                                const int32_t* sorted_assign, int E, int k, int D, int bias_grad,
                                float* dwg, float* dbias, hipStream_t s) {
-  hipLaunchKernelGGL(moe_router_wgrad_kernel, dim3((D + 255) / 256, E), dim3(256), 0, s, dl, x, offsets,
+  hipLaunchKernelGGL(moe_router_wgrad_kernel, dim3((D + 63) / 64, E), dim3(256), 0, s, dl, x, offsets,
                      sorted_assign, k, D, bias_grad, dwg, dbias);
   return hipGetLastError();
 }

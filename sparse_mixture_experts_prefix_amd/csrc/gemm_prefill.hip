@@ -619,7 +619,7 @@ hipError_t launch(bool gate_up, const GroupedGemm& g, hipStream_t s) {
 
 // ------------------------------------------------------------ weight gradients
 // Group g: C_g[m][n] = sum_k A[m][k0 + k] * B[n][k0 + k] over the group's
-// rows k0 = padded[g] .. padded[g+1] - 1 (read on the device), with the same
+// rows k0 = padded[g] .. padded[g] + counts[g] - 1 (read on the device), with the same
 // 256 x 256 x 64 tiles and K loop as the forward.  A and B are transposed
 // row buffers (one row per output row / column, the layer's rows along K),
 // whose padding rows hold zeros.  A group with no rows stores zeros.
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
   if (m0 >= M || n0 >= N) return;
   float* C = shared ? p.C_shared : p.C_routed + (int64_t)g * M * N;
   const int k0g = p.padded[g];
-  const int K = p.padded[g + 1] - k0g;
+  const int K = p.counts[g];  // the group's rows; its padding rows would add zeros
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

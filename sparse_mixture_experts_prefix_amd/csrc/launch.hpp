@@ -79,15 +79,17 @@ hipError_t launch_gemm_down_decode(const GroupedGemm& g, hipStream_t s);
 
 // Weight gradients of the grouped GEMMs: for each group g (E routed, then
 // the shared one when G > E), C_g[m][n] = sum over the group's rows r in
-// [padded[g], padded[g+1]) of A[m][r] * B[n][r].  A: rows_a rows, B: rows_b
-// rows, both bf16 with row stride ld; rows past the group's count are zero.
+// [padded[g], padded[g] + counts[g]) of A[m][r] * B[n][r].  A: rows_a rows,
+// B: rows_b rows, both bf16 with row stride ld; the group's padding rows hold
+// zeros (the K loop reads whole 8-element chunks).
 struct WgradGemm {
   const uint16_t* A;
   const uint16_t* B;
   int64_t ld, rows_a, rows_b;
   int M_routed, N_routed, M_shared, N_shared;
   int E, G;
-  const int32_t* padded;
+  const int32_t* padded;  // first row of each group
+  const int32_t* counts;  // rows of each group
   float* C_routed;  // [E][M_routed][N_routed]
   float* C_shared;  // [M_shared][N_shared]
   int64_t tiles_m, tiles_n;  // 256 x 256 tiles per group (max over both kinds)
@@ -98,6 +100,7 @@ hipError_t launch_gemm_wgrad(const WgradGemm& g, hipStream_t s);
 // The rows of one backward call: align outputs and per-row buffers.
 struct BwdRows {
   int64_t cap;                 // allocated rows
+  int64_t ldt;                 // row stride of the transposed row buffers (cap rounded up to 64)
   const int32_t* total;        // padded[G] on the device: rows in use
   const int32_t* row_token;
   const int32_t* row_assign;
@@ -118,7 +121,7 @@ hipError_t launch_row_assign(const int32_t* row_of, int A, int64_t cap, int32_t*
 hipError_t launch_fill_f32(float* out, int64_t n, hipStream_t s);
 // dst[b][c][r] = src[b][r][c] (bf16)
 hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t s);
-// dst[c][r] (row stride cap) of rows r in use; kind 0: p_r dy[t_r], 1: bf16(SiLU(g) u),
+// dst[c][r] (row stride ldt) of rows r in use; kind 0: p_r dy[t_r], 1: bf16(SiLU(g) u),
 // 2: dGU rows, 3: x rows
 hipError_t launch_rows_transpose(const BwdRows& b, int kind, int C, uint16_t* dst, hipStream_t s);
 hipError_t launch_swiglu_bwd(const BwdRows& b, const float* dhp, float* dp, hipStream_t s);

@@ -51,7 +51,8 @@ struct BwdPlan {
   size_t off_dp, off_dl;    // fp32 [T k]
   size_t off_wdt, off_wdts; // bf16 [E][F][D], [Fs][D]: W_down transposed
   size_t off_wgut, off_wguts;  // bf16 [E][D][2F], [D][2Fs]: W_gate_up transposed
-  size_t off_dot, off_ht, off_dgut, off_xt;  // bf16 [D | ldh | 2 ldh | D][cap]
+  size_t off_dot, off_ht, off_dgut, off_xt;  // bf16 [D | ldh | 2 ldh | D][ldt]
+  int64_t ldt;              // cap rounded up to a multiple of 64
   size_t total;
 };
 int make_backward_plan(const moe_shape* s, BwdPlan* b);
