@@ -191,14 +191,15 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int id_base, in
   return hipGetLastError();
 }
 
-__global__ void moe_fill_i32_kernel(int32_t* __restrict__ out, int n, int32_t v) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void moe_fill_i32_kernel(int32_t* __restrict__ out, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) out[i] = v;
 }
 
-hipError_t launch_fill_i32(int32_t* out, int n, int32_t v, hipStream_t s) {
+hipError_t launch_fill_i32(int32_t* out, int64_t n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, out, n, v);
+  hipLaunchKernelGGL(moe_fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, n,
+                     v);
   return hipGetLastError();
 }
 

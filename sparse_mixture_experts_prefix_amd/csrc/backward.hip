@@ -42,11 +42,6 @@ __global__ __launch_bounds__(256) void moe_gather_rows_kernel(const Src* __restr
     dst[r * D + d] = t >= 0 ? f32_to_bf16(load_f(src, (int64_t)t * D + d)) : (bf16_t)0;
 }
 
-__global__ void moe_fill_i32_rows_kernel(int32_t* __restrict__ out, int64_t n, int32_t v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = v;
-}
-
 __global__ void moe_fill_f32_kernel(float* __restrict__ out, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) out[i] = 0.f;
@@ -294,9 +289,8 @@ hipError_t launch_gather_rows(const void* src, bool src_f32, const int32_t* row_
 
 hipError_t launch_row_assign(const int32_t* row_of, int A, int64_t cap, int32_t* row_assign,
                              hipStream_t s) {
-  if (cap > 0)
-    hipLaunchKernelGGL(moe_fill_i32_rows_kernel, dim3((unsigned)((cap + 255) / 256)), dim3(256), 0, s,
-                       row_assign, cap, -1);
+  hipError_t e = launch_fill_i32(row_assign, cap, -1, s);
+  if (e != hipSuccess) return e;
   if (A > 0)
     hipLaunchKernelGGL(moe_row_assign_kernel, dim3((A + 255) / 256), dim3(256), 0, s, row_of, A,
                        row_assign);

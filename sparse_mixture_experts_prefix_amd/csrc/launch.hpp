@@ -38,7 +38,7 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int id_base, in
                         const RouteFinish* fin, hipStream_t s);
 
 // out[0..n) = v (a kernel, not a memset, so it is safe in a captured graph).
-hipError_t launch_fill_i32(int32_t* out, int n, int32_t v, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* out, int64_t n, int32_t v, hipStream_t s);
 
 struct GroupedGemm {
   const uint16_t* A;          // gate/up: x [T, D] (rows gathered by row_token); down: H
