@@ -18,8 +18,9 @@
 //    16-lane phases of the b128 operand reads on distinct banks.
 //  - The valid tiles are split into 8 equal runs, one per XCD (the hardware
 //    deals workgroups to the 8 XCDs round-robin), each walked in blocks of
-//    4 m-tiles x 8 n-tiles, so the workgroups an XCD runs together share
-//    their A and B tiles in its L2 and no XCD gets more tiles than another.
+//    up to 4 m-tiles of one expert x 8 n-tiles, so the workgroups an XCD runs
+//    together share their A and B tiles in its L2 and no XCD gets more tiles
+//    than another.
 //  - MFMA work of 32-row sub-tiles that hold only padding rows is skipped.
 //  - A short, partial last round of tiles is cut along K (see split_of).
 //  - E4M3 weights (one fp32 scale per weight row): a B stage holds the codes,
@@ -46,7 +47,7 @@ constexpr int kEpilogueBytes = BM * (BN / 2 + 8) * 4;
 static_assert(kEpilogueBytes <= kLdsBytes, "gate/up epilogue must fit in the LDS allocation");
 static_assert(2 * kABytes + 3 * kB8Bytes <= kLdsBytes, "E4M3 K stages must fit");
 template <bool FP8> constexpr int lds_bytes() { return kLdsBytes; }
-constexpr int MS = 4, NS = 8;                    // super-tile: MS m-tiles x NS n-tiles
+constexpr int MS = 4, NS = 8;                    // tile blocks: up to MS m-tiles x NS n-tiles
 constexpr int kMaxSplit = 8;                     // pieces per tile of the last round
 constexpr int kMinPieceStages = 4;               // K-stages per piece, at least
 constexpr int kSplitRounds = 4;                  // cut only when V < kSplitRounds * ctas
@@ -245,19 +246,26 @@ __device__ __forceinline__ Split split_of(const GroupedGemm& p) {
   return sp;
 }
 
-// Logical tile L -> (m_tile, n_tile): columns of NS n-tiles, and in each
-// column blocks of MS m-tiles x NS n-tiles, so consecutive tiles share their
-// A and B tiles.
-__device__ __forceinline__ void tile_coords(int64_t L, int64_t mt, int64_t nt_n, int64_t& m_tile,
+// Logical tile L -> (m_tile, n_tile): columns of NS n-tiles; inside a column
+// the groups in order, each cut into blocks of up to MS of its m-tiles x the
+// column's n-tiles, m-tile fastest.  Consecutive tiles (the workgroups an XCD
+// runs together) then share their A and B tiles, and a block never straddles
+// two experts' weights.
+__device__ __forceinline__ void tile_coords(const GroupedGemm& p, int64_t L, int64_t& m_tile,
                                             int64_t& n_tile) {
+  const int64_t mt = p.n_tiles[0];
   const int64_t colsz = mt * NS;
   const int64_t sn = L / colsz;
-  const int64_t cw = min((int64_t)NS, nt_n - sn * NS);  // n-tiles in this column
-  const int64_t rem = L - sn * colsz;
-  const int64_t mb = rem / (MS * cw);
-  const int64_t mh = min((int64_t)MS, mt - mb * MS);      // m-tiles in this block
-  const int64_t inner = rem - mb * MS * cw;
-  m_tile = mb * MS + inner % mh;
+  const int64_t cw = min((int64_t)NS, p.n_tiles_n - sn * NS);  // n-tiles in this column
+  const int64_t u = L - sn * colsz;                               // < mt * cw
+  const int g = p.tile_group[u / cw];
+  const int64_t t0 = p.group_padded[g] / p.BM;                   // the group's first m-tile
+  const int64_t mg = p.group_padded[g + 1] / p.BM - t0;          // and its m-tiles
+  const int64_t v = u - t0 * cw;                                  // < mg * cw
+  const int64_t mb = v / (MS * cw);                               // block of the group
+  const int64_t mh = min((int64_t)MS, mg - mb * MS);              // its m-tiles
+  const int64_t inner = v - mb * MS * cw;
+  m_tile = t0 + mb * MS + inner % mh;
   n_tile = sn * NS + inner / mh;
 }
 
@@ -285,7 +293,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const bool piece = L >= sp.n_dp;
   const int S = sp.S;
   int64_t m_tile, n_tile;
-  tile_coords(L, p.n_tiles[0], p.n_tiles_n, m_tile, n_tile);
+  tile_coords(p, L, m_tile, n_tile);
   const int g = p.tile_group[m_tile];
   const bool shared = g >= p.E;
   const int N = shared ? p.N_shared : p.N_routed;
@@ -519,7 +527,7 @@ __global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p
   const int64_t t = blockIdx.x / kFixBlocksPerTile;
   if (t >= sp.R) return;
   int64_t m_tile, n_tile;
-  tile_coords(sp.n_dp + t, p.n_tiles[0], p.n_tiles_n, m_tile, n_tile);
+  tile_coords(p, sp.n_dp + t, m_tile, n_tile);
   const int g = p.tile_group[m_tile];
   const int N = g >= p.E ? p.N_shared : p.N_routed;
   constexpr int NB = GATE_UP ? BN / 2 : BN;  // output columns of a tile
