@@ -50,6 +50,16 @@ struct Marks {
   }
 };
 
+// Row tiles that hold rows, as the host can bound them: each assignment sits
+// in at most one tile and each routed group's rows in ceil(rows / BM) tiles,
+// so at most min(T k, E) tiles for groups of at most BM rows (decode), plus
+// the shared expert's.
+int64_t busy_tiles(const moe::Plan& P) {
+  const int64_t routed = P.A < P.E_loc ? P.A : P.E_loc;
+  const int64_t est = routed > (P.A + P.BM - 1) / P.BM ? routed : (P.A + P.BM - 1) / P.BM;
+  return est + (P.Fs > 0 ? (P.T + P.BM - 1) / P.BM : 0);
+}
+
 // Everything after routing: align -> gate/up -> down -> combine.
 int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, const float* wts,
                 float* y, void* ws, hipStream_t s, Marks mk = Marks{nullptr},
@@ -96,6 +106,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   gu.n_tiles = n_tiles;
   gu.max_tiles = P.max_tiles;
   gu.min_tiles = (P.A + P.BM - 1) / P.BM + (P.Fs > 0 ? (P.T + P.BM - 1) / P.BM : 0);
+  gu.busy_tiles = busy_tiles(P);
   gu.C = H;
   gu.ldc = P.ldh;
   gu.BM = P.BM;
@@ -196,6 +207,7 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   g.n_tiles = n_tiles;
   g.max_tiles = P.max_tiles;
   g.min_tiles = (P.A + P.BM - 1) / P.BM + (Fs > 0 ? (P.T + P.BM - 1) / P.BM : 0);
+  g.busy_tiles = busy_tiles(P);
   g.BM = P.BM;
   g.group_count = counts;
   g.group_padded = padded;

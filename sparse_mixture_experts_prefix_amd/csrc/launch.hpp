@@ -56,6 +56,7 @@ struct GroupedGemm {
   const int32_t* n_tiles;     // device count of valid tiles
   int64_t max_tiles;          // host upper bound of n_tiles
   int64_t min_tiles;          // host lower bound of n_tiles when every id is valid
+  int64_t busy_tiles;         // host estimate of row tiles that hold rows (sizes decode column tiles)
   void* C;                    // gate/up: H bf16; down: Yp fp32
   int64_t ldc;                // elements
   int BM;
