@@ -176,14 +176,11 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int id_base, in
     if (T > kSmallRouteT || k > 8 || fin->E > kSmallRouteE) return hipErrorInvalidValue;
     f = *fin;
     lds = sizeof(float) * (size_t)T * (fin->E + 1) * (fin->sel ? 2 : 1);
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)moe_align_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)(sizeof(float) * 2 * kSmallRouteT * (kSmallRouteE + 1)));
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    // set once per process (a function-local static is initialised thread-safely)
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void*)moe_align_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)(sizeof(float) * 2 * kSmallRouteT * (kSmallRouteE + 1)));
+    if (attr != hipSuccess) return attr;
   }
   hipLaunchKernelGGL(moe_align_kernel, dim3(G), dim3(kThreads), lds, s, ids, T * k, k, E, id_base, BM,
                      shared_rows, counts, offsets, padded, sorted_assign, row_of, row_token,

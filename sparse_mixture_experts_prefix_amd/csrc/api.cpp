@@ -1,6 +1,7 @@
 // extern "C" entry points of libmoe (declared and documented in moe.h).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 
 #include "launch.hpp"
@@ -28,16 +29,16 @@ hipError_t split_ctas(int* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  static int cached[64] = {0};
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) {
-    *out = cached[dev];
+  static std::atomic<int> cached[64];  // zero-initialised; every writer stores the same value
+  if (dev >= 0 && dev < 64 && cached[dev].load(std::memory_order_relaxed) > 0) {
+    *out = cached[dev].load(std::memory_order_relaxed);
     return hipSuccess;
   }
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int n = cus < moe::kSplitCtas ? cus : moe::kSplitCtas;
-  if (dev >= 0 && dev < 64) cached[dev] = n;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   *out = n;
   return hipSuccess;
 }

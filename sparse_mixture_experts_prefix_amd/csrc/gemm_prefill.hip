@@ -580,16 +580,15 @@ __global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p
 template <bool FP8>
 hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
   constexpr int lds = lds_bytes<FP8>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel<FP8>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set once per process (a function-local static is initialised thread-safely)
+  static const hipError_t attr = [] {
+    const hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    return e != hipSuccess ? e
+                           : hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel<FP8>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  }();
+  if (attr != hipSuccess) return attr;
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
   const int NB = gate_up ? BN / 2 : BN;
   g.n_tiles_n = (nmax + NB - 1) / NB;
@@ -708,13 +707,9 @@ __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
 }  // namespace
 
 hipError_t launch_gemm_wgrad(const WgradGemm& g, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_wgrad_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)moe_gemm_wgrad_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (attr != hipSuccess) return attr;
   const int64_t blocks = (int64_t)g.G * g.tiles_m * g.tiles_n;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(moe_gemm_wgrad_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes, s, g);

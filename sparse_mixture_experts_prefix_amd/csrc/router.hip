@@ -126,13 +126,10 @@ hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias,
                       int T, int D, int E, int k, int32_t* ids, float* wts, hipStream_t s) {
   constexpr int kWaves = waves_for<NCT>();
   const size_t lds = sizeof(float) * kWaves * kTok * (16 * NCT + 1);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_router_kernel<NCT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set once per process (a function-local static is initialised thread-safely)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)moe_router_kernel<NCT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
   const int blocks = (T + kTok - 1) / kTok;
   hipLaunchKernelGGL(moe_router_kernel<NCT>, dim3(blocks), dim3(kWaves * 64), lds, s, x, w_g, bias,
                      sel, T, D, E, k, ids, wts);
