@@ -77,33 +77,56 @@ def _cpu_baseline(inp, target_s):
 
 def _bench_backward(args, s, wl, g, moe, torch, W, dev):
     """Backward pass timing: gradients of sum <dy, y> for the routing of one
-    forward call, on the same inputs; dy ~ N(0, 1) fp32."""
+    forward call, on the same inputs; dy ~ N(0, 1) fp32.  --saved: that call is
+    the training forward and the backward reads its saved g | u."""
     if s.fp8 or args.ep != 1:
         raise SystemExit("--backward takes bf16 weights and the whole layer")
     ids = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
     wts = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
-    moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias, g.ws_gate_up, g.ws_down,
-                    topk_ids=ids, topk_w=wts, bias_select=s.bias_select)
+    saved = None
+    if args.saved:
+        _, _, _, saved = moe.moe_forward_train(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias,
+                                               g.ws_gate_up, g.ws_down, bias_select=s.bias_select,
+                                               topk_ids=ids, topk_w=wts)
+    else:
+        moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias, g.ws_gate_up,
+                        g.ws_down, topk_ids=ids, topk_w=wts, bias_select=s.bias_select)
     dy = W.normal_f32((s.T, s.D), 0, 99, 1.0).to(dev)
     shape = moe.make_shape(s.T, s.D, s.E, s.F, s.k, s.Fs, moe.bias_mode(g.router_bias, s.bias_select))
     ws = torch.empty(moe.backward_workspace_size(shape), dtype=torch.uint8, device=dev)
     grads = moe.moe_backward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, ids, wts, dy, g.router_bias,
-                             g.ws_gate_up, g.ws_down, bias_select=s.bias_select, workspace=ws)
+                             g.ws_gate_up, g.ws_down, bias_select=s.bias_select, workspace=ws,
+                             saved=saved)
 
     def step():
         moe.moe_backward(g.x, g.w_g, g.w_gate_up, g.w_down, s.k, ids, wts, dy, g.router_bias,
-                         g.ws_gate_up, g.ws_down, bias_select=s.bias_select, workspace=ws, grads=grads)
+                         g.ws_gate_up, g.ws_down, bias_select=s.bias_select, workspace=ws, grads=grads,
+                         saved=saved)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
+
+    timed(step, args.warmup)
+    elapsed = timed(step, args.steps)
     ms = elapsed / args.steps * 1e3
     _log("timed %d backward steps: %.3f ms/step" % (args.steps, ms))
+    forward_ms = {}
+    if args.saved:  # the price of keeping g | u: the two forwards, timed apart from the backward
+        y = torch.empty((s.T, s.D), dtype=torch.float32, device=dev)
+        fws = torch.empty(moe.train_workspace_size(shape), dtype=torch.uint8, device=dev)
+        common = (g.x, g.w_g, g.w_gate_up, g.w_down, s.k, g.router_bias, g.ws_gate_up, g.ws_down)
+        kw = dict(bias_select=s.bias_select, y=y, topk_ids=ids, topk_w=wts, workspace=fws)
+        for name, fn in (("forward", lambda: moe.moe_forward(*common, **kw)),
+                         ("forward_train", lambda: moe.moe_forward_train(*common, **kw))):
+            timed(fn, args.warmup)
+            forward_ms[name] = round(timed(fn, args.steps) / args.steps * 1e3, 4)
+        _log("forward %.3f ms, training forward %.3f ms" % (forward_ms["forward"],
+                                                            forward_ms["forward_train"]))
     # algorithmic work: dgrad and wgrad of the three expert products (6 each
     # per routed row and unit of D*F, likewise for the shared expert) and the
     # router's two products; the recomputation of g and u is not counted
@@ -118,13 +141,17 @@ def _bench_backward(args, s, wl, g, moe, torch, W, dev):
         "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded counter-based normal draws: x ~ N(0,1), weights ~ N(0,0.02), "
                 "dy ~ N(0,1), bf16 weights)",
-        "config": {"workload": wl.name, "pass": "backward", "T": s.T, "D": s.D, "E": s.E, "k": s.k,
+        "config": {"workload": wl.name, "pass": "backward (saved g|u)" if args.saved else "backward",
+                   "T": s.T, "D": s.D, "E": s.E, "k": s.k,
                    "d_ff": s.F, "shared_d_ff": s.Fs, "router_bias": bool(s.router_bias)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "moe_backward (whole call)", "traffic": None},
+                     "kernel": "moe_backward_saved (whole call)" if args.saved else
+                               "moe_backward (whole call)", "traffic": None},
         "cpu_baseline": None,
     }
+    if forward_ms:
+        out["forward_ms"] = forward_ms
     print(json.dumps(out), flush=True)
 
 
@@ -149,6 +176,8 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (moe_backward) for the routing of one forward "
                          "call instead of the forward pass")
+    ap.add_argument("--saved", action="store_true",
+                    help="with --backward: take the routing and g | u from moe_forward_train")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="run one plain device copy of this many GiB first (a known-size kernel "
                          "for calibrating rocprofv3 byte counters)")

@@ -281,6 +281,29 @@ int moe_backward(const moe_shape* shape, const moe_weights* w, const int32_t* to
                  const float* topk_w, const float* dy, const moe_grads* grads, void* workspace,
                  size_t ws_bytes, void* stream);
 
+/*
+ * Training forward: moe_forward (same results, bitwise) that also keeps, in
+ * its larger workspace, the grouping of the rows and g | u of every row
+ * (bf16), so that moe_backward_saved can skip recomputing them.
+ *   workspace  device buffer of ws_bytes >= moe_train_workspace_size(shape);
+ *              topk_ids and topk_w are required.
+ * Restrictions and errors as moe_backward's (bf16 weights, whole layer).
+ */
+int moe_train_workspace_size(const moe_shape* shape, size_t* bytes);
+int moe_forward_train(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
+                      float* topk_w, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_backward using the workspace of a moe_forward_train call with the same
+ * shape, weights, x and the routing it returned (train_workspace, untouched
+ * since): its grouping and g | u replace the backward's own.  The gradients
+ * equal moe_backward's up to g and u being bf16 here (fp32 there).
+ */
+int moe_backward_saved(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
+                       const float* topk_w, const float* dy, const moe_grads* grads,
+                       const void* train_workspace, size_t train_ws_bytes, void* workspace,
+                       size_t ws_bytes, void* stream);
+
 /* Static text for an error code (for MOE_ERR_HIP: the last HIP error seen by
  * this thread).  Never NULL. */
 const char* moe_strerror(int code);

@@ -11,11 +11,13 @@ from .binding import (MOE_ERR_ALIGNMENT, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_E
                       WEIGHTS_FP8_E4M3,
                       HipEvents, bias_mode, block_m, layer_shape, load_library, make_shape, moe_align, moe_block_m,
                       moe_backward, moe_backward_workspace_size, backward_workspace_size,
+                      moe_forward_train, moe_train_workspace_size, train_workspace_size,
                       moe_expert_load, moe_forward, moe_forward_routed, moe_forward_timed, moe_route,
                       moe_strerror, moe_workspace_size, strerror, workspace_size)
 
 __all__ = ["moe_forward", "moe_route", "moe_align", "moe_forward_routed", "moe_workspace_size",
            "moe_block_m", "moe_strerror", "moe_forward_timed", "moe_expert_load", "moe_backward",
-           "moe_backward_workspace_size", "HipEvents", "MoEError",
+           "moe_backward_workspace_size", "moe_forward_train", "moe_train_workspace_size",
+           "HipEvents", "MoEError",
            "make_shape", "layer_shape", "alloc_workspace", "load_library", "ROUTER_BIAS_NONE",
            "ROUTER_BIAS_LOGITS", "ROUTER_BIAS_SELECT", "WEIGHTS_BF16", "WEIGHTS_FP8_E4M3"]

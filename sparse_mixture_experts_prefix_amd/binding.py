@@ -25,7 +25,8 @@ MOE_ERR_HIP = -5
 
 EXPORTS = ("moe_workspace_size", "moe_block_m", "moe_forward", "moe_route", "moe_align",
            "moe_forward_routed", "moe_forward_timed", "moe_expert_load",
-           "moe_backward_workspace_size", "moe_backward", "moe_strerror")
+           "moe_backward_workspace_size", "moe_backward", "moe_train_workspace_size",
+           "moe_forward_train", "moe_backward_saved", "moe_strerror")
 
 
 class MoEError(RuntimeError):
@@ -84,6 +85,13 @@ def load_library(path: str = LIB_PATH):
                                                         ctypes.POINTER(ctypes.c_size_t)]
             lib.moe_backward.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P, P,
                                          ctypes.POINTER(Grads), P, ctypes.c_size_t, P]
+            lib.moe_train_workspace_size.argtypes = [ctypes.POINTER(Shape),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+            lib.moe_forward_train.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P,
+                                              P, P, ctypes.c_size_t, P]
+            lib.moe_backward_saved.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P,
+                                               P, ctypes.POINTER(Grads), P, ctypes.c_size_t, P,
+                                               ctypes.c_size_t, P]
             lib.moe_strerror.argtypes = [ctypes.c_int]
             lib.moe_strerror.restype = ctypes.c_char_p
             for name in EXPORTS[:-1]:
@@ -370,12 +378,47 @@ def backward_workspace_size(shape: Shape) -> int:
     return n.value
 
 
+def train_workspace_size(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_train_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def moe_forward_train(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None,
+                      ws_down=None, *, bias_select=False, y=None, topk_ids=None, topk_w=None,
+                      workspace=None):
+    """moe_forward that keeps the rows' grouping and g | u in its workspace for
+    moe_backward(..., saved=workspace).  Returns (y, topk_ids, topk_w, workspace)."""
+    T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
+    _dev(w_g, "w_g", torch.bfloat16, (E, D))
+    if router_bias is not None:
+        _dev(router_bias, "router_bias", torch.float32, (E,))
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, bias_mode(router_bias, bias_select))
+    dev = x.device
+    y = torch.empty((T, D), dtype=torch.float32, device=dev) if y is None else y
+    topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    _dev(y, "y", torch.float32, (T, D))
+    _dev(topk_ids, "topk_ids", torch.int32, (T, k))
+    _dev(topk_w, "topk_w", torch.float32, (T, k))
+    if workspace is None:
+        workspace = torch.empty(max(train_workspace_size(shape), 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
+    _check(load_library().moe_forward_train(ctypes.byref(shape), ctypes.byref(w), _ptr(y),
+                                            _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
+                                            workspace.numel(), _stream(dev)))
+    return y, topk_ids, topk_w, workspace
+
+
 def moe_backward(x, w_g, w_gate_up, w_down, k, topk_ids, topk_w, dy, router_bias=None,
-                 ws_gate_up=None, ws_down=None, *, bias_select=False, workspace=None, grads=None):
+                 ws_gate_up=None, ws_down=None, *, bias_select=False, workspace=None, grads=None,
+                 saved=None):
     """Gradients of sum <dy, y> for the routing (topk_ids, topk_w) of a forward
     call with the same tensors.  Returns a dict of fp32 tensors dx, dw_g,
     d_bias, dw_gate_up, dw_down (and dws_gate_up, dws_down with a shared
-    expert); ``grads`` may hold preallocated ones."""
+    expert); ``grads`` may hold preallocated ones.  ``saved``: the workspace of
+    the moe_forward_train call that returned this routing (moe_backward_saved)."""
     T, D, E, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down)
     _dev(w_g, "w_g", torch.bfloat16, (E, D))
     _dev(topk_ids, "topk_ids", torch.int32, (T, k))
@@ -399,15 +442,24 @@ def moe_backward(x, w_g, w_gate_up, w_down, k, topk_ids, topk_w, dy, router_bias
     _dev(workspace, "workspace", torch.uint8)
     gr = Grads(*[_ptr(out.get(n)) for n, _ in Grads._fields_])
     w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down)
-    _check(load_library().moe_backward(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids),
-                                       _ptr(topk_w), _ptr(dy), ctypes.byref(gr), _ptr(workspace),
-                                       workspace.numel(), _stream(dev)))
+    lib = load_library()
+    if saved is None:
+        _check(lib.moe_backward(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids), _ptr(topk_w),
+                                _ptr(dy), ctypes.byref(gr), _ptr(workspace), workspace.numel(),
+                                _stream(dev)))
+    else:
+        _dev(saved, "saved", torch.uint8)
+        _check(lib.moe_backward_saved(ctypes.byref(shape), ctypes.byref(w), _ptr(topk_ids),
+                                      _ptr(topk_w), _ptr(dy), ctypes.byref(gr), _ptr(saved),
+                                      saved.numel(), _ptr(workspace), workspace.numel(),
+                                      _stream(dev)))
     return out
 
 
 # the C names, one to one
 moe_workspace_size = workspace_size
 moe_backward_workspace_size = backward_workspace_size
+moe_train_workspace_size = train_workspace_size
 moe_block_m = block_m
 moe_strerror = strerror
 

@@ -62,9 +62,10 @@ int64_t busy_tiles(const moe::Plan& P) {
 }
 
 // Everything after routing: align -> gate/up -> down -> combine.
+// gu_save (or NULL): keep g | u of every row, bf16 [cap][2 ldh] (training forward)
 int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, const float* wts,
                 float* y, void* ws, hipStream_t s, Marks mk = Marks{nullptr},
-                const moe::RouteFinish* fin = nullptr) {
+                const moe::RouteFinish* fin = nullptr, uint16_t* gu_save = nullptr) {
   using namespace moe;
   int32_t* counts = at<int32_t>(ws, P.off_counts);
   int32_t* offsets = at<int32_t>(ws, P.off_offsets);
@@ -116,11 +117,14 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   gu.a_bytes = P.T * P.D * 2;
   gu.ctas = ctas;
   gu.partial = prefill ? at<float>(ws, P.off_partial) : nullptr;
+  gu.gu_out = gu_save;
+  gu.ld_gu = 2 * P.ldh;
   e = P.BM == 256 ? launch_gemm_gate_up_prefill(gu, s) : launch_gemm_gate_up_decode(gu, s);
   if (e == hipSuccess) e = mk.mark(3, s);
   if (e != hipSuccess) return hip_fail(e);
 
   GroupedGemm dn = gu;
+  dn.gu_out = nullptr;
   dn.A = H;
   dn.row_token = nullptr;
   dn.lda = P.ldh;
@@ -147,19 +151,23 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
 }
 
 // Backward pass for a given routing (see moe_backward in moe.h).
+// saved (or NULL): the workspace of a training forward call with the same
+// shape and routing: its grouping and its g | u are used instead of redoing them.
 int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weights* w,
                  const int32_t* ids, const float* wts, const float* dy, const moe_grads* gr,
-                 void* ws, hipStream_t s) {
+                 void* ws, hipStream_t s, const void* saved = nullptr) {
   using namespace moe;
   const Plan& P = B.P;
-  int32_t* counts = at<int32_t>(ws, P.off_counts);
-  int32_t* offsets = at<int32_t>(ws, P.off_offsets);
-  int32_t* padded = at<int32_t>(ws, P.off_padded);
-  int32_t* n_tiles = at<int32_t>(ws, P.off_ntiles);
-  int32_t* sorted = at<int32_t>(ws, P.off_sorted);
-  int32_t* row_of = at<int32_t>(ws, P.off_rowof);
-  int32_t* row_token = at<int32_t>(ws, P.off_rowtoken);
-  int32_t* tile_group = at<int32_t>(ws, P.off_tilegroup);
+  // the grouping: the saved forward's (read only) or this call's own
+  void* grp = saved ? const_cast<void*>(saved) : ws;
+  int32_t* counts = at<int32_t>(grp, P.off_counts);
+  int32_t* offsets = at<int32_t>(grp, P.off_offsets);
+  int32_t* padded = at<int32_t>(grp, P.off_padded);
+  int32_t* n_tiles = at<int32_t>(grp, P.off_ntiles);
+  int32_t* sorted = at<int32_t>(grp, P.off_sorted);
+  int32_t* row_of = at<int32_t>(grp, P.off_rowof);
+  int32_t* row_token = at<int32_t>(grp, P.off_rowtoken);
+  int32_t* tile_group = at<int32_t>(grp, P.off_tilegroup);
   int32_t* row_assign = at<int32_t>(ws, B.off_rowa);
   uint16_t* xr = at<uint16_t>(ws, B.off_xr);
   uint16_t* dyr = at<uint16_t>(ws, B.off_dyr);
@@ -183,8 +191,10 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
     hipError_t e0 = split_ctas(&ctas);
     if (e0 != hipSuccess) return hip_fail(e0);
   }
-  hipError_t e = launch_align(ids, T, k, E, 0, P.BM, Fs > 0 ? T : 0, counts, offsets, padded, sorted,
-                              row_of, row_token, tile_group, n_tiles, nullptr, s);
+  hipError_t e = hipSuccess;
+  if (!saved)
+    e = launch_align(ids, T, k, E, 0, P.BM, Fs > 0 ? T : 0, counts, offsets, padded, sorted, row_of,
+                     row_token, tile_group, n_tiles, nullptr, s);
   if (e == hipSuccess) e = launch_row_assign(row_of, (int)P.A, cap, row_assign, s);
   const int32_t* total = padded + G;  // rows in use
   if (e == hipSuccess) e = launch_gather_rows(w->x, false, row_token, total, cap, D, xr, s);
@@ -230,11 +240,12 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
     q.ldc = ldc;
     return prefill ? launch_gemm_down_prefill(q, s) : launch_gemm_down_decode(q, s);
   };
-  // g | u again, then dh' = W_down^T dy
-  e = gemm(xr, D, w->w_gate_up, w->ws_gate_up, 2 * F, 2 * Fs, D, D, gu, 2 * ldh);
+  // g | u (kept by the training forward, or computed again), then dh' = W_down^T dy
+  const uint16_t* gu16 = saved ? at<const uint16_t>(grp, P.off_gusave) : nullptr;
+  if (!saved) e = gemm(xr, D, w->w_gate_up, w->ws_gate_up, 2 * F, 2 * Fs, D, D, gu, 2 * ldh);
   if (e == hipSuccess) e = gemm(dyr, D, wdt, wdts, F, Fs, D, D, dhp, ldh);
   BwdRows rows{cap, B.ldt, total, row_token, row_assign, padded, tile_group, wts, dy, E, P.BM, D, F, Fs,
-               ldh, gu, dgu, dgu, xr};
+               ldh, saved ? nullptr : gu, gu16, dgu, dgu, xr};
   if (e == hipSuccess) e = launch_swiglu_bwd(rows, dhp, dp, s);
   if (e == hipSuccess) e = launch_router_bwd(wts, dp, T, k, dl, s);
   // per-row dx = [dg du] W_gate_up, then dx
@@ -289,7 +300,7 @@ int moe_block_m(const moe_shape* shape) {
 
 static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
                         float* topk_w, void* workspace, size_t ws_bytes, void* stream,
-                        void* const* events) {
+                        void* const* events, bool train = false) {
   moe::Plan P;
   int rc = moe::make_plan(shape, &P);
   if (rc) return rc;
@@ -300,7 +311,8 @@ static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, 
   if (!moe::aligned16(y) || !moe::aligned16(workspace)) return MOE_ERR_ALIGNMENT;
   if ((topk_ids && !moe::aligned16(topk_ids)) || (topk_w && !moe::aligned16(topk_w)))
     return MOE_ERR_ALIGNMENT;
-  if (ws_bytes < P.total) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < (train ? P.total_train : P.total)) return MOE_ERR_WORKSPACE;
+  uint16_t* gu_save = train ? at<uint16_t>(workspace, P.off_gusave) : nullptr;
   if (events)
     for (int i = 0; i < 6; ++i)
       if (!events[i]) return MOE_ERR_INVALID_ARG;
@@ -321,14 +333,14 @@ static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, 
     if (e == hipSuccess) e = mk.mark(1, s);
     if (e != hipSuccess) return hip_fail(e);
     const moe::RouteFinish fin{rpart, moe::router_parts(P.D), (int)P.E, bias, sel, ids, wts};
-    return run_experts(P, w, ids, wts, y, workspace, s, mk, &fin);
+    return run_experts(P, w, ids, wts, y, workspace, s, mk, &fin, gu_save);
   }
   if (e == hipSuccess)
     e = moe::launch_router(static_cast<const uint16_t*>(w->x), static_cast<const uint16_t*>(w->w_g),
                            bias, sel, (int)P.T, (int)P.D, (int)P.E, (int)P.k, ids, wts, s);
   if (e == hipSuccess) e = mk.mark(1, s);
   if (e != hipSuccess) return hip_fail(e);
-  return run_experts(P, w, ids, wts, y, workspace, s, mk);
+  return run_experts(P, w, ids, wts, y, workspace, s, mk, nullptr, gu_save);
 }
 
 int moe_forward(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
@@ -429,9 +441,28 @@ int moe_backward_workspace_size(const moe_shape* shape, size_t* bytes) {
   return MOE_OK;
 }
 
-int moe_backward(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
-                 const float* topk_w, const float* dy, const moe_grads* grads, void* workspace,
-                 size_t ws_bytes, void* stream) {
+int moe_train_workspace_size(const moe_shape* shape, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe::BwdPlan B;  // a training forward is only useful where the backward pass runs
+  int rc = moe::make_backward_plan(shape, &B);
+  if (rc) return rc;
+  *bytes = B.P.total_train;
+  return MOE_OK;
+}
+
+int moe_forward_train(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
+                      float* topk_w, void* workspace, size_t ws_bytes, void* stream) {
+  moe::BwdPlan B;
+  int rc = moe::make_backward_plan(shape, &B);
+  if (rc) return rc;
+  if (shape->T > 0 && (!topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
+  return forward_impl(shape, w, y, topk_ids, topk_w, workspace, ws_bytes, stream, nullptr, true);
+}
+
+static int backward_impl(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
+                         const float* topk_w, const float* dy, const moe_grads* grads,
+                         const void* saved, size_t saved_bytes, void* workspace, size_t ws_bytes,
+                         void* stream) {
   moe::BwdPlan B;
   int rc = moe::make_backward_plan(shape, &B);
   if (rc) return rc;
@@ -460,7 +491,27 @@ int moe_backward(const moe_shape* shape, const moe_weights* w, const int32_t* to
       !moe::aligned16(workspace))
     return MOE_ERR_ALIGNMENT;
   if (ws_bytes < B.total) return MOE_ERR_WORKSPACE;
-  return run_backward(B, shape, w, topk_ids, topk_w, dy, grads, workspace, s);
+  if (saved) {
+    if (!moe::aligned16(saved)) return MOE_ERR_ALIGNMENT;
+    if (saved_bytes < P.total_train) return MOE_ERR_WORKSPACE;
+  }
+  return run_backward(B, shape, w, topk_ids, topk_w, dy, grads, workspace, s, saved);
+}
+
+int moe_backward(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
+                 const float* topk_w, const float* dy, const moe_grads* grads, void* workspace,
+                 size_t ws_bytes, void* stream) {
+  return backward_impl(shape, w, topk_ids, topk_w, dy, grads, nullptr, 0, workspace, ws_bytes,
+                       stream);
+}
+
+int moe_backward_saved(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
+                       const float* topk_w, const float* dy, const moe_grads* grads,
+                       const void* train_workspace, size_t train_ws_bytes, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  if (!train_workspace && shape && shape->T > 0) return MOE_ERR_INVALID_ARG;
+  return backward_impl(shape, w, topk_ids, topk_w, dy, grads, train_workspace, train_ws_bytes,
+                       workspace, ws_bytes, stream);
 }
 
 const char* moe_strerror(int code) {

@@ -111,9 +111,27 @@ struct RowSource {
   const int32_t* padded;      // group offsets; padded[E] is the first shared row
   const int32_t* tile_group;
   int E, BM, D, F, Fs, ldh;
-  const float* gu;            // [rows][2 ldh]
+  const float* gu;            // [rows][2 ldh], fp32 ...
+  const bf16_t* gu16;         // ... or bf16 (kept by a training forward)
   const bf16_t* rows16;       // [rows][cols] (kind 2: stride 2 ldh; kind 3: stride D)
 };
+
+// eight consecutive values of a g | u row, fp32 or bf16
+__device__ __forceinline__ void load8(const float* f32, const bf16_t* b16, int64_t i, float (&v)[8]) {
+  if (b16) {
+    const u32x4 w = ld16(b16 + i);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[2 * u] = bf16_to_f32((bf16_t)(w[u] & 0xffff));
+      v[2 * u + 1] = bf16_to_f32((bf16_t)(w[u] >> 16));
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(f32 + i);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
 
 // columns c .. c + 7 (c % 8 == 0) of row r, as bf16
 __device__ __forceinline__ u32x4 row_values8(const RowSource& q, int64_t r, int c) {
@@ -134,11 +152,9 @@ __device__ __forceinline__ u32x4 row_values8(const RowSource& q, int64_t r, int 
     case 1: {
       const int Fg = q.tile_group[r / q.BM] >= q.E ? q.Fs : q.F;
       if (c >= Fg) return u32x4{0, 0, 0, 0};  // Fg % 8 == 0: a chunk is all in or all out
-      const float4* gp = reinterpret_cast<const float4*>(q.gu + r * 2 * q.ldh + c);
-      const float4* up = reinterpret_cast<const float4*>(q.gu + r * 2 * q.ldh + Fg + c);
-      const float4 g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
-      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-      const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      float g[8], u[8];
+      load8(q.gu, q.gu16, r * 2 * q.ldh + c, g);
+      load8(q.gu, q.gu16, r * 2 * q.ldh + Fg + c, u);
 #pragma unroll
       for (int w = 0; w < 8; ++w) e[w] = f32_to_bf16(silu(g[w]) * u[w]);
       return pack8(e);
@@ -174,7 +190,8 @@ __global__ __launch_bounds__(256) void moe_rows_transpose_kernel(RowSource q, co
 // dGU[r] = [dg | du] (bf16; zeros past 2 Fg and on padding rows), dp per
 // assignment.  The wave's sum over f is a fixed shuffle tree.
 __global__ __launch_bounds__(256) void moe_swiglu_bwd_kernel(
-    const float* __restrict__ gu, const float* __restrict__ dhp, const int32_t* __restrict__ row_token,
+    const float* __restrict__ gu, const bf16_t* __restrict__ gu16, const float* __restrict__ dhp,
+    const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ row_assign, const int32_t* __restrict__ tile_group,
     const float* __restrict__ topk_w, const int32_t* __restrict__ total, int E, int BM, int F, int Fs,
     int ldh, bf16_t* __restrict__ dgu, float* __restrict__ dp) {
@@ -186,14 +203,15 @@ __global__ __launch_bounds__(256) void moe_swiglu_bwd_kernel(
   const int a = row_assign[r];
   const bool valid = row_token[r] >= 0;
   const float p = shared ? 1.f : (a >= 0 ? topk_w[a] : 0.f);
-  const float* gr = gu + r * 2 * ldh;
+  const int64_t gbase = r * 2 * ldh;  // g at gbase + f, u at gbase + Fg + f
   const float* hr = dhp + r * ldh;
   bf16_t* out = dgu + r * 2 * ldh;
   float acc = 0.f;
   for (int f = lane; f < ldh; f += 64) {
     float dg = 0.f, du = 0.f;
     if (valid && f < Fg) {
-      const float g = gr[f], u = gr[Fg + f];
+      const float g = gu16 ? bf16_to_f32(gu16[gbase + f]) : gu[gbase + f];
+      const float u = gu16 ? bf16_to_f32(gu16[gbase + Fg + f]) : gu[gbase + Fg + f];
       const float s = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
       const float sl = g * s;
       const float h = bf16_to_f32(f32_to_bf16(sl * u));
@@ -313,7 +331,7 @@ hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, in
 hipError_t launch_rows_transpose(const BwdRows& b, int kind, int C, uint16_t* dst, hipStream_t s) {
   if (b.cap <= 0 || C <= 0) return hipSuccess;
   RowSource q{kind, b.dy, b.topk_w, b.row_token, b.row_assign, b.padded, b.tile_group, b.E, b.BM,
-              b.D, b.F, b.Fs, b.ldh, b.gu, kind == 2 ? b.dgu : b.xr};
+              b.D, b.F, b.Fs, b.ldh, b.gu, b.gu16, kind == 2 ? b.dgu : b.xr};
   hipLaunchKernelGGL(moe_rows_transpose_kernel, dim3((unsigned)((b.cap + 63) / 64), (C + 63) / 64),
                      dim3(256), 0, s, q, b.total, C, b.ldt, dst);
   return hipGetLastError();
@@ -322,7 +340,7 @@ hipError_t launch_rows_transpose(const BwdRows& b, int kind, int C, uint16_t* ds
 hipError_t launch_swiglu_bwd(const BwdRows& b, const float* dhp, float* dp, hipStream_t s) {
   if (b.cap <= 0) return hipSuccess;
   hipLaunchKernelGGL(moe_swiglu_bwd_kernel, dim3((unsigned)((b.cap + 3) / 4)), dim3(256), 0, s, b.gu,
-                     dhp, b.row_token, b.row_assign, b.tile_group, b.topk_w, b.total, b.E, b.BM, b.F,
+                     b.gu16, dhp, b.row_token, b.row_assign, b.tile_group, b.topk_w, b.total, b.E, b.BM, b.F,
                      b.Fs, b.ldh, b.dgu_w, dp);
   return hipGetLastError();
 }

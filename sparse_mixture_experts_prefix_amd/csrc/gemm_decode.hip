@@ -267,6 +267,17 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
           const int f = n0 + j * 16 + c;
           if (f < N) H[grow * p.ldc + f] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + NG / 2][r]);
         }
+        if (p.gu_out && i * 16 + 4 * gq + r < valid_rows) {  // g and u kept for the backward pass
+          bf16_t* gr = reinterpret_cast<bf16_t*>(p.gu_out) + grow * p.ld_gu;
+#pragma unroll
+          for (int j = 0; j < NG / 2; ++j) {
+            const int f = n0 + j * 16 + c;
+            if (f < N) {
+              gr[f] = f32_to_bf16(acc[i][j][r]);
+              gr[N + f] = f32_to_bf16(acc[i][j + NG / 2][r]);
+            }
+          }
+        }
       } else {
         float* Y = reinterpret_cast<float*>(p.C);
 #pragma unroll

@@ -449,6 +449,26 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   }
 
   // -------------------------------------------------------------- epilogue
+  if (GATE_UP && p.gu_out) {  // keep g and u (bf16) of the valid rows for the backward pass
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= act) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
+        if (row >= valid_rows) continue;
+        bf16_t* gr = reinterpret_cast<bf16_t*>(p.gu_out) + (row0 + row) * p.ld_gu;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = n0 + wn * 64 + j * 32 + lr;
+          if (f < N) {
+            gr[f] = f32_to_bf16(acc[i][j][r]);
+            gr[N + f] = f32_to_bf16(acc[i][j + 2][r]);
+          }
+        }
+      }
+    }
+  }
   if (GATE_UP) {
     // SwiGLU in registers; the 256 x 128 fp32 result goes through the (now
     // idle) LDS so that each lane writes 16 bytes of H at a time, and padding
@@ -566,6 +586,16 @@ __global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (n0 + c + u < N) H[u] = f32_to_bf16(h[u]);
+      if (p.gu_out) {  // g and u kept for the backward pass
+        const float g4[4] = {gt.x, gt.y, gt.z, gt.w}, u4[4] = {up.x, up.y, up.z, up.w};
+        bf16_t* gr = reinterpret_cast<bf16_t*>(p.gu_out) + (row0 + row) * p.ld_gu;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (n0 + c + u < N) {
+            gr[n0 + c + u] = f32_to_bf16(g4[u]);
+            gr[N + n0 + c + u] = f32_to_bf16(u4[u]);
+          }
+      }
     } else {
       const float4 v = sum4(row, c);
       float* Y = reinterpret_cast<float*>(p.C) + (row0 + row) * p.ldc + n0 + c;

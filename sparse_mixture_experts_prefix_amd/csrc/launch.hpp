@@ -68,6 +68,10 @@ struct GroupedGemm {
   // and room for that many fp32 partial tiles of BM x BN (row-major)
   int ctas;
   float* partial;
+  // Gate/up only: when set, g and u of every valid row are also stored, bf16,
+  // row r at gu_out + r * ld_gu as [g (N) | u (N)] (kept for the backward pass)
+  uint16_t* gu_out;
+  int64_t ld_gu;
 };
 
 // 256 x 256 x 64 tiles for BM = 256 (prefill-sized groups); each launches
@@ -110,7 +114,8 @@ struct BwdRows {
   const float* topk_w;         // [T k]
   const float* dy;             // [T][D]
   int E, BM, D, F, Fs, ldh;
-  const float* gu;             // [cap][2 ldh]
+  const float* gu;             // [cap][2 ldh] (recomputed), or NULL when gu16 is set
+  const uint16_t* gu16;        // [cap][2 ldh] bf16, kept by a training forward
   const uint16_t* dgu;         // [cap][2 ldh]
   uint16_t* dgu_w;             // the same buffer, written by the SwiGLU backward
   const uint16_t* xr;          // [cap][D]

@@ -95,6 +95,8 @@ int make_plan(const moe_shape* s, Plan* p) {
                           ? sizeof(float) * router_parts(p->D) * p->T * p->E
                           : 0);
   p->total = o;
+  p->off_gusave = take(sizeof(uint16_t) * (size_t)p->cap_rows * 2 * p->ldh);
+  p->total_train = o;
   return MOE_OK;
 }
 

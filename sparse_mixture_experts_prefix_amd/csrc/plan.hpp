@@ -36,6 +36,8 @@ struct Plan {
   // byte offsets inside the workspace
   size_t off_ids, off_w, off_counts, off_offsets, off_padded, off_ntiles, off_sorted, off_rowof,
       off_rowtoken, off_tilegroup, off_h, off_yp, off_partial, off_rpart, total;
+  // training forward: the same layout, then g | u of every row (bf16 [cap][2 ldh])
+  size_t off_gusave, total_train;
 };
 
 // Backward-pass workspace: the forward's layout (align outputs, split

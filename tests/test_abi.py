@@ -256,3 +256,35 @@ def test_backward_errors(lib):
     s2 = _shape(F_shared=64)
     size(ctypes.byref(s2), ctypes.byref(n))
     assert bwd(shape=s2, w=_weights(ws_gate_up=FAKE, ws_down=FAKE), nb=n.value) == B.MOE_ERR_INVALID_ARG
+
+
+def test_train_entry_point_errors(lib):
+    n, nt = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    s = _shape()
+    assert lib.moe_workspace_size(ctypes.byref(s), ctypes.byref(n)) == B.MOE_OK
+    assert lib.moe_train_workspace_size(ctypes.byref(s), ctypes.byref(nt)) == B.MOE_OK
+    assert nt.value > n.value  # the forward's workspace plus g | u of every row
+    assert lib.moe_train_workspace_size(ctypes.byref(s), None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_train_workspace_size(ctypes.byref(_shape(weight_format=1)),
+                                        ctypes.byref(nt)) == B.MOE_ERR_UNSUPPORTED
+    lib.moe_train_workspace_size(ctypes.byref(s), ctypes.byref(nt))
+
+    def fwd(shape=s, ids=FAKE, wts=FAKE, ws=FAKE, nb=nt.value):
+        return lib.moe_forward_train(ctypes.byref(shape), ctypes.byref(_weights()), FAKE, ids, wts,
+                                     ws, nb, None)
+
+    assert fwd(ids=None) == B.MOE_ERR_INVALID_ARG  # the routing is needed by the backward
+    assert fwd(wts=None) == B.MOE_ERR_INVALID_ARG
+    assert fwd(nb=nt.value - 1) == B.MOE_ERR_WORKSPACE  # the plain forward's size is too small
+    assert fwd(shape=_shape(expert_begin=2, num_local_experts=4)) == B.MOE_ERR_UNSUPPORTED
+    nb = ctypes.c_size_t(0)
+    lib.moe_backward_workspace_size(ctypes.byref(s), ctypes.byref(nb))
+    g = B.Grads(FAKE, FAKE, None, FAKE, FAKE, None, None)
+
+    def bwd(saved=FAKE, saved_bytes=nt.value):
+        return lib.moe_backward_saved(ctypes.byref(s), ctypes.byref(_weights()), FAKE, FAKE, FAKE,
+                                      ctypes.byref(g), saved, saved_bytes, FAKE, nb.value, None)
+
+    assert bwd(saved=None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(saved_bytes=nt.value - 1) == B.MOE_ERR_WORKSPACE
+    assert bwd(saved=FAKE + 8) == B.MOE_ERR_ALIGNMENT
