@@ -201,13 +201,18 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   if (e == hipSuccess) e = launch_gather_rows(dy, true, row_token, total, cap, D, dyr, s);
   const uint16_t* wgu = static_cast<const uint16_t*>(w->w_gate_up);
   const uint16_t* wdn = static_cast<const uint16_t*>(w->w_down);
-  if (e == hipSuccess) e = launch_transpose(wdn, wdt, E, D, F, s);
-  if (e == hipSuccess) e = launch_transpose(wgu, wgut, E, 2 * F, D, s);
-  if (Fs > 0) {
-    if (e == hipSuccess)
-      e = launch_transpose(static_cast<const uint16_t*>(w->ws_down), wdts, 1, D, Fs, s);
-    if (e == hipSuccess)
-      e = launch_transpose(static_cast<const uint16_t*>(w->ws_gate_up), wguts, 1, 2 * Fs, D, s);
+  // The 256-row tiles read W_down and W_gate_up K-major, as stored; the
+  // decode-sized tiles take transposed copies.
+  const bool kmajor = prefill;
+  if (!kmajor) {
+    if (e == hipSuccess) e = launch_transpose(wdn, wdt, E, D, F, s);
+    if (e == hipSuccess) e = launch_transpose(wgu, wgut, E, 2 * F, D, s);
+    if (Fs > 0) {
+      if (e == hipSuccess)
+        e = launch_transpose(static_cast<const uint16_t*>(w->ws_down), wdts, 1, D, Fs, s);
+      if (e == hipSuccess)
+        e = launch_transpose(static_cast<const uint16_t*>(w->ws_gate_up), wguts, 1, 2 * Fs, D, s);
+    }
   }
   if (e != hipSuccess) return hip_fail(e);
 
@@ -225,8 +230,9 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   g.ctas = ctas;
   g.partial = prefill ? at<float>(ws, P.off_partial) : nullptr;
   auto gemm = [&](const uint16_t* A, int64_t lda, const void* Br, const void* Bs, int Nr, int Ns,
-                  int Kr, int Ks, float* C, int64_t ldc) {
+                  int Kr, int Ks, float* C, int64_t ldc, bool bk = false) {
     GroupedGemm q = g;
+    q.b_kmajor = bk ? 1 : 0;
     q.A = A;
     q.lda = lda;
     q.a_bytes = cap * lda * 2;
@@ -243,13 +249,17 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   // g | u (kept by the training forward, or computed again), then dh' = W_down^T dy
   const uint16_t* gu16 = saved ? at<const uint16_t>(grp, P.off_gusave) : nullptr;
   if (!saved) e = gemm(xr, D, w->w_gate_up, w->ws_gate_up, 2 * F, 2 * Fs, D, D, gu, 2 * ldh);
-  if (e == hipSuccess) e = gemm(dyr, D, wdt, wdts, F, Fs, D, D, dhp, ldh);
+  if (e == hipSuccess)
+    e = kmajor ? gemm(dyr, D, w->w_down, w->ws_down, F, Fs, D, D, dhp, ldh, true)
+               : gemm(dyr, D, wdt, wdts, F, Fs, D, D, dhp, ldh);
   BwdRows rows{cap, B.ldt, total, row_token, row_assign, padded, tile_group, wts, dy, E, P.BM, D, F, Fs,
                ldh, saved ? nullptr : gu, gu16, dgu, dgu, xr};
   if (e == hipSuccess) e = launch_swiglu_bwd(rows, dhp, dp, s);
   if (e == hipSuccess) e = launch_router_bwd(wts, dp, T, k, dl, s);
   // per-row dx = [dg du] W_gate_up, then dx
-  if (e == hipSuccess) e = gemm(dgu, 2 * ldh, wgut, wguts, D, D, 2 * F, 2 * Fs, dxr, D);
+  if (e == hipSuccess)
+    e = kmajor ? gemm(dgu, 2 * ldh, w->w_gate_up, w->ws_gate_up, D, D, 2 * F, 2 * Fs, dxr, D, true)
+               : gemm(dgu, 2 * ldh, wgut, wguts, D, D, 2 * F, 2 * Fs, dxr, D);
   if (e == hipSuccess)
     e = launch_combine_bwd(dxr, row_of, ids, dl, static_cast<const uint16_t*>(w->w_g), padded, T, D, k,
                            E, Fs > 0 ? 1 : 0, gr->dx, s);

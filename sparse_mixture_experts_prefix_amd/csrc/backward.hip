@@ -188,7 +188,8 @@ __global__ __launch_bounds__(256) void moe_rows_transpose_kernel(RowSource q, co
 //   dp = sum_f dh'_f h_f (h rounded to bf16, as the forward stores it),
 //   dh = p dh',  dg = dh u SiLU'(g),  du = dh SiLU(g);
 // dGU[r] = [dg | du] (bf16; zeros past 2 Fg and on padding rows), dp per
-// assignment.  The wave's sum over f is a fixed shuffle tree.
+// assignment.  Each lane sums its columns in order, then the wave's lanes are
+// added by a fixed shuffle tree.
 __global__ __launch_bounds__(256) void moe_swiglu_bwd_kernel(
     const float* __restrict__ gu, const bf16_t* __restrict__ gu16, const float* __restrict__ dhp,
     const int32_t* __restrict__ row_token,
@@ -207,26 +208,37 @@ __global__ __launch_bounds__(256) void moe_swiglu_bwd_kernel(
   const float* hr = dhp + r * ldh;
   bf16_t* out = dgu + r * 2 * ldh;
   float acc = 0.f;
-  for (int f = lane; f < ldh; f += 64) {
-    float dg = 0.f, du = 0.f;
-    if (valid && f < Fg) {
-      const float g = gu16 ? bf16_to_f32(gu16[gbase + f]) : gu[gbase + f];
-      const float u = gu16 ? bf16_to_f32(gu16[gbase + Fg + f]) : gu[gbase + Fg + f];
-      const float s = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
-      const float sl = g * s;
-      const float h = bf16_to_f32(f32_to_bf16(sl * u));
-      const float d1 = hr[f];
-      acc += d1 * h;
-      const float dh = p * d1;
-      dg = dh * u * s * (1.f + g * (1.f - s));
-      du = dh * sl;
-    }
+  // eight consecutive columns per lane and step (F, Fs and ldh are multiples
+  // of 8, so a chunk is all inside or all outside [0, Fg))
+  for (int f = 8 * lane; f < ldh; f += 8 * 64) {
+    bf16_t eg[8], eu[8];
     if (f < Fg) {
-      out[f] = f32_to_bf16(dg);
-      out[Fg + f] = f32_to_bf16(du);
-    } else {
-      out[Fg + f] = (bf16_t)0;  // columns 2 Fg .. 2 ldh - 1 (reached when Fg < ldh)
-      out[f + ldh] = (bf16_t)0;
+      if (valid) {
+        float g[8], u[8];
+        load8(gu, gu16, gbase + f, g);
+        load8(gu, gu16, gbase + Fg + f, u);
+        const float4 d0 = *reinterpret_cast<const float4*>(hr + f);
+        const float4 d4 = *reinterpret_cast<const float4*>(hr + f + 4);
+        const float d1[8] = {d0.x, d0.y, d0.z, d0.w, d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const float s = 1.f / (1.f + __builtin_amdgcn_exp2f(-g[w] * 1.4426950408889634f));
+          const float sl = g[w] * s;
+          const float h = bf16_to_f32(f32_to_bf16(sl * u[w]));
+          acc += d1[w] * h;
+          const float dh = p * d1[w];
+          eg[w] = f32_to_bf16(dh * u[w] * s * (1.f + g[w] * (1.f - s)));
+          eu[w] = f32_to_bf16(dh * sl);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) eg[w] = eu[w] = 0;
+      }
+      st16(out + f, pack8(eg));
+      st16(out + Fg + f, pack8(eu));
+    } else {  // columns 2 Fg .. 2 ldh - 1 (reached when Fg < ldh)
+      st16(out + Fg + f, u32x4{0, 0, 0, 0});
+      st16(out + f + ldh, u32x4{0, 0, 0, 0});
     }
   }
 #pragma unroll

@@ -76,6 +76,32 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// One 16-byte-per-lane buffer load into LDS (lane i writes bytes 16 i ..
+// 16 i + 15 of the 1-KB block at `dst`), written out for the kernels that
+// read B with the transposing LDS read: the compiler makes such a read wait
+// for every LDS load it knows to be in flight (vmcnt(0), which would drain
+// the prefetch of the coming stages), while the K loop's own waits and
+// barriers already order these loads before the reads of their stage.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const char* dst, uint32_t voff,
+                                          uint32_t soff) {
+  // M0 (the LDS base of the load) is saved and restored around it
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)dst;  // low bits of the generic pointer
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");
+}
+
+// K-major B stage: 64 k-rows of 512 B (256 columns).  16-byte chunk c of
+// k-row k is stored at chunk position c ^ (4 (k % 4)): the transposing reads of
+// a 32-lane half (4 k-rows x 4 chunks) then hit 16 distinct chunk positions
+// mod 16, i.e. all 64 banks once.
+__device__ __forceinline__ int kmaj_chunk(int k, int c) { return c ^ (4 * (k & 3)); }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
 // First LDS row of B sub-tile j of wave column wn.
 template <bool GATE_UP>
 __device__ __forceinline__ int b_row_of(int wn, int j) {
@@ -99,9 +125,10 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 // Stages s0 .. s0+n-1 (n >= 1); ACT = active 32-row A sub-tiles of this wave.
 // E4M3 B: four loads per wave and stage instead of eight, so B(i+3) takes
 // two per substep and the barrier waits with vmcnt(4).
-template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB>
+template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB, bool KMAJ = false>
 __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, int lane,
                                        IssueA& issue_a, IssueB& issue_b, f32x16 (&acc)[4][4]) {
+  static_assert(!KMAJ || (!GATE_UP && !FP8), "K-major B: bf16 rows x weight products only");
   constexpr int NBL = FP8 ? 4 : 8;  // B loads per wave and stage
   const int lr = lane & 31, kh = lane >> 5;
   // LDS byte offset of this lane's A chunk inside a 32-row block, per k-substep.
@@ -117,6 +144,23 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
   int rd8[2];  // E4M3 B: byte offset of chunk 2m + kh inside a 32-row block
 #pragma unroll
   for (int m = 0; m < 2; ++m) rd8[m] = lr * 64 + ((2 * m + kh) ^ swz4(lr)) * 16;
+  // K-major B (a stage is 64 k-rows of 512 B; see kmaj_chunk): a transposing
+  // 8-byte read gives lane i of each 16-lane group element (i % 4) of the
+  // word that lane (i / 4) + 4 j of the group points at, as its element j.
+  // So group lane q points at k-row 4 t + q / 4 (t: which half of the lane's
+  // eight k) and columns 4 (q % 4) .. + 3 of its 16; the four words of a
+  // lane's column then arrive as k, k + 1, k + 2, k + 3.
+  int rdk[4];
+  {
+    const int q = lane & 15, g16 = (lane >> 4) & 1;
+    const int k = 8 * kh + (q >> 2);                     // k-row of this lane's word
+    const int col = 16 * g16 + 4 * (q & 3);               // first column, inside a 32-wide sub-tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = b_row_of<false>(wn, j) + col;         // column in the 256-wide tile
+      rdk[j] = k * 512 + kmaj_chunk(k, c >> 3) * 16 + (c & 7) * 2;
+    }
+  }
 
   bf16x8 fa[2][4], fb[2][4];
   u32x4 fq[4];  // E4M3 B: the codes of two substeps
@@ -133,6 +177,16 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
         if ((ks & 1) == 0)
           fq[j] = *reinterpret_cast<const u32x4*>(sb + b_row_of<GATE_UP>(wn, j) * 64 + rd8[ks >> 1]);
         fb[slot][j] = e4m3x8_to_bf16(fq[j][2 * (ks & 1)], fq[j][2 * (ks & 1) + 1]);
+      } else if constexpr (KMAJ) {
+        // k-rows 16 ks + 4 t + ... of this lane's word; kmaj_chunk depends on
+        // k % 4 only, which the 16 ks + 4 t step keeps
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const char* b0 = sb + rdk[j] + ks * 16 * 512;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(
+            (__attribute__((address_space(3))) char*)b0));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(
+            (__attribute__((address_space(3))) char*)(b0 + 4 * 512)));
+        fb[slot][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       } else {
         fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + b_row_of<GATE_UP>(wn, j) * 128 + rd[ks]);
       }
@@ -148,21 +202,24 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
   // fragment reads of the next substep each behind one MFMA (a burst of reads
   // queues behind the other waves' reads and the loads' LDS writes), then the
   // four loads, one per two MFMAs.  Measured 3-4% faster than reads first.
+  // (K-major B: 12 reads, each B fragment being two transposing reads, and
+  // one MFMA between the loads)
   auto pattern = [&]() {
+    constexpr int RD = KMAJ ? 12 : 8, GAP = KMAJ ? 1 : 2;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < RD; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one fragment read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // one load
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, GAP, 0);
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, GAP, 0);
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, GAP, 0);
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (15 - RD - 3 * GAP > 0) __builtin_amdgcn_sched_group_barrier(0x008, 15 - RD - 3 * GAP, 0);
   };
 
   issue_b(s0, 0, 0, NBL);
@@ -269,7 +326,7 @@ __device__ __forceinline__ void tile_coords(const GroupedGemm& p, int64_t L, int
   n_tile = sn * NS + inner / mh;
 }
 
-template <bool GATE_UP, bool FP8>
+template <bool GATE_UP, bool FP8, bool KMAJ = false>
 __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   // The V - R whole tiles are cut into 8 equal runs, one per XCD: the
   // hardware deals workgroup b to XCD b % 8, so XCD x executes run x in
@@ -340,7 +397,13 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     } else {
       offA[j] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + kb : kOob;
     }
-    if constexpr (!FP8) {
+    if constexpr (KMAJ) {
+      // K-major B: load j writes k-rows 2 (wave*8 + j) and + 1 of a stage;
+      // lane i carries k-row +i/32, chunk position i % 32 (see kmaj_chunk)
+      const int kr = 2 * (wave * 8 + j) + (lane >> 5);
+      const int n = n0 + 8 * kmaj_chunk(kr, lane & 31);
+      offB[j] = n < N ? (uint32_t)kr * (uint32_t)(N * 2) + (uint32_t)n * 2 : kOob;
+    } else if constexpr (!FP8) {
       const int wr = b_weight_row(r);
       offB[j] = wr >= 0 ? (uint32_t)wr * (uint32_t)(K * 2) + kb : kOob;
     } else if (j < 4) {
@@ -368,7 +431,9 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
       if (j < j0 || j >= j1) continue;
       uint32_t o = isB ? offB[j] : offA[j];
       if (tail) {
-        if (b8) {
+        if (KMAJ && isB) {
+          if (k0 + 2 * (wave * 8 + j) + (lane >> 5) >= K) o = kOob;
+        } else if (b8) {
           const int r8 = (wave * 4 + j) * 16 + (lane >> 2);
           if (k0 + ((lane & 3) ^ swz4(r8)) * 16 >= K) o = kOob;
         } else {
@@ -378,8 +443,14 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
         }
       }
       const int blk = b8 ? wave * 4 + j : wave * 8 + j;  // 1-KB block of the stage
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA, (lds_void*)(base + blk * 1024), 16,
-                                               o, k0 * (isB ? EB : 2), 0, 0);
+      // stage offset: k0 elements along each row, or (K-major B) k0 rows of N
+      const uint32_t soff = isB ? (KMAJ ? (uint32_t)k0 * (uint32_t)(N * 2) : (uint32_t)(k0 * EB))
+                                : (uint32_t)(k0 * 2);
+      if constexpr (KMAJ)
+        lds_dma16(isB ? rsB : rsA, base + blk * 1024, o, soff);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA, (lds_void*)(base + blk * 1024), 16,
+                                                 o, (int)soff, 0, 0);
     }
   };
   auto issue_a = [&](int stage, int buf, int j0, int j1) { issue(false, stage, buf, j0, j1); };
@@ -401,11 +472,11 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int s0 = piece ? (int)((int64_t)part * nk / S) : 0;
   const int s1 = piece ? (int)((int64_t)(part + 1) * nk / S) : nk;
   switch (act) {
-    case 4: k_loop<GATE_UP, 4, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 3: k_loop<GATE_UP, 3, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 2: k_loop<GATE_UP, 2, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 1: k_loop<GATE_UP, 1, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    default: k_loop<GATE_UP, 0, FP8>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 4: k_loop<GATE_UP, 4, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 3: k_loop<GATE_UP, 3, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 2: k_loop<GATE_UP, 2, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 1: k_loop<GATE_UP, 1, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    default: k_loop<GATE_UP, 0, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
   }
   auto a_row = [&](int i) { return wm * 128 + i * 32; };
 
@@ -533,6 +604,13 @@ __global__ __launch_bounds__(256) void moe_gemm_down_prefill_kernel(GroupedGemm 
   prefill_tile<false, FP8>(p, lds);
 }
 
+// rows x weight with the weight stored K-major ([K][N] per group): the
+// backward pass's products with W_down and W_gate_up read in their own layout
+__global__ __launch_bounds__(256) void moe_gemm_rows_kmajor_prefill_kernel(GroupedGemm p) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  prefill_tile<false, false, true>(p, lds);
+}
+
 // Finishes the cut tiles of the last round: block b owns rows
 // 16*(b % 16) .. +15 of cut tile b / 16, adds the S partials of each output
 // in K order (piece 0 first) and runs the GEMM's epilogue on the valid rows
@@ -612,11 +690,15 @@ hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
   constexpr int lds = lds_bytes<FP8>();
   // set once per process (a function-local static is initialised thread-safely)
   static const hipError_t attr = [] {
-    const hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    return e != hipSuccess ? e
-                           : hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel<FP8>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel<FP8>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess && !FP8)
+      e = hipFuncSetAttribute((const void*)moe_gemm_rows_kmajor_prefill_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    return e;
   }();
   if (attr != hipSuccess) return attr;
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
@@ -637,6 +719,9 @@ hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
   if (gate_up)
     hipLaunchKernelGGL(moe_gemm_gate_up_prefill_kernel<FP8>, dim3((unsigned)blocks), dim3(256), lds,
                        s, g);
+  else if (g.b_kmajor)
+    hipLaunchKernelGGL(moe_gemm_rows_kmajor_prefill_kernel, dim3((unsigned)blocks), dim3(256), lds,
+                       s, g);
   else
     hipLaunchKernelGGL(moe_gemm_down_prefill_kernel<FP8>, dim3((unsigned)blocks), dim3(256), lds, s,
                        g);
@@ -651,6 +736,7 @@ hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
 }
 
 hipError_t launch(bool gate_up, const GroupedGemm& g, hipStream_t s) {
+  if (g.b_kmajor && (gate_up || g.fp8)) return hipErrorInvalidValue;  // no such variant
   return g.fp8 ? launch_fmt<true>(gate_up, g, s) : launch_fmt<false>(gate_up, g, s);
 }
 

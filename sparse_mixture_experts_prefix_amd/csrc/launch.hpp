@@ -72,6 +72,10 @@ struct GroupedGemm {
   // row r at gu_out + r * ld_gu as [g (N) | u (N)] (kept for the backward pass)
   uint16_t* gu_out;
   int64_t ld_gu;
+  // Down (rows x weight) kernel, bf16, prefill tiles only: B_routed / B_shared
+  // are stored K-major, [K][N] per group (row k holds the N weights that
+  // multiply column k of A), instead of [N][K]
+  int b_kmajor;
 };
 
 // 256 x 256 x 64 tiles for BM = 256 (prefill-sized groups); each launches
