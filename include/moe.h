@@ -1,7 +1,7 @@
 /*
  * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts SwiGLU
  * feed-forward layer: forward pass (moe_forward and its steps) and backward
- * pass (moe_backward).
+ * pass (moe_backward, or moe_forward_train followed by moe_backward_saved).
  *
  * The layer (pages cited by title and section):
  *  - Router: "Mixture of experts: por qué un modelo enorme apenas usa sus
@@ -51,7 +51,8 @@
  *  - Ownership: the caller owns every buffer.  The library allocates no device
  *    memory and keeps no state between calls except a cached device-property
  *    lookup.  The workspace is caller-provided, sized by moe_workspace_size
- *    (moe_backward_workspace_size for the backward pass), and its contents
+ *    (moe_backward_workspace_size for the backward pass,
+ *    moe_train_workspace_size for the training forward), and its contents
  *    need not be initialised.
  *  - Execution: all work is enqueued on `stream` (a hipStream_t; NULL is the
  *    default stream) with no host synchronisation.  Calls on different streams

@@ -51,8 +51,10 @@ struct BwdPlan {
   size_t off_dhp;           // fp32 [cap][ldh]: W_down^T dy
   size_t off_dgu;           // bf16 [cap][2 ldh]: dg | du
   size_t off_dp, off_dl;    // fp32 [T k]
-  size_t off_wdt, off_wdts; // bf16 [E][F][D], [Fs][D]: W_down transposed
-  size_t off_wgut, off_wguts;  // bf16 [E][D][2F], [D][2Fs]: W_gate_up transposed
+  // bf16 transposed weights, for the 16/32-row tiles only (empty regions with
+  // 256-row tiles, which read the weights K-major)
+  size_t off_wdt, off_wdts; // [E][F][D], [Fs][D]: W_down transposed
+  size_t off_wgut, off_wguts;  // [E][D][2F], [D][2Fs]: W_gate_up transposed
   size_t off_dot, off_ht, off_dgut, off_xt;  // bf16 [D | ldh | 2 ldh | D][ldt]
   int64_t ldt;              // cap rounded up to a multiple of 64
   size_t total;
