@@ -326,6 +326,29 @@ __device__ __forceinline__ void tile_coords(const GroupedGemm& p, int64_t L, int
   n_tile = sn * NS + inner / mh;
 }
 
+// Rows of m-tile `m_tile` (of group g).  A group of two m-tiles (a few hundred
+// rows: many experts, few rows each) shares its rows out evenly, q = ceil(count
+// / 2) rounded up to whole 32-row sub-tiles: otherwise its second m-tile holds
+// a few rows, runs ahead of the first (it is load-bound, with almost no MFMA
+// work) and reads the expert's weights from HBM a second time instead of from
+// L2 together with the first.  Larger groups keep full 256-row m-tiles (q =
+// 256): there the light last m-tile costs a smaller share of the weight
+// traffic, and evening out would make every m-tile as slow as a full one (the
+// busier half of a workgroup's waves sets its pace).  Rows stay contiguous:
+// m-tile j covers the group's rows j q .. j q + valid - 1, stored from padded
+// row row0 = group_padded[g] + j q (its 256-row window may reach into the next
+// m-tile's rows, which it neither reads nor writes).
+__device__ __forceinline__ void tile_rows(const GroupedGemm& p, int64_t m_tile, int g, int64_t& row0,
+                                          int& valid) {
+  const int64_t first = p.group_padded[g] / BM;
+  const int64_t mg = p.group_padded[g + 1] / BM - first;
+  const int cnt = p.group_count[g];
+  const int q = mg == 2 ? ((cnt + 1) / 2 + 31) / 32 * 32 : BM;
+  const int64_t j = m_tile - first;
+  row0 = p.group_padded[g] + j * q;
+  valid = max(0, min(q, cnt - (int)(j * q)));
+}
+
 template <bool GATE_UP, bool FP8, bool KMAJ = false>
 __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   // The V - R whole tiles are cut into 8 equal runs, one per XCD: the
@@ -358,8 +381,9 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   constexpr int NB = GATE_UP ? BN / 2 : BN;
   const int n0 = (int)n_tile * NB;
   if (n0 >= N) return;
-  const int64_t row0 = m_tile * BM;
-  const int valid_rows = min(BM, (int)(p.group_count[g] - (row0 - p.group_padded[g])));
+  int64_t row0;
+  int valid_rows;
+  tile_rows(p, m_tile, g, row0, valid_rows);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -581,6 +605,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (row >= valid_rows) continue;  // past the tile's rows: the next m-tile's or padding
       const int64_t grow = row0 + row;
       float* Y = reinterpret_cast<float*>(p.C);
 #pragma unroll
@@ -631,8 +656,9 @@ __global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p
   constexpr int NB = GATE_UP ? BN / 2 : BN;  // output columns of a tile
   const int n0 = (int)n_tile * NB;
   if (n0 >= N) return;
-  const int64_t row0 = m_tile * BM;
-  const int valid_rows = min(BM, (int)(p.group_count[g] - (row0 - p.group_padded[g])));
+  int64_t row0;
+  int valid_rows;
+  tile_rows(p, m_tile, g, row0, valid_rows);
   const int r0 = (blockIdx.x % kFixBlocksPerTile) * kFixRows;
   const int r1 = min(r0 + kFixRows, valid_rows);
   const float* P = p.partial + t * sp.S * (BM * BN);
