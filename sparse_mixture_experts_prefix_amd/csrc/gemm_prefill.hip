@@ -5,9 +5,9 @@
 // packed [E, 2F, D] gate/up tensor of "Transformers v5 El Secreto Detrás de
 // los Modelos MoE Más Rápidos", section "La Solución: WeightConverter"), laid
 // out for CDNA4:
-//  - 4 wavefronts, each owning a 128 x 128 output block as 4 x 4 MFMA
-//    32x32x16 tiles (256 fp32 accumulators per lane), so every 16-byte LDS
-//    read feeds four MFMAs.
+//  - 4 wavefronts, each owning 128 x 128 outputs as 4 x 4 MFMA 32x32x16
+//    tiles (256 fp32 accumulators per lane; its 4 row blocks of 32 alternate
+//    with the other wave row's), so every 16-byte LDS read feeds four MFMAs.
 //  - Operands go HBM/L2 -> LDS with buffer_load ... lds (no registers, no
 //    ds_write); A is double- and B triple-buffered, and a wave's loads of a
 //    stage are spread evenly over the MFMA substeps (see k_loop).
@@ -102,6 +102,11 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const char*
 __device__ __forceinline__ int kmaj_chunk(int k, int c) { return c ^ (4 * (k & 3)); }
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+// First row of A sub-tile i of wave row wm: the 8 sub-tiles of 32 rows
+// alternate between the two wave rows, so a partly filled tile splits its MFMA
+// work over both (the busier wave row sets a workgroup's pace).
+__device__ __forceinline__ int a_row_of(int wm, int i) { return 32 * (2 * i + wm); }
+
 // First LDS row of B sub-tile j of wave column wn.
 template <bool GATE_UP>
 __device__ __forceinline__ int b_row_of(int wn, int j) {
@@ -170,7 +175,7 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     const char* sb = lds + 2 * kABytes + bb * b_stage_bytes<FP8>();
 #pragma unroll
     for (int i = 0; i < ACT; ++i)
-      fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32) * 128 + rd[ks]);
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + a_row_of(wm, i) * 128 + rd[ks]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (FP8) {
@@ -482,7 +487,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
 
   // active 32-row sub-tiles of this wave (uniform): the K loop is compiled
   // once per count so no MFMA sits under a branch
-  const int act = min(4, max(0, (valid_rows - wm * 128 + 31) / 32));
+  const int act = min(4, max(0, ((valid_rows + 31) / 32 - wm + 1) / 2));
   const int lr = lane & 31, kh = lane >> 5;
   f32x16 acc[4][4];
 #pragma unroll
@@ -502,7 +507,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     case 1: k_loop<GATE_UP, 1, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
     default: k_loop<GATE_UP, 0, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
   }
-  auto a_row = [&](int i) { return wm * 128 + i * 32; };
+  auto a_row = [&](int i) { return a_row_of(wm, i); };
 
   // E4M3: every output column times the scale of its weight row
   if constexpr (FP8) {
@@ -533,7 +538,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
       for (int r = 0; r < 16; ++r)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int off = ((i * 32 + 8 * (r >> 2) + (r & 3)) * BN +
+          const int off = ((a_row_of(0, i) + 8 * (r >> 2) + (r & 3)) * BN +
                            (b_row_of<GATE_UP>(0, j) - b_row_of<GATE_UP>(0, 0))) * 4;
           const float v = acc[i][j][r];  // a scalar first: bit_cast of a vector element
                                          // reinterprets the vector's first lane
@@ -836,7 +841,7 @@ __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      const int m = m0 + a_row_of(wm, i) + 8 * (r >> 2) + 4 * kh + (r & 3);
       if (m >= M) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
