@@ -200,3 +200,29 @@ def test_backward_saved_twice_is_deterministic():
     torch.cuda.synchronize()
     for name in a:
         assert torch.equal(a[name], b[name]), name
+
+
+def test_backward_tile_boundaries():
+    """The backward's 256-row tiles at group sizes around tile boundaries (k = 1:
+    exact counts 257, 300, 511, 512, 256, 1, 0, 700; tokens shuffled), with a shared
+    expert.  With k = 1 the routing weight is 1 and the router gradient is exactly 0."""
+    counts = [257, 300, 511, 512, 256, 1, 0, 700]
+    T, D, F, E = sum(counts), 256, 320, len(counts)
+    s = W.Shape(T=T, D=D, E=E, k=1, F=F, Fs=64)
+    inp = W.make_inputs(s, seed=12)
+    order = np.random.default_rng(6).permutation(T)
+    ids = np.repeat(np.arange(E), counts)[order].astype(np.int32).reshape(T, 1)
+    p32 = np.ones((T, 1), np.float32)
+    dy = W.normal_f32((T, D), 3, TAG_DY, 1.0)
+    g = inp.to(DEV)
+    got = moe.moe_backward(g.x, g.w_g, g.w_gate_up, g.w_down, 1, torch.from_numpy(ids).to(DEV),
+                           torch.from_numpy(p32).to(DEV), dy.to(DEV), None, g.ws_gate_up, g.ws_down)
+    torch.cuda.synchronize()
+    got = {n: v.cpu().numpy() for n, v in got.items()}
+    ref = oracle.backward(inp, ids, p32.astype(np.float64), dy.numpy())
+    assert np.all(got["dw_g"] == 0) and np.all(got["d_bias"] == 0)
+    assert np.all(got["dw_gate_up"][6] == 0) and np.all(got["dw_down"][6] == 0)  # the empty expert
+    for name in ("dx", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"):
+        r, m = grad_error(got[name], ref[name])
+        print("tile boundaries %s: RMS err %.3g, max err %.3g (of RMS)" % (name, r, m))
+        assert r <= RMS_TOL and m <= MAX_TOL, name

@@ -525,3 +525,25 @@ def test_errors_are_raised_before_launch():
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_forward(g.x, g.w_g, g.w_gate_up, g.w_down, 9)
     assert ei.value.code in (moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED)
+
+
+def test_forward_routed_tile_boundaries():
+    """256-row tiles at group sizes around tile boundaries (k = 1, so the counts are
+    exact): 257, 300, 511 and 700 rows (two- and three-m-tile groups, the two-tile ones
+    split evenly), 512 and 256 (full tiles), 1 row and an empty expert; tokens in
+    shuffled order so every tile gathers scattered rows."""
+    counts = [257, 300, 511, 512, 256, 1, 0, 700]
+    T, D, F = sum(counts), 256, 320
+    assert moe.moe_block_m(moe.make_shape(T, D, len(counts), F, 1)) == 256
+    s = W.Shape(T=T, D=D, E=len(counts), k=1, F=F, Fs=64)
+    inp = W.make_inputs(s, seed=11)
+    order = np.random.default_rng(5).permutation(T)
+    ids = np.repeat(np.arange(len(counts)), counts)[order].astype(np.int32).reshape(T, 1)
+    p = np.ones((T, 1), np.float32)
+    g = _gpu(inp)
+    y = moe.moe_forward_routed(g.x, g.w_gate_up, g.w_down, torch.from_numpy(ids).to(DEV),
+                               torch.from_numpy(p).to(DEV), g.ws_gate_up, g.ws_down)
+    torch.cuda.synchronize()
+    y_ref = oracle.experts(inp, ids, p.astype(np.float64))
+    rel, _, _ = y_error(y.cpu().numpy(), y_ref)
+    assert rel <= 2e-2
