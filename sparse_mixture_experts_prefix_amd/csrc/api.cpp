@@ -252,8 +252,8 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   if (e == hipSuccess)
     e = kmajor ? gemm(dyr, D, w->w_down, w->ws_down, F, Fs, D, D, dhp, ldh, true)
                : gemm(dyr, D, wdt, wdts, F, Fs, D, D, dhp, ldh);
-  BwdRows rows{cap, B.ldt, total, row_token, row_assign, padded, tile_group, wts, dy, E, P.BM, D, F, Fs,
-               ldh, saved ? nullptr : gu, gu16, dgu, dgu, xr};
+  BwdRows rows{cap, total, row_token, row_assign, padded, tile_group, wts, dy, E, P.BM, D, F, Fs,
+               ldh, saved ? nullptr : gu, gu16, dgu};
   if (e == hipSuccess) e = launch_swiglu_bwd(rows, dhp, dp, s);
   if (e == hipSuccess) e = launch_router_bwd(wts, dp, T, k, dl, s);
   // per-row dx = [dg du] W_gate_up, then dx
@@ -269,20 +269,18 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
                             gr->d_bias, s);
   if (e != hipSuccess) return hip_fail(e);
 
-  // weight gradients over transposed row buffers
-  uint16_t* dot = at<uint16_t>(ws, B.off_dot);
-  uint16_t* ht = at<uint16_t>(ws, B.off_ht);
-  uint16_t* dgut = at<uint16_t>(ws, B.off_dgut);
-  uint16_t* xt = at<uint16_t>(ws, B.off_xt);
-  e = launch_rows_transpose(rows, 0, D, dot, s);
-  if (e == hipSuccess) e = launch_rows_transpose(rows, 1, ldh, ht, s);
-  if (e == hipSuccess) e = launch_rows_transpose(rows, 2, 2 * ldh, dgut, s);
-  if (e == hipSuccess) e = launch_rows_transpose(rows, 3, D, xt, s);
+  // weight gradients over the per-row buffers (the rows are the reduction):
+  // dW_down = sum (p dy) h^T, dW_gate_up = sum [dg du] x^T
+  uint16_t* pdy = at<uint16_t>(ws, B.off_pdy);
+  e = launch_rows(rows, 0, D, pdy, D, s);
+  const uint16_t* hr = saved ? at<const uint16_t>(grp, P.off_h)  // the training forward's h rows
+                             : at<const uint16_t>(ws, B.off_hr);
+  if (!saved && e == hipSuccess) e = launch_rows(rows, 1, ldh, at<uint16_t>(ws, B.off_hr), ldh, s);
   auto tiles = [](int64_t n) { return (n + 255) / 256; };
-  WgradGemm wd{dot, ht, B.ldt, D, ldh, D, F, D, Fs, E, G, padded, counts, gr->dw_down, gr->dws_down,
+  WgradGemm wd{pdy, hr, D, ldh, D, F, D, Fs, E, G, padded, counts, gr->dw_down, gr->dws_down,
                tiles(D), tiles(F > Fs ? F : Fs)};
   if (e == hipSuccess) e = launch_gemm_wgrad(wd, s);
-  WgradGemm wu{dgut, xt, B.ldt, 2 * ldh, D, 2 * F, D, 2 * Fs, D, E, G, padded, counts, gr->dw_gate_up,
+  WgradGemm wu{dgu, xr, 2 * ldh, D, 2 * F, D, 2 * Fs, D, E, G, padded, counts, gr->dw_gate_up,
                gr->dws_gate_up, tiles(2 * ldh), tiles(D)};
   if (e == hipSuccess) e = launch_gemm_wgrad(wu, s);
   if (e != hipSuccess) return hip_fail(e);

@@ -100,10 +100,11 @@ __global__ __launch_bounds__(256) void moe_transpose_kernel(const bf16_t* __rest
   store_tile_t(tile, dst + b * (int64_t)R * C, R, r0, c0, R, C);
 }
 
-// The row-space operands of the weight gradients, transposed: dst[c][r]
-// (row stride ld) for rows r < padded[G] of the layer and columns c < C.
+// Row-space operands of the weight gradients that no kernel stores as bf16
+// rows: dst[r][c] (row stride ld) for rows r < padded[G] of the layer and
+// columns c < C.
 struct RowSource {
-  int kind;  // 0: p_r * dy[t_r] (dO), 1: bf16(SiLU(g) u) (h), 2: dGU rows, 3: x rows
+  int kind;  // 0: p_r * dy[t_r] (dO), 1: bf16(SiLU(g) u) (h)
   const float* dy;            // [T][D]
   const float* topk_w;        // [T*k]
   const int32_t* row_token;   // [rows]
@@ -113,7 +114,6 @@ struct RowSource {
   int E, BM, D, F, Fs, ldh;
   const float* gu;            // [rows][2 ldh], fp32 ...
   const bf16_t* gu16;         // ... or bf16 (kept by a training forward)
-  const bf16_t* rows16;       // [rows][cols] (kind 2: stride 2 ldh; kind 3: stride D)
 };
 
 // eight consecutive values of a g | u row, fp32 or bf16
@@ -149,7 +149,7 @@ __device__ __forceinline__ u32x4 row_values8(const RowSource& q, int64_t r, int 
       for (int u = 0; u < 8; ++u) e[u] = f32_to_bf16(p * f[u]);
       return pack8(e);
     }
-    case 1: {
+    default: {  // 1
       const int Fg = q.tile_group[r / q.BM] >= q.E ? q.Fs : q.F;
       if (c >= Fg) return u32x4{0, 0, 0, 0};  // Fg % 8 == 0: a chunk is all in or all out
       float g[8], u[8];
@@ -159,28 +159,17 @@ __device__ __forceinline__ u32x4 row_values8(const RowSource& q, int64_t r, int 
       for (int w = 0; w < 8; ++w) e[w] = f32_to_bf16(silu(g[w]) * u[w]);
       return pack8(e);
     }
-    case 2: return ld16(q.rows16 + r * 2 * q.ldh + c);
-    default: return ld16(q.rows16 + r * q.D + c);
   }
 }
 
-__global__ __launch_bounds__(256) void moe_rows_transpose_kernel(RowSource q, const int32_t* total,
-                                                                 int C, int64_t ld,
-                                                                 bf16_t* __restrict__ dst) {
-  __shared__ __attribute__((aligned(16))) tile_t tile;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;  // rows on x: their count is the large one
-  const int c0 = blockIdx.y * 64;
-  const int64_t R = total[0];
-  if (r0 >= R) return;
-  for (int i8 = threadIdx.x; i8 < 512; i8 += blockDim.x) {
-    const int i = i8 >> 3, c8 = (i8 & 7) * 8;
-    const int64_t r = r0 + i;
-    const int c = c0 + c8;
-    *reinterpret_cast<u32x4*>(&tile[i][c8]) =
-        (r < R && c < C) ? row_values8(q, r, c) : u32x4{0, 0, 0, 0};
-  }
-  __syncthreads();
-  store_tile_t(tile, dst, ld, r0, c0, R, C);
+__global__ __launch_bounds__(256) void moe_rows_kernel(RowSource q, const int32_t* total, int C,
+                                                      int64_t ld, bf16_t* __restrict__ dst) {
+  const int per_row = C / 8;  // C % 8 == 0
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = i / per_row;
+  if (r >= total[0]) return;
+  const int c = (int)(i - r * per_row) * 8;
+  st16(dst + r * ld + c, row_values8(q, r, c));
 }
 
 // One wave per row: SwiGLU backward.  dh' = W_down^T dy (fp32 rows), p the
@@ -340,12 +329,13 @@ hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, in
   return hipGetLastError();
 }
 
-hipError_t launch_rows_transpose(const BwdRows& b, int kind, int C, uint16_t* dst, hipStream_t s) {
+hipError_t launch_rows(const BwdRows& b, int kind, int C, uint16_t* dst, int64_t ld, hipStream_t s) {
   if (b.cap <= 0 || C <= 0) return hipSuccess;
   RowSource q{kind, b.dy, b.topk_w, b.row_token, b.row_assign, b.padded, b.tile_group, b.E, b.BM,
-              b.D, b.F, b.Fs, b.ldh, b.gu, b.gu16, kind == 2 ? b.dgu : b.xr};
-  hipLaunchKernelGGL(moe_rows_transpose_kernel, dim3((unsigned)((b.cap + 63) / 64), (C + 63) / 64),
-                     dim3(256), 0, s, q, b.total, C, b.ldt, dst);
+              b.D, b.F, b.Fs, b.ldh, b.gu, b.gu16};
+  const int64_t n = b.cap * (C / 8);
+  hipLaunchKernelGGL(moe_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, q, b.total,
+                     C, ld, dst);
   return hipGetLastError();
 }
 

@@ -130,10 +130,13 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 // Stages s0 .. s0+n-1 (n >= 1); ACT = active 32-row A sub-tiles of this wave.
 // E4M3 B: four loads per wave and stage instead of eight, so B(i+3) takes
 // two per substep and the barrier waits with vmcnt(4).
-template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB, bool KMAJ = false>
+// KMAJ: B is K-major (see kmaj_chunk); KA: A is too.
+template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB, bool KMAJ = false,
+          bool KA = false>
 __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, int lane,
                                        IssueA& issue_a, IssueB& issue_b, f32x16 (&acc)[4][4]) {
   static_assert(!KMAJ || (!GATE_UP && !FP8), "K-major B: bf16 rows x weight products only");
+  static_assert(!KA || KMAJ, "K-major A comes with K-major B");
   constexpr int NBL = FP8 ? 4 : 8;  // B loads per wave and stage
   const int lr = lane & 31, kh = lane >> 5;
   // LDS byte offset of this lane's A chunk inside a 32-row block, per k-substep.
@@ -155,7 +158,8 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
   // So group lane q points at k-row 4 t + q / 4 (t: which half of the lane's
   // eight k) and columns 4 (q % 4) .. + 3 of its 16; the four words of a
   // lane's column then arrive as k, k + 1, k + 2, k + 3.
-  int rdk[4];
+  // (A operand alike: lane l needs A[m = l % 32][8 consecutive k], the same shape)
+  int rdk[4], rdka[4];
   {
     const int q = lane & 15, g16 = (lane >> 4) & 1;
     const int k = 8 * kh + (q >> 2);                     // k-row of this lane's word
@@ -164,8 +168,20 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     for (int j = 0; j < 4; ++j) {
       const int c = b_row_of<false>(wn, j) + col;         // column in the 256-wide tile
       rdk[j] = k * 512 + kmaj_chunk(k, c >> 3) * 16 + (c & 7) * 2;
+      const int ca = a_row_of(wm, j) + col;
+      rdka[j] = k * 512 + kmaj_chunk(k, ca >> 3) * 16 + (ca & 7) * 2;
     }
   }
+  // the fragment (8 consecutive k of one column) of a K-major stage, from two
+  // transposing reads at byte offset `off` and 4 k-rows further
+  auto read_tr = [](const char* base, int off) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    typedef __attribute__((address_space(3))) char lds_char;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_char*)(base + off)));
+    const i16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_char*)(base + off + 4 * 512)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   bf16x8 fa[2][4], fb[2][4];
   u32x4 fq[4];  // E4M3 B: the codes of two substeps
@@ -174,8 +190,12 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     const char* sa = lds + (ls & 1) * kABytes;
     const char* sb = lds + 2 * kABytes + bb * b_stage_bytes<FP8>();
 #pragma unroll
-    for (int i = 0; i < ACT; ++i)
-      fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + a_row_of(wm, i) * 128 + rd[ks]);
+    for (int i = 0; i < ACT; ++i) {
+      if constexpr (KA)
+        fa[slot][i] = read_tr(sa, rdka[i] + ks * 16 * 512);
+      else
+        fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + a_row_of(wm, i) * 128 + rd[ks]);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if constexpr (FP8) {
@@ -185,13 +205,7 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
       } else if constexpr (KMAJ) {
         // k-rows 16 ks + 4 t + ... of this lane's word; kmaj_chunk depends on
         // k % 4 only, which the 16 ks + 4 t step keeps
-        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-        const char* b0 = sb + rdk[j] + ks * 16 * 512;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(
-            (__attribute__((address_space(3))) char*)b0));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(
-            (__attribute__((address_space(3))) char*)(b0 + 4 * 512)));
-        fb[slot][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        fb[slot][j] = read_tr(sb, rdk[j] + ks * 16 * 512);
       } else {
         fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + b_row_of<GATE_UP>(wn, j) * 128 + rd[ks]);
       }
@@ -209,7 +223,25 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
   // four loads, one per two MFMAs.  Measured 3-4% faster than reads first.
   // (K-major B: 12 reads, each B fragment being two transposing reads, and
   // one MFMA between the loads)
+  // (both K-major: 16 reads, one per MFMA, with the loads among the last)
   auto pattern = [&]() {
+    if constexpr (KA) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int q = 0; q < 12; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      return;
+    }
     constexpr int RD = KMAJ ? 12 : 8, GAP = KMAJ ? 1 : 2;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
@@ -772,11 +804,13 @@ hipError_t launch(bool gate_up, const GroupedGemm& g, hipStream_t s) {
 }
 
 // ------------------------------------------------------------ weight gradients
-// Group g: C_g[m][n] = sum_k A[m][k0 + k] * B[n][k0 + k] over the group's
-// rows k0 = padded[g] .. padded[g] + counts[g] - 1 (read on the device), with the same
-// 256 x 256 x 64 tiles and K loop as the forward.  A and B are transposed
-// row buffers (one row per output row / column, the layer's rows along K),
-// whose padding rows hold zeros.  A group with no rows stores zeros.
+// Group g: C_g[m][n] = sum_r A[r][m] * B[r][n] over the group's rows
+// r = padded[g] .. padded[g] + counts[g] - 1 (read on the device), with the
+// same 256 x 256 x 64 tiles and K loop as the forward.  A and B are per-row
+// buffers as the layer stores them (row r: its M, resp. N, values), read
+// K-major (the rows are the reduction): both operands through the
+// transposing LDS reads, the loads written out (see lds_dma16).  A group with
+// no rows stores zeros.
 __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int64_t per_group = p.tiles_m * p.tiles_n;
@@ -789,8 +823,8 @@ __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
   const int m0 = mt * BM, n0 = nt * BN;
   if (m0 >= M || n0 >= N) return;
   float* C = shared ? p.C_shared : p.C_routed + (int64_t)g * M * N;
-  const int k0g = p.padded[g];
-  const int K = p.counts[g];  // the group's rows; its padding rows would add zeros
+  const int64_t k0g = p.padded[g];
+  const int K = p.counts[g];  // the group's rows
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -805,37 +839,35 @@ __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   if (K > 0) {
-    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, (uint32_t)(p.rows_a * p.ld * 2));
-    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.B, (uint32_t)(p.rows_b * p.ld * 2));
+    // the group's rows only: reads past them (the K tail) return zeros
+    const __amdgpu_buffer_rsrc_t rsA =
+        make_rsrc(p.A + k0g * p.lda, (uint32_t)((int64_t)K * p.lda * 2));
+    const __amdgpu_buffer_rsrc_t rsB =
+        make_rsrc(p.B + k0g * p.ldb, (uint32_t)((int64_t)K * p.ldb * 2));
+    // load j of a wave writes k-rows 2 (wave*8 + j) and + 1 of a stage; lane
+    // i carries k-row +i/32 and chunk position i % 32 (see kmaj_chunk)
     uint32_t offA[8], offB[8];
-    const int sub = lane >> 3;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int r = (wave * 8 + j) * 8 + sub;
-      const uint32_t kb = ((lane & 7) ^ swz(r)) * 16 + (uint32_t)k0g * 2;
-      offA[j] = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)(p.ld * 2) + kb : kOob;
-      offB[j] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(p.ld * 2) + kb : kOob;
+      const int kr = 2 * (wave * 8 + j) + (lane >> 5);
+      const int c8 = 8 * kmaj_chunk(kr, lane & 31);
+      offA[j] = m0 + c8 < M ? (uint32_t)kr * (uint32_t)(p.lda * 2) + (uint32_t)(m0 + c8) * 2 : kOob;
+      offB[j] = n0 + c8 < N ? (uint32_t)kr * (uint32_t)(p.ldb * 2) + (uint32_t)(n0 + c8) * 2 : kOob;
     }
     auto issue = [&](bool isB, int stage, int buf, int j0, int j1) {
       const int k0 = stage * BK;
       char* base = isB ? lds + 2 * kABytes + buf * kBBytes : lds + buf * kABytes;
-      const bool tail = k0 + BK > K;
+      const uint32_t soff = (uint32_t)k0 * (uint32_t)((isB ? p.ldb : p.lda) * 2);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j < j0 || j >= j1) continue;
-        uint32_t o = isB ? offB[j] : offA[j];
-        if (tail) {
-          const int r = (wave * 8 + j) * 8 + sub;
-          if (k0 + ((lane & 7) ^ swz(r)) * 8 >= K) o = kOob;
-        }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA,
-                                                 (lds_void*)(base + (wave * 8 + j) * 1024), 16, o,
-                                                 k0 * 2, 0, 0);
+        lds_dma16(isB ? rsB : rsA, base + (wave * 8 + j) * 1024, isB ? offB[j] : offA[j], soff);
       }
     };
     auto issue_a = [&](int stage, int buf, int j0, int j1) { issue(false, stage, buf, j0, j1); };
     auto issue_b = [&](int stage, int buf, int j0, int j1) { issue(true, stage, buf, j0, j1); };
-    k_loop<false, 4, false>(lds, 0, (K + BK - 1) / BK, wm, wn, lane, issue_a, issue_b, acc);
+    k_loop<false, 4, false, decltype(issue_a), decltype(issue_b), true, true>(
+        lds, 0, (K + BK - 1) / BK, wm, wn, lane, issue_a, issue_b, acc);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)

@@ -91,10 +91,12 @@ hipError_t launch_gemm_down_decode(const GroupedGemm& g, hipStream_t s);
 // [padded[g], padded[g] + counts[g]) of A[m][r] * B[n][r].  A: rows_a rows,
 // B: rows_b rows, both bf16 with row stride ld; the group's padding rows hold
 // zeros (the K loop reads whole 8-element chunks).
+// Weight gradients: per group C[m][n] = sum over its rows r of A[r][m] B[r][n]
+// (A, B: bf16 row buffers of the layer's padded rows, row strides lda, ldb).
 struct WgradGemm {
   const uint16_t* A;
   const uint16_t* B;
-  int64_t ld, rows_a, rows_b;
+  int64_t lda, ldb;
   int M_routed, N_routed, M_shared, N_shared;
   int E, G;
   const int32_t* padded;  // first row of each group
@@ -109,7 +111,6 @@ hipError_t launch_gemm_wgrad(const WgradGemm& g, hipStream_t s);
 // The rows of one backward call: align outputs and per-row buffers.
 struct BwdRows {
   int64_t cap;                 // allocated rows
-  int64_t ldt;                 // row stride of the transposed row buffers (cap rounded up to 64)
   const int32_t* total;        // padded[G] on the device: rows in use
   const int32_t* row_token;
   const int32_t* row_assign;
@@ -120,9 +121,7 @@ struct BwdRows {
   int E, BM, D, F, Fs, ldh;
   const float* gu;             // [cap][2 ldh] (recomputed), or NULL when gu16 is set
   const uint16_t* gu16;        // [cap][2 ldh] bf16, kept by a training forward
-  const uint16_t* dgu;         // [cap][2 ldh]
-  uint16_t* dgu_w;             // the same buffer, written by the SwiGLU backward
-  const uint16_t* xr;          // [cap][D]
+  uint16_t* dgu_w;             // [cap][2 ldh], written by the SwiGLU backward
 };
 hipError_t launch_gather_rows(const void* src, bool src_f32, const int32_t* row_token,
                               const int32_t* total, int64_t cap, int D, uint16_t* dst, hipStream_t s);
@@ -131,9 +130,9 @@ hipError_t launch_row_assign(const int32_t* row_of, int A, int64_t cap, int32_t*
 hipError_t launch_fill_f32(float* out, int64_t n, hipStream_t s);
 // dst[b][c][r] = src[b][r][c] (bf16)
 hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t s);
-// dst[c][r] (row stride ldt) of rows r in use; kind 0: p_r dy[t_r], 1: bf16(SiLU(g) u),
-// 2: dGU rows, 3: x rows
-hipError_t launch_rows_transpose(const BwdRows& b, int kind, int C, uint16_t* dst, hipStream_t s);
+// dst[r][c] (bf16, row stride ld) of rows r in use, c < C (C % 8 == 0);
+// kind 0: p_r dy[t_r], 1: bf16(SiLU(g) u)
+hipError_t launch_rows(const BwdRows& b, int kind, int C, uint16_t* dst, int64_t ld, hipStream_t s);
 hipError_t launch_swiglu_bwd(const BwdRows& b, const float* dhp, float* dp, hipStream_t s);
 hipError_t launch_router_bwd(const float* topk_w, const float* dp, int T, int k, float* dl,
                              hipStream_t s);

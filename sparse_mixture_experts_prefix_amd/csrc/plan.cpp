@@ -106,10 +106,10 @@ int make_backward_plan(const moe_shape* s, BwdPlan* b) {
   const Plan& P = b->P;
   if (P.fp8) return MOE_ERR_UNSUPPORTED;                       // bf16 expert weights only
   if (s->num_local_experts > 0 && s->num_local_experts != s->E) return MOE_ERR_UNSUPPORTED;
-  // the transposed row buffers are addressed through 32-bit buffer offsets
+  // the row buffers the weight-gradient GEMMs read are addressed through
+  // 32-bit buffer offsets
   const int64_t widest = P.D > 2 * P.ldh ? P.D : 2 * P.ldh;
-  b->ldt = (P.cap_rows + 63) / 64 * 64;
-  if (b->ldt * widest * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (P.cap_rows * widest * 2 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   size_t o = P.total;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -132,11 +132,8 @@ int make_backward_plan(const moe_shape* s, BwdPlan* b) {
   b->off_wdts = take(wt * 2 * (size_t)P.Fs * P.D);
   b->off_wgut = take(wt * 2 * (size_t)P.E_loc * P.D * 2 * P.F);
   b->off_wguts = take(wt * 2 * (size_t)P.D * 2 * P.Fs);
-  const size_t ldt = (size_t)b->ldt;
-  b->off_dot = take(2 * (size_t)P.D * ldt);
-  b->off_ht = take(2 * (size_t)P.ldh * ldt);
-  b->off_dgut = take(2 * (size_t)2 * P.ldh * ldt);
-  b->off_xt = take(2 * (size_t)P.D * ldt);
+  b->off_pdy = take(2 * cap * P.D);
+  b->off_hr = take(2 * cap * P.ldh);
   b->total = o;
   return MOE_OK;
 }

@@ -55,8 +55,7 @@ struct BwdPlan {
   // 256-row tiles, which read the weights K-major)
   size_t off_wdt, off_wdts; // [E][F][D], [Fs][D]: W_down transposed
   size_t off_wgut, off_wguts;  // [E][D][2F], [D][2Fs]: W_gate_up transposed
-  size_t off_dot, off_ht, off_dgut, off_xt;  // bf16 [D | ldh | 2 ldh | D][ldt]
-  int64_t ldt;              // cap rounded up to a multiple of 64
+  size_t off_pdy, off_hr;   // bf16 [cap][D]: p dy rows; [cap][ldh]: h rows (recomputed g | u)
   size_t total;
 };
 int make_backward_plan(const moe_shape* s, BwdPlan* b);

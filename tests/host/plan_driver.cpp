@@ -39,10 +39,8 @@ int main() {
     if (!rb) {
       const size_t boff[] = {P.total,     B.off_rowa, B.off_xr,    B.off_dyr,   B.off_gu,
                              B.off_dhp,   B.off_dgu,  B.off_dp,    B.off_dl,    B.off_wdt,
-                             B.off_wdts,  B.off_wgut, B.off_wguts, B.off_dot,   B.off_ht,
-                             B.off_dgut,  B.off_xt};
-      if (!ordered(boff, 17, B.total)) return 4;
-      if (B.ldt % 64 || B.ldt < P.cap_rows) return 5;
+                             B.off_wdts,  B.off_wgut, B.off_wguts, B.off_pdy,   B.off_hr};
+      if (!ordered(boff, 15, B.total)) return 4;
       btotal = B.total;
     }
     std::printf("%d %d %zu %d %zu\n", rc, moe::choose_block_m(&s), P.total, rb, btotal);
