@@ -6,8 +6,9 @@
 // los Modelos MoE Más Rápidos", section "La Solución: WeightConverter"), laid
 // out for CDNA4:
 //  - 4 wavefronts, each owning 128 x 128 outputs as 4 x 4 MFMA 32x32x16
-//    tiles (256 fp32 accumulators per lane; its 4 row blocks of 32 alternate
-//    with the other wave row's), so every 16-byte LDS read feeds four MFMAs.
+//    tiles (256 fp32 accumulators per lane; in a partly filled tile its 4 row
+//    blocks of 32 alternate with the other wave row's), so every 16-byte LDS
+//    read feeds four MFMAs.
 //  - Operands go HBM/L2 -> LDS with buffer_load ... lds (no registers, no
 //    ds_write); A is double- and B triple-buffered, and a wave's loads of a
 //    stage are spread evenly over the MFMA substeps (see k_loop).
@@ -102,10 +103,13 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const char*
 __device__ __forceinline__ int kmaj_chunk(int k, int c) { return c ^ (4 * (k & 3)); }
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// First row of A sub-tile i of wave row wm: the 8 sub-tiles of 32 rows
-// alternate between the two wave rows, so a partly filled tile splits its MFMA
-// work over both (the busier wave row sets a workgroup's pace).
-__device__ __forceinline__ int a_row_of(int wm, int i) { return 32 * (2 * i + wm); }
+// First row of A sub-tile i of wave row wm.  A full tile gives each wave row
+// a contiguous half; in a partly filled tile (il) the 8 sub-tiles of 32 rows
+// alternate between the two wave rows, so its MFMA work is split over both
+// (the busier wave row sets a workgroup's pace).
+__device__ __forceinline__ int a_row_of(int wm, int i, bool il) {
+  return il ? 32 * (2 * i + wm) : 128 * wm + 32 * i;
+}
 
 // First LDS row of B sub-tile j of wave column wn.
 template <bool GATE_UP>
@@ -133,8 +137,9 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 // KMAJ: B is K-major (see kmaj_chunk); KA: A is too.
 template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB, bool KMAJ = false,
           bool KA = false>
-__device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, int lane,
-                                       IssueA& issue_a, IssueB& issue_b, f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, bool il,
+                                       int lane, IssueA& issue_a, IssueB& issue_b,
+                                       f32x16 (&acc)[4][4]) {
   static_assert(!KMAJ || (!GATE_UP && !FP8), "K-major B: bf16 rows x weight products only");
   static_assert(!KA || KMAJ, "K-major A comes with K-major B");
   constexpr int NBL = FP8 ? 4 : 8;  // B loads per wave and stage
@@ -168,7 +173,7 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     for (int j = 0; j < 4; ++j) {
       const int c = b_row_of<false>(wn, j) + col;         // column in the 256-wide tile
       rdk[j] = k * 512 + kmaj_chunk(k, c >> 3) * 16 + (c & 7) * 2;
-      const int ca = a_row_of(wm, j) + col;
+      const int ca = a_row_of(wm, j, il) + col;
       rdka[j] = k * 512 + kmaj_chunk(k, ca >> 3) * 16 + (ca & 7) * 2;
     }
   }
@@ -194,7 +199,7 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
       if constexpr (KA)
         fa[slot][i] = read_tr(sa, rdka[i] + ks * 16 * 512);
       else
-        fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + a_row_of(wm, i) * 128 + rd[ks]);
+        fa[slot][i] = *reinterpret_cast<const bf16x8*>(sa + a_row_of(wm, i, il) * 128 + rd[ks]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -519,7 +524,9 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
 
   // active 32-row sub-tiles of this wave (uniform): the K loop is compiled
   // once per count so no MFMA sits under a branch
-  const int act = min(4, max(0, ((valid_rows + 31) / 32 - wm + 1) / 2));
+  const bool il = valid_rows < BM;
+  const int act = il ? min(4, max(0, ((valid_rows + 31) / 32 - wm + 1) / 2))
+                     : min(4, max(0, (valid_rows - wm * 128 + 31) / 32));
   const int lr = lane & 31, kh = lane >> 5;
   f32x16 acc[4][4];
 #pragma unroll
@@ -533,13 +540,13 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int s0 = piece ? (int)((int64_t)part * nk / S) : 0;
   const int s1 = piece ? (int)((int64_t)(part + 1) * nk / S) : nk;
   switch (act) {
-    case 4: k_loop<GATE_UP, 4, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 3: k_loop<GATE_UP, 3, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 2: k_loop<GATE_UP, 2, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    case 1: k_loop<GATE_UP, 1, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
-    default: k_loop<GATE_UP, 0, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, lane, issue_a, issue_b, acc); break;
+    case 4: k_loop<GATE_UP, 4, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
+    case 3: k_loop<GATE_UP, 3, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
+    case 2: k_loop<GATE_UP, 2, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
+    case 1: k_loop<GATE_UP, 1, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
+    default: k_loop<GATE_UP, 0, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
   }
-  auto a_row = [&](int i) { return a_row_of(wm, i); };
+  auto a_row = [&](int i) { return a_row_of(wm, i, il); };
 
   // E4M3: every output column times the scale of its weight row
   if constexpr (FP8) {
@@ -570,7 +577,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
       for (int r = 0; r < 16; ++r)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int off = ((a_row_of(0, i) + 8 * (r >> 2) + (r & 3)) * BN +
+          const int off = ((a_row(i) - a_row(0) + 8 * (r >> 2) + (r & 3)) * BN +
                            (b_row_of<GATE_UP>(0, j) - b_row_of<GATE_UP>(0, 0))) * 4;
           const float v = acc[i][j][r];  // a scalar first: bit_cast of a vector element
                                          // reinterprets the vector's first lane
@@ -867,13 +874,13 @@ __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
     auto issue_a = [&](int stage, int buf, int j0, int j1) { issue(false, stage, buf, j0, j1); };
     auto issue_b = [&](int stage, int buf, int j0, int j1) { issue(true, stage, buf, j0, j1); };
     k_loop<false, 4, false, decltype(issue_a), decltype(issue_b), true, true>(
-        lds, 0, (K + BK - 1) / BK, wm, wn, lane, issue_a, issue_b, acc);
+        lds, 0, (K + BK - 1) / BK, wm, wn, false, lane, issue_a, issue_b, acc);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + a_row_of(wm, i) + 8 * (r >> 2) + 4 * kh + (r & 3);
+      const int m = m0 + a_row_of(wm, i, false) + 8 * (r >> 2) + 4 * kh + (r & 3);
       if (m >= M) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
