@@ -297,8 +297,9 @@ int moe_forward_train(const moe_shape* shape, const moe_weights* w, float* y, in
 /*
  * moe_backward using the workspace of a moe_forward_train call with the same
  * shape, weights, x and the routing it returned (train_workspace, untouched
- * since): its grouping and g | u replace the backward's own.  The gradients
- * equal moe_backward's up to g and u being bf16 here (fp32 there).
+ * since, and only read here): its grouping, g | u and h replace the
+ * backward's own.  The gradients equal moe_backward's up to g and u being
+ * bf16 here (fp32 there).
  */
 int moe_backward_saved(const moe_shape* shape, const moe_weights* w, const int32_t* topk_ids,
                        const float* topk_w, const float* dy, const moe_grads* grads,

@@ -152,7 +152,8 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
 
 // Backward pass for a given routing (see moe_backward in moe.h).
 // saved (or NULL): the workspace of a training forward call with the same
-// shape and routing: its grouping and its g | u are used instead of redoing them.
+// shape and routing: its grouping, g | u and h rows are used instead of
+// redoing them (it is only read).
 int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weights* w,
                  const int32_t* ids, const float* wts, const float* dy, const moe_grads* gr,
                  void* ws, hipStream_t s, const void* saved = nullptr) {
