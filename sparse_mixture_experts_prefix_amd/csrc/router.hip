@@ -29,6 +29,11 @@ constexpr int kTok = 16;  // tokens per workgroup
 // depend on T.
 template <int NCT>
 constexpr int waves_for() { return NCT > 8 ? 8 : 16; }
+// 16-token tiles per workgroup: 2 when E > 128, where every workgroup streams
+// all of W_g (E x D) for very little MFMA work; each W_g chunk a wave loads
+// then serves both tiles.  A token's arithmetic is the same either way.
+template <int NCT>
+constexpr int tiles_for() { return NCT > 8 ? 2 : 1; }
 
 template <int NCT>  // 16-expert column tiles; E <= 16 * NCT
 __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const bf16_t* __restrict__ x,
@@ -40,6 +45,7 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
                                                           float* __restrict__ wts) {
   constexpr int EP = 16 * NCT;
   constexpr int kWaves = waves_for<NCT>();
+  constexpr int TT = tiles_for<NCT>();
   // 64-wide K chunks whose loads are in flight together (the same chunk order
   // per wave for every UNR, so the sums do not depend on it)
   constexpr int UNR = NCT <= 2 ? 3 : (NCT <= 4 ? 2 : 1);
@@ -49,31 +55,44 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
   };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t0 = blockIdx.x * kTok;
+  const int tb = blockIdx.x * kTok * TT;  // first token of the workgroup
 
   // ---- this wave's share of the reduction over D
-  f32x4 acc[NCT];
+  f32x4 acc[TT][NCT];
 #pragma unroll
-  for (int c = 0; c < NCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[tt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Inside a 64-wide chunk, x and W_g use the same K permutation: lane
   // (r16, kb) holds bytes [32kb, 32kb+32) of its row for two MFMAs, so the
   // four lanes of a row read one whole 128-byte line.
   const int r16 = lane & 15, kb = lane >> 4;
-  const int tok = t0 + r16;
-  const bf16_t* xr = x + (int64_t)(tok < T ? tok : 0) * D;
+  const bf16_t* xr[TT];
+  bool tin[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int tok = tb + tt * kTok + r16;
+    tin[tt] = tok < T;
+    xr[tt] = x + (int64_t)(tin[tt] ? tok : 0) * D;
+  }
   const int nchunks = (D + 63) / 64;
-  constexpr int CG = NCT < 8 ? NCT : 8;  // column tiles whose weights are loaded together
+  // column tiles whose weights are loaded together (fewer with two token
+  // tiles, for their accumulators' registers)
+  constexpr int CG = TT > 1 ? 4 : (NCT < 8 ? NCT : 8);
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int ch0 = wave; ch0 < nchunks; ch0 += UNR * kWaves) {
 #pragma unroll
     for (int c0 = 0; c0 < NCT; c0 += CG) {
-      u32x4 av[UNR][2], bv[UNR][CG][2];
+      u32x4 av[TT][UNR][2], bv[UNR][CG][2];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         const int kk = (ch0 + u * kWaves) * 64 + kb * 16;  // D % 8 == 0: 8-runs are all in or out
         const bool in0 = ch0 + u * kWaves < nchunks && kk < D, in1 = in0 && kk + 8 < D;
-        av[u][0] = (tok < T && in0) ? ld16(xr + kk) : zero;
-        av[u][1] = (tok < T && in1) ? ld16(xr + kk + 8) : zero;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          av[tt][u][0] = (tin[tt] && in0) ? ld16(xr[tt] + kk) : zero;
+          av[tt][u][1] = (tin[tt] && in1) ? ld16(xr[tt] + kk + 8) : zero;
+        }
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
           const int e = (c0 + c) * 16 + r16;
@@ -84,40 +103,48 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
       }
       __builtin_amdgcn_sched_barrier(0);  // all loads of the trip before the MFMAs
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int u = 0; u < UNR; ++u)
 #pragma unroll
-          for (int c = 0; c < CG; ++c)
-            acc[c0 + c] = mfma16(as_bf16x8(av[u][h]), as_bf16x8(bv[u][c][h]), acc[c0 + c]);
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+              acc[tt][c0 + c] =
+                  mfma16(as_bf16x8(av[tt][u][h]), as_bf16x8(bv[u][c][h]), acc[tt][c0 + c]);
     }
   }
 
-  // ---- partial sums of all waves into LDS; each logit is then the sum over
-  // the waves in wave order (one barrier instead of a tree of them)
 #pragma unroll
-  for (int c = 0; c < NCT; ++c)
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t0 = tb + tt * kTok;
+    if (tt > 0) __syncthreads();  // the previous tile's logits are no longer read
+    // ---- partial sums of all waves into LDS; each logit is then the sum over
+    // the waves in wave order (one barrier instead of a tree of them)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) slot(wave, 4 * kb + r, c * 16 + r16) = acc[c][r];
-  __syncthreads();
-  for (int idx = tid; idx < kTok * EP; idx += kWaves * 64) {
-    const int row = idx / EP, col = idx - row * EP;
-    float sum = slot(0, row, col);
+    for (int c = 0; c < NCT; ++c)
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += slot(w, row, col);
-    if (bias && col < E) sum += bias[col];
-    slot(0, row, col) = sum;  // only this thread reads or writes this element
-  }
-  __syncthreads();
+      for (int r = 0; r < 4; ++r) slot(wave, 4 * kb + r, c * 16 + r16) = acc[tt][c][r];
+    __syncthreads();
+    for (int idx = tid; idx < kTok * EP; idx += kWaves * 64) {
+      const int row = idx / EP, col = idx - row * EP;
+      float sum = slot(0, row, col);
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) sum += slot(w, row, col);
+      if (bias && col < E) sum += bias[col];
+      slot(0, row, col) = sum;  // only this thread reads or writes this element
+    }
+    __syncthreads();
 
-  // ---- top-k + softmax: wave w ranks tokens w, w + kWaves, ...
-  for (int r = wave; r < kTok; r += kWaves) {
-    const int t = t0 + r;
-    if (t >= T) break;
-    topk_softmax(&slot(0, r, 0), sel, E, k, lane, [&](int q, int e, float w) {
-      ids[(int64_t)t * k + q] = e;
-      wts[(int64_t)t * k + q] = w;
-    });
+    // ---- top-k + softmax: wave w ranks tokens w, w + kWaves, ...
+    for (int r = wave; r < kTok; r += kWaves) {
+      const int t = t0 + r;
+      if (t >= T) break;
+      topk_softmax(&slot(0, r, 0), sel, E, k, lane, [&](int q, int e, float w) {
+        ids[(int64_t)t * k + q] = e;
+        wts[(int64_t)t * k + q] = w;
+      });
+    }
   }
 }
 
@@ -130,7 +157,8 @@ hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias,
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)moe_router_kernel<NCT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  const int blocks = (T + kTok - 1) / kTok;
+  const int per_block = kTok * tiles_for<NCT>();
+  const int blocks = (T + per_block - 1) / per_block;
   hipLaunchKernelGGL(moe_router_kernel<NCT>, dim3(blocks), dim3(kWaves * 64), lds, s, x, w_g, bias,
                      sel, T, D, E, k, ids, wts);
   return hipGetLastError();
@@ -210,13 +238,11 @@ template <int NCT>
 hipError_t launch_partial_nct(const uint16_t* x, const uint16_t* w_g, int T, int D, int E,
                               float* partial, hipStream_t s) {
   const size_t lds = sizeof(float) * kPartWaves * kTok * (16 * NCT + 1);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_router_partial_kernel<NCT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set once per process (a function-local static is initialised thread-safely)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)moe_router_partial_kernel<NCT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)lds);
+  if (attr != hipSuccess) return attr;
   const dim3 grid((T + kTok - 1) / kTok, router_parts(D));
   hipLaunchKernelGGL(moe_router_partial_kernel<NCT>, grid, dim3(kPartWaves * 64), lds, s, x, w_g, T,
                      D, E, partial);

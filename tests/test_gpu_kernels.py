@@ -116,12 +116,13 @@ def test_router_exact_ties_on_grid_inputs():
     assert np.array_equal(ids.cpu().numpy(), ids_or)  # logits are exact, so order is too
 
 
-def test_router_batch_invariance():
-    s = W.Shape(T=64, D=2880, E=32, k=4, F=8)
+@pytest.mark.parametrize("E,k", [(32, 4), (256, 8)])  # 256: two 16-token tiles per workgroup
+def test_router_batch_invariance(E, k):
+    s = W.Shape(T=64, D=2880, E=E, k=k, F=8)
     inp = W.make_inputs(s, seed=3)
     g = _gpu(inp)
     ids, w = moe.moe_route(g.x, g.w_g, s.k)
-    for t in (0, 15, 16, 63):
+    for t in (0, 15, 16, 31, 32, 63):
         i1, w1 = moe.moe_route(g.x[t:t + 1].contiguous(), g.w_g, s.k)
         assert torch.equal(i1[0], ids[t]) and torch.equal(w1[0], w[t])
 
