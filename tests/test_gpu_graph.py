@@ -90,3 +90,47 @@ def test_backward_graph_replays_match_eager():
         torch.cuda.synchronize()
         for name in ref:
             assert torch.equal(grads[name], ref[name]), (r, name)
+
+
+def test_training_step_graph_replays_match_eager():
+    """moe_forward_train then moe_backward_saved, captured together as one step."""
+    T, D, E, k, F, Fs = 700, 256, 8, 2, 256, 128
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs)
+    g = W.make_inputs(s, seed=8).to(DEV)
+    x = g.x.clone()
+    dy = W.normal_f32((T, D), 2, 99, 1.0).to(DEV)
+    shape = moe.make_shape(T, D, E, F, k, Fs)
+
+    def bufs():
+        return dict(y=torch.empty((T, D), device=DEV),
+                    ids=torch.empty((T, k), dtype=torch.int32, device=DEV),
+                    w=torch.empty((T, k), device=DEV),
+                    tws=torch.empty(moe.train_workspace_size(shape), dtype=torch.uint8, device=DEV),
+                    bws=torch.empty(moe.backward_workspace_size(shape), dtype=torch.uint8, device=DEV),
+                    grads=None)
+
+    def step(b):
+        moe.moe_forward_train(x, g.w_g, g.w_gate_up, g.w_down, k, None, g.ws_gate_up, g.ws_down,
+                              y=b["y"], topk_ids=b["ids"], topk_w=b["w"], workspace=b["tws"])
+        b["grads"] = moe.moe_backward(x, g.w_g, g.w_gate_up, g.w_down, k, b["ids"], b["w"], dy, None,
+                                      g.ws_gate_up, g.ws_down, workspace=b["bws"],
+                                      grads=b["grads"], saved=b["tws"])
+
+    a = bufs()
+    step(a)  # allocates the gradients and sets the kernels' attributes outside the graph
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(a)
+    ref = bufs()
+    for r in range(3):
+        x.copy_(W.make_x(T, D, seed=200 + r).to(DEV))
+        dy.copy_(W.normal_f32((T, D), 20 + r, 99, 1.0).to(DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(ref)
+        torch.cuda.synchronize()
+        assert torch.equal(a["y"], ref["y"]) and torch.equal(a["ids"], ref["ids"]), r
+        for name in ref["grads"]:
+            assert torch.equal(a["grads"][name], ref["grads"][name]), (r, name)
