@@ -77,7 +77,7 @@ enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* null pointer, size out of range, k > E, D or F not a multiple of 8 */
   MOE_ERR_UNSUPPORTED = -2, /* E > 256, k > 8, or sizes overflowing 32-bit row indices */
-  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than the call's *_workspace_size() */
   MOE_ERR_ALIGNMENT = -4,   /* a pointer not 16-byte aligned */
   MOE_ERR_HIP = -5          /* a HIP launch failed; moe_strerror gives HIP's text */
 };
