@@ -184,8 +184,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the layer has no multi-GPU path; --ep/--rank "
+              "time one expert-parallel rank's shard on one GPU (run with --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -4,7 +4,8 @@ The grouping is the "sort tokens by expert id" of "Mixture of Experts optimiza
 Transformers y LLMs", section "Ejecución eficiente: backends de expertos"
 (grouped_mm backend) together with the token duplication of the glossary
 "MoE (Mixture of Experts - Mezcla de Expertos)", section 3 step 3.  Stability
-(ascending assignment index inside each expert) is this build's reading.
+(ascending assignment index inside each expert) is a reading: the pages leave
+the order inside an expert open.
 """
 import numpy as np
 import pytest
