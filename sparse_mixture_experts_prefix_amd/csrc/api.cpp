@@ -178,10 +178,6 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   float* dxr = at<float>(ws, P.off_yp);
   float* dp = at<float>(ws, B.off_dp);
   float* dl = at<float>(ws, B.off_dl);
-  uint16_t* wdt = at<uint16_t>(ws, B.off_wdt);
-  uint16_t* wdts = at<uint16_t>(ws, B.off_wdts);
-  uint16_t* wgut = at<uint16_t>(ws, B.off_wgut);
-  uint16_t* wguts = at<uint16_t>(ws, B.off_wguts);
   const int E = (int)P.E_loc, D = (int)P.D, F = (int)P.F, Fs = (int)P.Fs, T = (int)P.T,
             k = (int)P.k, ldh = (int)P.ldh;
   const int64_t cap = P.cap_rows;
@@ -200,21 +196,6 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   const int32_t* total = padded + G;  // rows in use
   if (e == hipSuccess) e = launch_gather_rows(w->x, false, row_token, total, cap, D, xr, s);
   if (e == hipSuccess) e = launch_gather_rows(dy, true, row_token, total, cap, D, dyr, s);
-  const uint16_t* wgu = static_cast<const uint16_t*>(w->w_gate_up);
-  const uint16_t* wdn = static_cast<const uint16_t*>(w->w_down);
-  // The 256-row tiles read W_down and W_gate_up K-major, as stored; the
-  // decode-sized tiles take transposed copies.
-  const bool kmajor = prefill;
-  if (!kmajor) {
-    if (e == hipSuccess) e = launch_transpose(wdn, wdt, E, D, F, s);
-    if (e == hipSuccess) e = launch_transpose(wgu, wgut, E, 2 * F, D, s);
-    if (Fs > 0) {
-      if (e == hipSuccess)
-        e = launch_transpose(static_cast<const uint16_t*>(w->ws_down), wdts, 1, D, Fs, s);
-      if (e == hipSuccess)
-        e = launch_transpose(static_cast<const uint16_t*>(w->ws_gate_up), wguts, 1, 2 * Fs, D, s);
-    }
-  }
   if (e != hipSuccess) return hip_fail(e);
 
   // row-space products on the forward's grouped GEMM (rows x weight^T)
@@ -250,17 +231,15 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   // g | u (kept by the training forward, or computed again), then dh' = W_down^T dy
   const uint16_t* gu16 = saved ? at<const uint16_t>(grp, P.off_gusave) : nullptr;
   if (!saved) e = gemm(xr, D, w->w_gate_up, w->ws_gate_up, 2 * F, 2 * Fs, D, D, gu, 2 * ldh);
-  if (e == hipSuccess)
-    e = kmajor ? gemm(dyr, D, w->w_down, w->ws_down, F, Fs, D, D, dhp, ldh, true)
-               : gemm(dyr, D, wdt, wdts, F, Fs, D, D, dhp, ldh);
+  // (both GEMM families read W_down and W_gate_up K-major, as stored)
+  if (e == hipSuccess) e = gemm(dyr, D, w->w_down, w->ws_down, F, Fs, D, D, dhp, ldh, true);
   BwdRows rows{cap, total, row_token, row_assign, padded, tile_group, wts, dy, E, P.BM, D, F, Fs,
                ldh, saved ? nullptr : gu, gu16, dgu};
   if (e == hipSuccess) e = launch_swiglu_bwd(rows, dhp, dp, s);
   if (e == hipSuccess) e = launch_router_bwd(wts, dp, T, k, dl, s);
   // per-row dx = [dg du] W_gate_up, then dx
   if (e == hipSuccess)
-    e = kmajor ? gemm(dgu, 2 * ldh, w->w_gate_up, w->ws_gate_up, D, D, 2 * F, 2 * Fs, dxr, D, true)
-               : gemm(dgu, 2 * ldh, wgut, wguts, D, D, 2 * F, 2 * Fs, dxr, D);
+    e = gemm(dgu, 2 * ldh, w->w_gate_up, w->ws_gate_up, D, D, 2 * F, 2 * Fs, dxr, D, true);
   if (e == hipSuccess)
     e = launch_combine_bwd(dxr, row_of, ids, dl, static_cast<const uint16_t*>(w->w_g), padded, T, D, k,
                            E, Fs > 0 ? 1 : 0, gr->dx, s);

@@ -6,11 +6,11 @@
 // on training; "Transformers v5 El Secreto Detrás de los Modelos MoE Más
 // Rápidos", section "Entrenamiento MoE").  The row-space products (g and u
 // again, dh' = W_down^T dy, dx rows = [dg du] W_gate_up) run on the forward's
-// grouped GEMM over transposed weight copies; the weight gradients on the
-// variable-K grouped GEMM over transposed row buffers.  This file holds the
-// rest, all bandwidth-bound:
+// grouped GEMM families, reading the weights K-major as stored; the weight
+// gradients on a variable-K grouped GEMM over per-row buffers.  This file
+// holds the rest, all bandwidth-bound:
 //  - gathering x and dy rows in expert order (bf16, padding rows zero),
-//  - a batched tiled transpose with a per-element source function,
+//  - per-row bf16 operand rows (p dy, h) of the weight gradients,
 //  - the SwiGLU backward per row, which also forms dp = <dy, O_row>,
 //  - the router's softmax backward dl = p (dp - sum p dp), dW_g and the bias
 //    gradient (sums over an expert's assignments in ascending order),
@@ -54,50 +54,11 @@ __global__ void moe_row_assign_kernel(const int32_t* __restrict__ row_of, int A,
   if (a < A) row_assign[row_of[a]] = a;
 }
 
-// 64 x 64 bf16 tiles through LDS: 16-byte loads along the source rows and
-// 16-byte stores along the destination rows.  LDS rows are 72 elements (144
-// bytes), so the eight rows a store gathers from one column sit on distinct
-// banks.  Needs R and C multiples of 8 (every width here is).
-typedef bf16_t tile_t[64][72];
-
 __device__ __forceinline__ u32x4 pack8(const bf16_t (&e)[8]) {
   u32x4 v;
 #pragma unroll
   for (int u = 0; u < 4; ++u) v[u] = (uint32_t)e[2 * u] | ((uint32_t)e[2 * u + 1] << 16);
   return v;
-}
-
-// tile rows i (source rows r0 + i) are in the tile; write dst[c][r0 + ...] for
-// c in [c0, c0 + 64) and rows < R, row stride ld
-__device__ __forceinline__ void store_tile_t(const tile_t& tile, bf16_t* dst, int64_t ld, int64_t r0,
-                                             int c0, int64_t R, int C) {
-  for (int q = threadIdx.x; q < 512; q += blockDim.x) {
-    const int j = q >> 3, r8 = (q & 7) * 8;
-    const int c = c0 + j;
-    const int64_t r = r0 + r8;
-    if (c >= C || r >= R) continue;
-    bf16_t e[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) e[u] = tile[r8 + u][j];
-    st16(dst + (int64_t)c * ld + r, pack8(e));
-  }
-}
-
-// Batched transpose: dst[b][c][r] = src[b][r][c].
-__global__ __launch_bounds__(256) void moe_transpose_kernel(const bf16_t* __restrict__ src,
-                                                            bf16_t* __restrict__ dst, int R, int C) {
-  __shared__ __attribute__((aligned(16))) tile_t tile;
-  const int64_t b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const bf16_t* s = src + b * (int64_t)R * C;
-  for (int q = threadIdx.x; q < 512; q += blockDim.x) {
-    const int i = q >> 3, c8 = (q & 7) * 8;
-    const int r = r0 + i, c = c0 + c8;
-    const u32x4 v = (r < R && c < C) ? ld16(s + (int64_t)r * C + c) : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(&tile[i][c8]) = v;
-  }
-  __syncthreads();
-  store_tile_t(tile, dst + b * (int64_t)R * C, R, r0, c0, R, C);
 }
 
 // Row-space operands of the weight gradients that no kernel stores as bf16
@@ -319,13 +280,6 @@ hipError_t launch_row_assign(const int32_t* row_of, int A, int64_t cap, int32_t*
 hipError_t launch_fill_f32(float* out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(moe_fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, out, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t s) {
-  if (B <= 0 || R <= 0 || C <= 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_transpose_kernel, dim3((C + 63) / 64, (R + 63) / 64, B), dim3(256), 0, s, src,
-                     dst, R, C);
   return hipGetLastError();
 }
 

@@ -40,4 +40,23 @@ __device__ __forceinline__ float silu(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// One 16-byte-per-lane buffer load into LDS (lane i writes bytes 16 i ..
+// 16 i + 15 of the 1-KB block at `dst`), written out for the kernels that
+// read B with the transposing LDS read: the compiler makes such a read wait
+// for every LDS load it knows to be in flight (vmcnt(0), which would drain
+// the prefetch of the coming stages), while the K loop's own waits and
+// barriers already order these loads before the reads of their stage.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const char* dst, uint32_t voff,
+                                          uint32_t soff) {
+  // M0 (the LDS base of the load) is saved and restored around it
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)dst;  // low bits of the generic pointer
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");
+}
+
 }  // namespace moe

@@ -28,6 +28,9 @@
 //    value), and each output column's sum is multiplied by its row's scale
 //    after the reduction: sum_k x_k (q_k s) = s sum_k x_k q_k.  Half the
 //    weight bytes of bf16, for the same MFMAs.
+//  - The backward pass's products with the weights as stored (contracting
+//    over their row index) stage the weights through LDS instead; see the
+//    K-major tile below.
 #include <type_traits>
 
 #include "device.hpp"
@@ -312,6 +315,207 @@ template <bool FP8, bool NARROW> constexpr int ng_down() {
 }
 template <bool FP8> constexpr int unroll() { return FP8 ? kUnrFp8 : kUnr; }
 
+// ---------------------------------------------------------------- K-major B
+// The backward pass's row products with W_down and W_gate_up as they are
+// stored: C[r][n] = sum_k A[r][k] B[k][n], B being the group's [K][N] slab
+// (k-row k holds the N weights that multiply column k of A).  An MFMA operand
+// takes eight consecutive k of one column per lane, so each wave stages 64
+// k-rows x 64 columns of B, with its 16 MT rows x 64 k of A, through LDS
+// (16-byte LDS-direct loads) and reads B back with the transposing read.
+// A wave owns a ring of stages, so the K loop has no workgroup barrier:
+// the later chunks stream in while one is multiplied.  The waves
+// split K by chunks as above, and their sums are added in the same order.
+constexpr int kKmBBytes = 64 * 128;  // a stage's B: 64 k-rows x 64 columns, bf16
+template <int MT> constexpr int km_a_bytes() { return 16 * MT * 128; }
+template <int MT> constexpr int km_stage_bytes() { return km_a_bytes<MT>() + kKmBBytes; }
+// stages per wave: 16-row tiles take two, so two workgroups share a CU (80 KB
+// each) and one's start and end overlap the other's streaming; 32-row tiles
+// take three (144 KB, one workgroup per CU)
+template <int MT> constexpr int km_stages() { return MT == 1 ? 2 : 3; }
+template <int MT> constexpr int km_lds_bytes() { return kKw * km_stages<MT>() * km_stage_bytes<MT>(); }
+
+// 16-byte chunk c (columns 8c .. 8c + 7) of k-row r of a B stage sits at
+// chunk position c ^ km_b_swz(r) of the row's 128 bytes.  A 32-lane half of a
+// transposing read covers k-rows R .. R + 3 and R + 8 .. R + 11 (R a multiple
+// of 4 with bit 3 clear), two chunks each: row parity picks the 128-byte half
+// of the 64 banks and the swizzle spreads the four rows of each parity over
+// distinct chunk pairs, so every bank is hit once.  Row r of an A stage keeps
+// chunk c (k 8c .. 8c + 7) at c ^ ((r >> 1) & 7): 16 rows' same chunk land in
+// 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int km_b_swz(int r) { return 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1); }
+__device__ __forceinline__ int km_a_swz(int r) { return (r >> 1) & 7; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int MT>
+__device__ __forceinline__ void decode_tile_kmajor(const GroupedGemm& p, char* lds) {
+  constexpr int NG = 4, BMD = 16 * MT, NOUT = 16 * NG;
+  constexpr int SB = km_stage_bytes<MT>(), AB = km_a_bytes<MT>(), S = km_stages<MT>();
+  constexpr int NA = AB / 1024, NB = kKmBBytes / 1024, V = NA + NB;  // 1-KB loads per chunk
+
+  const int64_t bid = blockIdx.x;
+  const int64_t n_tile = bid % p.n_tiles_n;
+  const int64_t m_tile = bid / p.n_tiles_n;
+  if (m_tile >= p.n_tiles[0]) return;
+  const int g = p.tile_group[m_tile];
+  const bool shared = g >= p.E;
+  const int N = shared ? p.N_shared : p.N_routed;
+  const int K = shared ? p.K_shared : p.K_routed;
+  const int n0 = (int)n_tile * NOUT;
+  if (n0 >= N) return;
+  const int64_t row0 = m_tile * BMD;
+  const int valid_rows = min(BMD, (int)(p.group_count[g] - (row0 - p.group_padded[g])));
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, gq = lane >> 4;
+
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A + row0 * p.lda, (uint32_t)(BMD * p.lda * 2));
+  const char* Bbytes = shared ? static_cast<const char*>(p.B_shared)
+                              : static_cast<const char*>(p.B_routed) + (int64_t)g * K * N * 2;
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Bbytes, (uint32_t)((int64_t)K * N * 2));
+  // LDS-direct load b of a stage: lane i writes 16 bytes at 16 i of its 1-KB
+  // block, i.e. row (A) or k-row (B) 8 b + i / 8, chunk position i % 8.
+  // Offsets at k = 0; out-of-range ones (rows past the group, columns past N)
+  // stay out of range when k0's bytes are added.
+  const int ir = lane >> 3, ip = lane & 7;
+  uint32_t aoff[NA], boff[NB];
+  int akc[NA];  // first k of the A chunk, inside the 64-wide K chunk
+#pragma unroll
+  for (int b = 0; b < NA; ++b) {
+    const int r = 8 * b + ir, ch = ip ^ km_a_swz(r);
+    akc[b] = 8 * ch;
+    aoff[b] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + ch * 16 : kOob;
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = 8 * b + ir, n = n0 + 8 * (ip ^ km_b_swz(r));
+    boff[b] = n < N ? (uint32_t)r * (uint32_t)(N * 2) + n * 2 : kOob;
+  }
+  // Reads.  MFMA step h of a chunk takes k = 32 h + 8 gq + (0 .. 7) in lane
+  // (c, gq).  A: row 16 i + c, chunk 4 h + gq.  B: a transposing read gives
+  // lane i of each 16-lane group element i % 4 of the words of group lanes
+  // i / 4, + 4, + 8, + 12, so lane c points at k-row 8 gq + c / 4 (+ 4 for the
+  // upper four k, + 32 h) and columns 16 j + 4 (c % 4) .. + 3: lane c then gets
+  // column 16 j + c at four consecutive k.  The swizzle of those k-rows does
+  // not depend on h or the + 4.
+  int rdA[MT][2], rdB[NG];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 16 * i + c;
+      rdA[i][h] = r * 128 + 16 * ((4 * h + gq) ^ km_a_swz(r));
+    }
+  {
+    const int rb = 8 * gq + (c >> 2);
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+      rdB[j] = AB + rb * 128 + 16 * ((2 * j + ((c & 3) >> 1)) ^ km_b_swz(rb)) + 8 * (c & 1);
+  }
+
+  f32x4 acc[MT][NG];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's chunks: q = wave + kKw m, m = 0 .. nm - 1
+  const int nq = (K + 63) / 64;
+  const int nm = wave < nq ? (nq - 1 - wave) / kKw + 1 : 0;
+  char* ring = lds + wave * (S * SB);
+  auto issue = [&](int m, int slot) {
+    const int k0 = (wave + kKw * m) * 64;
+    char* st = ring + slot * SB;
+#pragma unroll
+    for (int b = 0; b < NA; ++b)
+      lds_dma16(rsA, st + b * 1024, k0 + akc[b] < K ? aoff[b] + 2 * k0 : kOob, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      lds_dma16(rsB, st + AB + b * 1024,
+                k0 + 8 * b + ir < K ? boff[b] + (uint32_t)k0 * (uint32_t)(N * 2) : kOob, 0);
+  };
+  auto read_tr = [](const char* q) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_v4;
+    typedef __attribute__((address_space(3))) char lds_char;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)((lds_char*)q));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)((lds_char*)(q + 4 * 128)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // all S stages start filling; chunk m + S refills chunk m's stage once its
+  // MFMAs have taken their operands
+#pragma unroll
+  for (int m = 0; m < S; ++m)
+    if (m < nm) issue(m, m);
+  int slot = 0;
+  for (int m = 0; m < nm; ++m) {
+    // chunk m has landed once at most the loads of the later chunks issued so
+    // far (min(nm - 1 - m, S - 1) chunks) are in flight
+    const int later = min(nm - 1 - m, S - 1);
+    if (S > 2 && later >= 2)
+      wait_vmcnt<(S > 2 ? 2 : 1) * V>();
+    else if (later >= 1)
+      wait_vmcnt<V>();
+    else
+      wait_vmcnt<0>();
+    const char* st = ring + slot * SB;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 a[MT], b[NG];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + rdA[i][h]);
+#pragma unroll
+      for (int j = 0; j < NG; ++j) b[j] = read_tr(st + rdB[j] + h * 32 * 128);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NG; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+    }
+    if (m + S < nm) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's reads are done
+      issue(m + S, slot);
+    }
+    slot = slot == S - 1 ? 0 : slot + 1;
+  }
+
+  // ---- fixed-order sum over the waves, (((w0 + w1) + w2) + w3), in the
+  // stage memory (every wave's loads have landed: its last wait was vmcnt(0))
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [kKw - 1][MT][NG][64]
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NG; ++j) red[(((wave - 1) * MT + i) * NG + j) * 64 + lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kKw - 1; ++w)
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NG; ++j) acc[i][j] += red[((w * MT + i) * NG + j) * 64 + lane];
+
+  // ---- epilogue: lane (c, gq) holds rows 4 gq + r, column c of each 16x16 tile
+  float* Y = reinterpret_cast<float*>(p.C);
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t grow = row0 + i * 16 + 4 * gq + r;
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const int n = n0 + j * 16 + c;
+        if (n < N) Y[grow * p.ldc + n] = acc[i][j][r];
+      }
+    }
+}
+
 template <int MT, bool FP8, bool NARROW>
 __global__ __launch_bounds__(kKw * 64) void moe_gemm_gate_up_decode_kernel(GroupedGemm p) {
   decode_tile<true, MT, ng_gate_up<FP8, NARROW>(), kKw, unroll<FP8>(), FP8>(p);
@@ -352,6 +556,32 @@ hipError_t launch_width(bool gate_up, const GroupedGemm& g, hipStream_t s) {
 }
 
 template <int MT>
+__global__ __launch_bounds__(kKw * 64) void moe_gemm_rows_kmajor_decode_kernel(GroupedGemm p) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  decode_tile_kmajor<MT>(p, lds);
+}
+
+template <int MT>
+hipError_t launch_kmajor(const GroupedGemm& g0, hipStream_t s) {
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)moe_gemm_rows_kmajor_decode_kernel<MT>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, km_lds_bytes<MT>());
+  if (attr != hipSuccess) return attr;
+  // a group's slab is addressed with 32-bit offsets
+  if ((int64_t)g0.K_routed * g0.N_routed * 2 >= (int64_t(1) << 31) ||
+      (int64_t)g0.K_shared * g0.N_shared * 2 >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  GroupedGemm g = g0;
+  const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
+  g.n_tiles_n = (nmax + 63) / 64;
+  const int64_t blocks = g.max_tiles * g.n_tiles_n;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((moe_gemm_rows_kmajor_decode_kernel<MT>), dim3((unsigned)blocks), dim3(kKw * 64),
+                     km_lds_bytes<MT>(), s, g);
+  return hipGetLastError();
+}
+
+template <int MT>
 hipError_t launch_fmt(bool gate_up, const GroupedGemm& g, hipStream_t s) {
   return g.fp8 ? launch_width<MT, true>(gate_up, g, s) : launch_width<MT, false>(gate_up, g, s);
 }
@@ -359,12 +589,19 @@ hipError_t launch_fmt(bool gate_up, const GroupedGemm& g, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_gate_up_decode(const GroupedGemm& g, hipStream_t s) {
+  if (g.b_kmajor) return hipErrorInvalidValue;
   if (g.BM == 16) return launch_fmt<1>(true, g, s);
   if (g.BM == 32) return launch_fmt<2>(true, g, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_down_decode(const GroupedGemm& g, hipStream_t s) {
+  if (g.b_kmajor) {
+    if (g.fp8) return hipErrorInvalidValue;  // K-major weights: bf16 only
+    if (g.BM == 16) return launch_kmajor<1>(g, s);
+    if (g.BM == 32) return launch_kmajor<2>(g, s);
+    return hipErrorInvalidValue;
+  }
   if (g.BM == 16) return launch_fmt<1>(false, g, s);
   if (g.BM == 32) return launch_fmt<2>(false, g, s);
   return hipErrorInvalidValue;

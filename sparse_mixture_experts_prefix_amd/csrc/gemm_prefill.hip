@@ -77,25 +77,6 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// One 16-byte-per-lane buffer load into LDS (lane i writes bytes 16 i ..
-// 16 i + 15 of the 1-KB block at `dst`), written out for the kernels that
-// read B with the transposing LDS read: the compiler makes such a read wait
-// for every LDS load it knows to be in flight (vmcnt(0), which would drain
-// the prefetch of the coming stages), while the K loop's own waits and
-// barriers already order these loads before the reads of their stage.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, const char* dst, uint32_t voff,
-                                          uint32_t soff) {
-  // M0 (the LDS base of the load) is saved and restored around it
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)dst;  // low bits of the generic pointer
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
-      : "memory");
-}
-
 // K-major B stage: 64 k-rows of 512 B (256 columns).  16-byte chunk c of
 // k-row k is stored at chunk position c ^ (4 (k % 4)): the transposing reads of
 // a 32-lane half (4 k-rows x 4 chunks) then hit 16 distinct chunk positions

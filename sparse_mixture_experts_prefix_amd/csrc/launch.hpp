@@ -72,9 +72,9 @@ struct GroupedGemm {
   // row r at gu_out + r * ld_gu as [g (N) | u (N)] (kept for the backward pass)
   uint16_t* gu_out;
   int64_t ld_gu;
-  // Down (rows x weight) kernel, bf16, prefill tiles only: B_routed / B_shared
-  // are stored K-major, [K][N] per group (row k holds the N weights that
-  // multiply column k of A), instead of [N][K]
+  // Down (rows x weight) kernels, bf16 only: B_routed / B_shared are stored
+  // K-major, [K][N] per group (row k holds the N weights that multiply
+  // column k of A), instead of [N][K]
   int b_kmajor;
 };
 
@@ -128,8 +128,6 @@ hipError_t launch_gather_rows(const void* src, bool src_f32, const int32_t* row_
 hipError_t launch_row_assign(const int32_t* row_of, int A, int64_t cap, int32_t* row_assign,
                              hipStream_t s);
 hipError_t launch_fill_f32(float* out, int64_t n, hipStream_t s);
-// dst[b][c][r] = src[b][r][c] (bf16)
-hipError_t launch_transpose(const uint16_t* src, uint16_t* dst, int B, int R, int C, hipStream_t s);
 // dst[r][c] (bf16, row stride ld) of rows r in use, c < C (C % 8 == 0);
 // kind 0: p_r dy[t_r], 1: bf16(SiLU(g) u)
 hipError_t launch_rows(const BwdRows& b, int kind, int C, uint16_t* dst, int64_t ld, hipStream_t s);

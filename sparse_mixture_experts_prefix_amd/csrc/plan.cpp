@@ -125,13 +125,6 @@ int make_backward_plan(const moe_shape* s, BwdPlan* b) {
   b->off_dgu = take(2 * cap * 2 * P.ldh);
   b->off_dp = take(4 * (size_t)P.A);
   b->off_dl = take(4 * (size_t)P.A);
-  // transposed weights: only the 16/32-row tiles use them (the 256-row tiles
-  // read the weights K-major as stored)
-  const size_t wt = P.BM == 256 ? 0 : 1;
-  b->off_wdt = take(wt * 2 * (size_t)P.E_loc * P.F * P.D);
-  b->off_wdts = take(wt * 2 * (size_t)P.Fs * P.D);
-  b->off_wgut = take(wt * 2 * (size_t)P.E_loc * P.D * 2 * P.F);
-  b->off_wguts = take(wt * 2 * (size_t)P.D * 2 * P.Fs);
   b->off_pdy = take(2 * cap * P.D);
   b->off_hr = take(2 * cap * P.ldh);
   b->total = o;

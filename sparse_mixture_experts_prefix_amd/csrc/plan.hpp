@@ -51,10 +51,6 @@ struct BwdPlan {
   size_t off_dhp;           // fp32 [cap][ldh]: W_down^T dy
   size_t off_dgu;           // bf16 [cap][2 ldh]: dg | du
   size_t off_dp, off_dl;    // fp32 [T k]
-  // bf16 transposed weights, for the 16/32-row tiles only (empty regions with
-  // 256-row tiles, which read the weights K-major)
-  size_t off_wdt, off_wdts; // [E][F][D], [Fs][D]: W_down transposed
-  size_t off_wgut, off_wguts;  // [E][D][2F], [D][2Fs]: W_gate_up transposed
   size_t off_pdy, off_hr;   // bf16 [cap][D]: p dy rows; [cap][ldh]: h rows (recomputed g | u)
   size_t total;
 };

@@ -37,10 +37,9 @@ int main() {
     const int rb = moe::make_backward_plan(&s, &B);
     size_t btotal = 0;
     if (!rb) {
-      const size_t boff[] = {P.total,     B.off_rowa, B.off_xr,    B.off_dyr,   B.off_gu,
-                             B.off_dhp,   B.off_dgu,  B.off_dp,    B.off_dl,    B.off_wdt,
-                             B.off_wdts,  B.off_wgut, B.off_wguts, B.off_pdy,   B.off_hr};
-      if (!ordered(boff, 15, B.total)) return 4;
+      const size_t boff[] = {P.total,   B.off_rowa, B.off_xr, B.off_dyr, B.off_gu, B.off_dhp,
+                             B.off_dgu, B.off_dp,   B.off_dl, B.off_pdy, B.off_hr};
+      if (!ordered(boff, 11, B.total)) return 4;
       btotal = B.total;
     }
     std::printf("%d %d %zu %d %zu\n", rc, moe::choose_block_m(&s), P.total, rb, btotal);

@@ -78,6 +78,8 @@ CASES = [
     (2048, 256, 8, 2, 512, 0, False),    # 256-row tiles
     (1500, 320, 8, 2, 200, 0, True),     # 256-row tiles, ragged M, N and K, bias in the logits
     (700, 512, 16, 4, 256, 256, False),  # 256-row tiles with the shared expert
+    (32, 1024, 8, 2, 768, 256, False),   # 16-row tiles, K = 1024 and 1536: several K chunks per wave
+    (200, 1024, 16, 2, 640, 0, True),    # 32-row tiles, K = 1024 and 1280
 ]
 
 
@@ -202,11 +204,15 @@ def test_backward_saved_twice_is_deterministic():
         assert torch.equal(a[name], b[name]), name
 
 
-def test_backward_tile_boundaries():
-    """The backward's 256-row tiles at group sizes around tile boundaries (k = 1:
-    exact counts 257, 300, 511, 512, 256, 1, 0, 700; tokens shuffled), with a shared
-    expert.  With k = 1 the routing weight is 1 and the router gradient is exactly 0."""
-    counts = [257, 300, 511, 512, 256, 1, 0, 700]
+@pytest.mark.parametrize("counts", [
+    [257, 300, 511, 512, 256, 1, 0, 700],  # 256-row tiles
+    [16, 17, 1, 0, 15, 32, 8, 3],          # 16-row tiles
+    [33, 32, 64, 1, 0, 40, 31, 47],        # 32-row tiles
+])
+def test_backward_tile_boundaries(counts):
+    """The backward's tiles at group sizes around tile boundaries (k = 1, exact
+    counts, tokens shuffled), with a shared expert.  With k = 1 the routing weight
+    is 1 and the router gradient is exactly 0."""
     T, D, F, E = sum(counts), 256, 320, len(counts)
     s = W.Shape(T=T, D=D, E=E, k=1, F=F, Fs=64)
     inp = W.make_inputs(s, seed=12)
@@ -221,7 +227,8 @@ def test_backward_tile_boundaries():
     got = {n: v.cpu().numpy() for n, v in got.items()}
     ref = oracle.backward(inp, ids, p32.astype(np.float64), dy.numpy())
     assert np.all(got["dw_g"] == 0) and np.all(got["d_bias"] == 0)
-    assert np.all(got["dw_gate_up"][6] == 0) and np.all(got["dw_down"][6] == 0)  # the empty expert
+    z = counts.index(0)  # the empty expert
+    assert np.all(got["dw_gate_up"][z] == 0) and np.all(got["dw_down"][z] == 0)
     for name in ("dx", "dw_gate_up", "dw_down", "dws_gate_up", "dws_down"):
         r, m = grad_error(got[name], ref[name])
         print("tile boundaries %s: RMS err %.3g, max err %.3g (of RMS)" % (name, r, m))
