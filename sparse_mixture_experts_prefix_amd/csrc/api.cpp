@@ -257,11 +257,15 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
                              : at<const uint16_t>(ws, B.off_hr);
   if (!saved && e == hipSuccess) e = launch_rows(rows, 1, ldh, at<uint16_t>(ws, B.off_hr), ldh, s);
   auto tiles = [](int64_t n) { return (n + 255) / 256; };
+  // a token picks an expert at most once, so with T <= 64 every group has at
+  // most 64 rows: one K stage per tile, run by one workgroup per CU
+  int one_stage = 0;
+  if (e == hipSuccess && T <= 64) e = split_ctas(&one_stage);
   WgradGemm wd{pdy, hr, D, ldh, D, F, D, Fs, E, G, padded, counts, gr->dw_down, gr->dws_down,
-               tiles(D), tiles(F > Fs ? F : Fs)};
+               tiles(D), tiles(F > Fs ? F : Fs), one_stage};
   if (e == hipSuccess) e = launch_gemm_wgrad(wd, s);
   WgradGemm wu{dgu, xr, 2 * ldh, D, 2 * F, D, 2 * Fs, D, E, G, padded, counts, gr->dw_gate_up,
-               gr->dws_gate_up, tiles(2 * ldh), tiles(D)};
+               gr->dws_gate_up, tiles(2 * ldh), tiles(D), one_stage};
   if (e == hipSuccess) e = launch_gemm_wgrad(wu, s);
   if (e != hipSuccess) return hip_fail(e);
   return MOE_OK;

@@ -117,7 +117,7 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 // two per substep and the barrier waits with vmcnt(4).
 // KMAJ: B is K-major (see kmaj_chunk); KA: A is too.
 template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB, bool KMAJ = false,
-          bool KA = false>
+          bool KA = false, bool PRE = false>
 __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, bool il,
                                        int lane, IssueA& issue_a, IssueB& issue_b,
                                        f32x16 (&acc)[4][4]) {
@@ -245,8 +245,10 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     if constexpr (15 - RD - 3 * GAP > 0) __builtin_amdgcn_sched_group_barrier(0x008, 15 - RD - 3 * GAP, 0);
   };
 
-  issue_b(s0, 0, 0, NBL);
-  issue_a(s0, 0, 0, 8);
+  if constexpr (!PRE) {  // PRE: the caller has issued stage s0's loads
+    issue_b(s0, 0, 0, NBL);
+    issue_a(s0, 0, 0, 8);
+  }
   if (n > 1) issue_b(s0 + 1, 1, 0, NBL);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
@@ -791,6 +793,84 @@ hipError_t launch(bool gate_up, const GroupedGemm& g, hipStream_t s) {
   return g.fp8 ? launch_fmt<true>(gate_up, g, s) : launch_fmt<false>(gate_up, g, s);
 }
 
+// One tile of a weight gradient: its group, corner and row count.
+struct WgradTile {
+  int g, M, N, m0, n0, K;
+  int64_t k0g;  // the group's first row
+  float* C;
+  bool valid;   // the tile's corner lies inside its group's matrix
+};
+
+__device__ __forceinline__ WgradTile wgrad_tile(const WgradGemm& p, int64_t t) {
+  const int64_t per_group = p.tiles_m * p.tiles_n;
+  WgradTile w;
+  w.g = (int)(t / per_group);
+  const int64_t rem = t - (int64_t)w.g * per_group;
+  const int mt = (int)(rem / p.tiles_n), nt = (int)(rem % p.tiles_n);
+  const bool shared = w.g >= p.E;
+  w.M = shared ? p.M_shared : p.M_routed;
+  w.N = shared ? p.N_shared : p.N_routed;
+  w.m0 = mt * BM;
+  w.n0 = nt * BN;
+  w.valid = w.m0 < w.M && w.n0 < w.N;
+  w.C = shared ? p.C_shared : p.C_routed + (int64_t)w.g * w.M * w.N;
+  // uniform across the workgroup: they feed the loads' scalar descriptors
+  w.k0g = __builtin_amdgcn_readfirstlane(p.padded[w.g]);
+  w.K = __builtin_amdgcn_readfirstlane(p.counts[w.g]);
+  return w;
+}
+
+// Issues K stage `stage` of tile w into LDS buffer `buf` (A at buf * kABytes,
+// B at 2 kABytes + buf * kBBytes), the part of load slots j0 .. j1 - 1 of
+// each wave: load j of a wave writes k-rows 2 (wave*8 + j) and + 1 of a
+// stage; lane i carries k-row +i/32 and chunk position i % 32 (see
+// kmaj_chunk).  Only the group's rows are addressable, so reads past them
+// (the K tail) return zeros.
+__device__ __forceinline__ void wgrad_issue(const WgradGemm& p, const WgradTile& w, char* lds, bool isB,
+                                            int stage, int buf, int j0, int j1, int wave, int lane) {
+  const int64_t ld = isB ? p.ldb : p.lda;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc((isB ? p.B : p.A) + w.k0g * ld, (uint32_t)((int64_t)w.K * ld * 2));
+  const int lim = isB ? w.N : w.M, c0 = isB ? w.n0 : w.m0;
+  const int k0 = stage * BK;
+  char* base = isB ? lds + 2 * kABytes + buf * kBBytes : lds + buf * kABytes;
+  const uint32_t soff = (uint32_t)k0 * (uint32_t)(ld * 2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < j0 || j >= j1) continue;
+    const int kr = 2 * (wave * 8 + j) + (lane >> 5);
+    const int c8 = 8 * kmaj_chunk(kr, lane & 31);
+    const uint32_t off = c0 + c8 < lim ? (uint32_t)kr * (uint32_t)(ld * 2) + (uint32_t)(c0 + c8) * 2 : kOob;
+    lds_dma16(rs, base + (wave * 8 + j) * 1024, off, soff);
+  }
+}
+
+__device__ __forceinline__ void wgrad_store(const WgradTile& w, int wm, int wn, int lane,
+                                            const f32x16 (&acc)[4][4]) {
+  const int lr = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = w.m0 + a_row_of(wm, i, false) + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (m >= w.M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = w.n0 + b_row_of<false>(wn, j) + lr;
+        if (n < w.N) w.C[(int64_t)m * w.N + n] = acc[i][j][r];
+      }
+    }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
 // ------------------------------------------------------------ weight gradients
 // Group g: C_g[m][n] = sum_r A[r][m] * B[r][n] over the group's rows
 // r = padded[g] .. padded[g] + counts[g] - 1 (read on the device), with the
@@ -801,46 +881,27 @@ hipError_t launch(bool gate_up, const GroupedGemm& g, hipStream_t s) {
 // no rows stores zeros.
 __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  const int64_t per_group = p.tiles_m * p.tiles_n;
-  const int g = (int)(blockIdx.x / per_group);
-  const int64_t rem = blockIdx.x - (int64_t)g * per_group;
-  const int mt = (int)(rem / p.tiles_n), nt = (int)(rem % p.tiles_n);
-  const bool shared = g >= p.E;
-  const int M = shared ? p.M_shared : p.M_routed;
-  const int N = shared ? p.N_shared : p.N_routed;
-  const int m0 = mt * BM, n0 = nt * BN;
-  if (m0 >= M || n0 >= N) return;
-  float* C = shared ? p.C_shared : p.C_routed + (int64_t)g * M * N;
-  const int64_t k0g = p.padded[g];
-  const int K = p.counts[g];  // the group's rows
-
+  const WgradTile w = wgrad_tile(p, blockIdx.x);
+  if (!w.valid) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, kh = lane >> 5;
   f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  if (K > 0) {
+  zero_acc(acc);
+  if (w.K > 0) {
     // the group's rows only: reads past them (the K tail) return zeros
     const __amdgpu_buffer_rsrc_t rsA =
-        make_rsrc(p.A + k0g * p.lda, (uint32_t)((int64_t)K * p.lda * 2));
+        make_rsrc(p.A + w.k0g * p.lda, (uint32_t)((int64_t)w.K * p.lda * 2));
     const __amdgpu_buffer_rsrc_t rsB =
-        make_rsrc(p.B + k0g * p.ldb, (uint32_t)((int64_t)K * p.ldb * 2));
-    // load j of a wave writes k-rows 2 (wave*8 + j) and + 1 of a stage; lane
-    // i carries k-row +i/32 and chunk position i % 32 (see kmaj_chunk)
+        make_rsrc(p.B + w.k0g * p.ldb, (uint32_t)((int64_t)w.K * p.ldb * 2));
+    // load slots as in wgrad_issue, their offsets computed once
     uint32_t offA[8], offB[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kr = 2 * (wave * 8 + j) + (lane >> 5);
       const int c8 = 8 * kmaj_chunk(kr, lane & 31);
-      offA[j] = m0 + c8 < M ? (uint32_t)kr * (uint32_t)(p.lda * 2) + (uint32_t)(m0 + c8) * 2 : kOob;
-      offB[j] = n0 + c8 < N ? (uint32_t)kr * (uint32_t)(p.ldb * 2) + (uint32_t)(n0 + c8) * 2 : kOob;
+      offA[j] = w.m0 + c8 < w.M ? (uint32_t)kr * (uint32_t)(p.lda * 2) + (uint32_t)(w.m0 + c8) * 2 : kOob;
+      offB[j] = w.n0 + c8 < w.N ? (uint32_t)kr * (uint32_t)(p.ldb * 2) + (uint32_t)(w.n0 + c8) * 2 : kOob;
     }
     auto issue = [&](bool isB, int stage, int buf, int j0, int j1) {
       const int k0 = stage * BK;
@@ -855,20 +916,56 @@ __global__ __launch_bounds__(256) void moe_gemm_wgrad_kernel(WgradGemm p) {
     auto issue_a = [&](int stage, int buf, int j0, int j1) { issue(false, stage, buf, j0, j1); };
     auto issue_b = [&](int stage, int buf, int j0, int j1) { issue(true, stage, buf, j0, j1); };
     k_loop<false, 4, false, decltype(issue_a), decltype(issue_b), true, true>(
-        lds, 0, (K + BK - 1) / BK, wm, wn, false, lane, issue_a, issue_b, acc);
+        lds, 0, (w.K + BK - 1) / BK, wm, wn, false, lane, issue_a, issue_b, acc);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + a_row_of(wm, i, false) + 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (m >= M) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + b_row_of<false>(wn, j) + lr;
-        if (n < N) C[(int64_t)m * N + n] = acc[i][j][r];
+  wgrad_store(w, wm, wn, lane, acc);
+}
+
+// The same products when every group has at most 64 rows (a token picks an
+// expert once, so T <= 64 guarantees it): one K stage per tile.  With 256
+// accumulators per lane a CU runs one workgroup, which would wait for each
+// tile's loads with nothing else to do; here a workgroup walks tiles
+// blockIdx.x, + gridDim.x, ... and issues the next tile's stage into the other
+// LDS buffer before storing the current tile, so the loads fly under the
+// stores.
+__global__ __launch_bounds__(256) void moe_gemm_wgrad_one_stage_kernel(WgradGemm p) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int64_t total = (int64_t)p.G * p.tiles_m * p.tiles_n;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  auto no_issue = [](int, int, int, int) {};
+  f32x16 acc[4][4];
+  int64_t t = blockIdx.x;
+  int buf = 0;
+  if (t < total) {
+    const WgradTile w = wgrad_tile(p, t);
+    if (w.valid && w.K > 0) {
+      wgrad_issue(p, w, lds, false, 0, 0, 0, 8, wave, lane);
+      wgrad_issue(p, w, lds, true, 0, 0, 0, 8, wave, lane);
+    }
+  }
+  for (; t < total; t += gridDim.x) {
+    const WgradTile w = wgrad_tile(p, t);
+    zero_acc(acc);
+    if (w.valid && w.K > 0)  // its stage is in buffer buf (issued one tile earlier)
+      k_loop<false, 4, false, decltype(no_issue), decltype(no_issue), true, true, true>(
+          lds + buf * kABytes, 0, 1, wm, wn, false, lane, no_issue, no_issue, acc);
+    // every wave is done reading this tile's stage (and the one before, in
+    // the other buffer) before the next tile's loads go there
+    __syncthreads();
+    const int64_t tn = t + gridDim.x;
+    if (tn < total) {
+      const WgradTile wn_ = wgrad_tile(p, tn);
+      if (wn_.valid && wn_.K > 0) {
+        wgrad_issue(p, wn_, lds, false, 0, buf ^ 1, 0, 8, wave, lane);
+        wgrad_issue(p, wn_, lds, true, 0, buf ^ 1, 0, 8, wave, lane);
       }
     }
+    if (w.valid) wgrad_store(w, wm, wn, lane, acc);
+    buf ^= 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be writing LDS at exit
 }
 
 }  // namespace
@@ -877,9 +974,19 @@ hipError_t launch_gemm_wgrad(const WgradGemm& g, hipStream_t s) {
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)moe_gemm_wgrad_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (attr != hipSuccess) return attr;
+  static const hipError_t attr1 =
+      hipFuncSetAttribute((const void*)moe_gemm_wgrad_one_stage_kernel,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (attr1 != hipSuccess) return attr1;
   const int64_t blocks = (int64_t)g.G * g.tiles_m * g.tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_gemm_wgrad_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes, s, g);
+  if (g.one_stage_ctas > 0) {
+    const int64_t grid = blocks < g.one_stage_ctas ? blocks : g.one_stage_ctas;
+    hipLaunchKernelGGL(moe_gemm_wgrad_one_stage_kernel, dim3((unsigned)grid), dim3(256), kLdsBytes, s,
+                       g);
+  } else {
+    hipLaunchKernelGGL(moe_gemm_wgrad_kernel, dim3((unsigned)blocks), dim3(256), kLdsBytes, s, g);
+  }
   return hipGetLastError();
 }
 

@@ -104,6 +104,9 @@ struct WgradGemm {
   float* C_routed;  // [E][M_routed][N_routed]
   float* C_shared;  // [M_shared][N_shared]
   int64_t tiles_m, tiles_n;  // 256 x 256 tiles per group (max over both kinds)
+  // > 0 only when every group has at most 64 rows: that many workgroups walk
+  // the tiles, each issuing the next tile's loads before storing the current one
+  int one_stage_ctas;
 };
 hipError_t launch_gemm_wgrad(const WgradGemm& g, hipStream_t s);
 

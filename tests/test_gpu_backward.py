@@ -80,6 +80,8 @@ CASES = [
     (700, 512, 16, 4, 256, 256, False),  # 256-row tiles with the shared expert
     (32, 1024, 8, 2, 768, 256, False),   # 16-row tiles, K = 1024 and 1536: several K chunks per wave
     (200, 1024, 16, 2, 640, 0, True),    # 32-row tiles, K = 1024 and 1280
+    # T <= 64: the weight gradients' one-stage kernel, several tiles per workgroup
+    (64, 2048, 16, 2, 1024, 0, False),
 ]
 
 
@@ -204,16 +206,19 @@ def test_backward_saved_twice_is_deterministic():
         assert torch.equal(a[name], b[name]), name
 
 
-@pytest.mark.parametrize("counts", [
-    [257, 300, 511, 512, 256, 1, 0, 700],  # 256-row tiles
-    [16, 17, 1, 0, 15, 32, 8, 3],          # 16-row tiles
-    [33, 32, 64, 1, 0, 40, 31, 47],        # 32-row tiles
+@pytest.mark.parametrize("counts,D,F", [
+    ([257, 300, 511, 512, 256, 1, 0, 700], 256, 320),  # 256-row tiles
+    ([16, 17, 1, 0, 15, 32, 8, 3], 256, 320),          # 16-row tiles
+    ([33, 32, 64, 1, 0, 40, 31, 47], 256, 320),        # 32-row tiles
+    # T = 64: the one-stage weight gradients, 576 tiles over 256 workgroups, with
+    # empty groups' tiles between others in a workgroup's sequence
+    ([9, 0, 13, 1, 0, 7, 20, 14], 2048, 1024),
 ])
-def test_backward_tile_boundaries(counts):
+def test_backward_tile_boundaries(counts, D, F):
     """The backward's tiles at group sizes around tile boundaries (k = 1, exact
     counts, tokens shuffled), with a shared expert.  With k = 1 the routing weight
     is 1 and the router gradient is exactly 0."""
-    T, D, F, E = sum(counts), 256, 320, len(counts)
+    T, E = sum(counts), len(counts)
     s = W.Shape(T=T, D=D, E=E, k=1, F=F, Fs=64)
     inp = W.make_inputs(s, seed=12)
     order = np.random.default_rng(6).permutation(T)
