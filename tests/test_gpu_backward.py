@@ -80,6 +80,7 @@ CASES = [
     (700, 512, 16, 4, 256, 256, False),  # 256-row tiles with the shared expert
     (32, 1024, 8, 2, 768, 256, False),   # 16-row tiles, K = 1024 and 1536: several K chunks per wave
     (200, 1024, 16, 2, 640, 0, True),    # 32-row tiles, K = 1024 and 1280
+    (200, 200, 16, 2, 136, 64, False),   # 32-row tiles, ragged K and N, shared expert
     # T <= 64: the weight gradients' one-stage kernel, several tiles per workgroup
     (64, 2048, 16, 2, 1024, 0, False),
 ]
