@@ -28,9 +28,9 @@
 //    value), and each output column's sum is multiplied by its row's scale
 //    after the reduction: sum_k x_k (q_k s) = s sum_k x_k q_k.  Half the
 //    weight bytes of bf16, for the same MFMAs.
-//  - The backward pass's products with the weights as stored (contracting
-//    over their row index) stage the weights through LDS instead; see the
-//    K-major tile below.
+//  - bf16 weights with the wide column tiles, and the backward pass's
+//    products with the weights as stored (contracting over their row index),
+//    stage the weights through LDS instead; see the staged tile below.
 #include <type_traits>
 
 #include "device.hpp"
@@ -64,6 +64,48 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
   const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Epilogue of a decode tile: lane (c, gq) holds rows 4 gq + r, column c of
+// each 16x16 tile.  Gate/up: column groups j < NG/2 are gate, j + NG/2 the
+// matching up columns; H = bf16(SiLU(g) u), and g | u of the valid rows when
+// kept for the backward pass.  Down: fp32 rows.
+template <bool GATE_UP, int MT, int NG>
+__device__ __forceinline__ void store_tile(const GroupedGemm& p, const f32x4 (&acc)[MT][NG], int64_t row0,
+                                           int n0, int N, int valid_rows, int c, int gq) {
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t grow = row0 + i * 16 + 4 * gq + r;
+      if (GATE_UP) {
+        bf16_t* H = reinterpret_cast<bf16_t*>(p.C);
+#pragma unroll
+        for (int j = 0; j < NG / 2; ++j) {
+          const int f = n0 + j * 16 + c;
+          if (f < N) H[grow * p.ldc + f] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + NG / 2][r]);
+        }
+        if (p.gu_out && i * 16 + 4 * gq + r < valid_rows) {  // g and u kept for the backward pass
+          bf16_t* gr = reinterpret_cast<bf16_t*>(p.gu_out) + grow * p.ld_gu;
+#pragma unroll
+          for (int j = 0; j < NG / 2; ++j) {
+            const int f = n0 + j * 16 + c;
+            if (f < N) {
+              gr[f] = f32_to_bf16(acc[i][j][r]);
+              gr[N + f] = f32_to_bf16(acc[i][j + NG / 2][r]);
+            }
+          }
+        }
+      } else {
+        float* Y = reinterpret_cast<float*>(p.C);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+          const int n = n0 + j * 16 + c;
+          if (n < N) Y[grow * p.ldc + n] = acc[i][j][r];
+        }
+      }
+    }
+  }
 }
 
 template <bool GATE_UP, int MT, int NG, int kWaves, int kUnroll, bool FP8>
@@ -257,40 +299,7 @@ __device__ __forceinline__ void decode_tile(const GroupedGemm& p) {
     }
   }
 
-  // ---- epilogue: lane (c, gq) holds rows 4*gq + r, column c of each 16x16 tile
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t grow = row0 + i * 16 + 4 * gq + r;
-      if (GATE_UP) {
-        bf16_t* H = reinterpret_cast<bf16_t*>(p.C);
-#pragma unroll
-        for (int j = 0; j < NG / 2; ++j) {
-          const int f = n0 + j * 16 + c;
-          if (f < N) H[grow * p.ldc + f] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + NG / 2][r]);
-        }
-        if (p.gu_out && i * 16 + 4 * gq + r < valid_rows) {  // g and u kept for the backward pass
-          bf16_t* gr = reinterpret_cast<bf16_t*>(p.gu_out) + grow * p.ld_gu;
-#pragma unroll
-          for (int j = 0; j < NG / 2; ++j) {
-            const int f = n0 + j * 16 + c;
-            if (f < N) {
-              gr[f] = f32_to_bf16(acc[i][j][r]);
-              gr[N + f] = f32_to_bf16(acc[i][j + NG / 2][r]);
-            }
-          }
-        }
-      } else {
-        float* Y = reinterpret_cast<float*>(p.C);
-#pragma unroll
-        for (int j = 0; j < NG; ++j) {
-          const int n = n0 + j * 16 + c;
-          if (n < N) Y[grow * p.ldc + n] = acc[i][j][r];
-        }
-      }
-    }
-  }
+  store_tile<GATE_UP, MT, NG>(p, acc, row0, n0, N, valid_rows, c, gq);
 }
 
 // 16-row column groups per tile (gate/up: half gate, half up), waves splitting
@@ -315,7 +324,7 @@ template <bool FP8, bool NARROW> constexpr int ng_down() {
 }
 template <bool FP8> constexpr int unroll() { return FP8 ? kUnrFp8 : kUnr; }
 
-// ---------------------------------------------------------------- K-major B
+// ------------------------------------------------------- weights through LDS
 // The backward pass's row products with W_down and W_gate_up as they are
 // stored: C[r][n] = sum_k A[r][k] B[k][n], B being the group's [K][N] slab
 // (k-row k holds the N weights that multiply column k of A).  An MFMA operand
@@ -325,6 +334,8 @@ template <bool FP8> constexpr int unroll() { return FP8 ? kUnrFp8 : kUnr; }
 // A wave owns a ring of stages, so the K loop has no workgroup barrier:
 // the later chunks stream in while one is multiplied.  The waves
 // split K by chunks as above, and their sums are added in the same order.
+// The forward's bf16 products (row-major weights) use the same staging; see
+// decode_tile_staged.
 constexpr int kKmBBytes = 64 * 128;  // a stage's B: 64 k-rows x 64 columns, bf16
 template <int MT> constexpr int km_a_bytes() { return 16 * MT * 128; }
 template <int MT> constexpr int km_stage_bytes() { return km_a_bytes<MT>() + kKmBBytes; }
@@ -350,9 +361,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int MT>
-__device__ __forceinline__ void decode_tile_kmajor(const GroupedGemm& p, char* lds) {
-  constexpr int NG = 4, BMD = 16 * MT, NOUT = 16 * NG;
+// KMAJ = false: the forward's products with row-major weights ([N][K] per
+// group; gate/up: 32 gate rows and the matching 32 up rows), staged the same
+// way: a stage's B is 64 weight rows x 64 k, laid out like A, read with plain
+// 16-byte LDS reads.
+template <int MT, bool KMAJ, bool GATE_UP>
+__device__ __forceinline__ void decode_tile_staged(const GroupedGemm& p, char* lds) {
+  static_assert(!(KMAJ && GATE_UP), "K-major weights: rows x weight products only");
+  constexpr int NG = 4, BMD = 16 * MT, NOUT = GATE_UP ? 16 * NG / 2 : 16 * NG;
   constexpr int SB = km_stage_bytes<MT>(), AB = km_a_bytes<MT>(), S = km_stages<MT>();
   constexpr int NA = AB / 1024, NB = kKmBBytes / 1024, V = NA + NB;  // 1-KB loads per chunk
 
@@ -373,27 +389,44 @@ __device__ __forceinline__ void decode_tile_kmajor(const GroupedGemm& p, char* l
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, gq = lane >> 4;
 
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A + row0 * p.lda, (uint32_t)(BMD * p.lda * 2));
+  const __amdgpu_buffer_rsrc_t rsA = GATE_UP ? make_rsrc(p.A, (uint32_t)p.a_bytes)
+                                             : make_rsrc(p.A + row0 * p.lda, (uint32_t)(BMD * p.lda * 2));
+  const int64_t slab = (int64_t)(GATE_UP ? 2 : 1) * K * N * 2;  // the group's weight bytes
   const char* Bbytes = shared ? static_cast<const char*>(p.B_shared)
-                              : static_cast<const char*>(p.B_routed) + (int64_t)g * K * N * 2;
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Bbytes, (uint32_t)((int64_t)K * N * 2));
+                              : static_cast<const char*>(p.B_routed) + (int64_t)g * slab;
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(Bbytes, (uint32_t)slab);
   // LDS-direct load b of a stage: lane i writes 16 bytes at 16 i of its 1-KB
   // block, i.e. row (A) or k-row (B) 8 b + i / 8, chunk position i % 8.
   // Offsets at k = 0; out-of-range ones (rows past the group, columns past N)
   // stay out of range when k0's bytes are added.
   const int ir = lane >> 3, ip = lane & 7;
   uint32_t aoff[NA], boff[NB];
-  int akc[NA];  // first k of the A chunk, inside the 64-wide K chunk
+  int akc[NA], bkc[NB];  // first k of the chunk, inside the 64-wide K chunk (row-major operands)
 #pragma unroll
   for (int b = 0; b < NA; ++b) {
     const int r = 8 * b + ir, ch = ip ^ km_a_swz(r);
     akc[b] = 8 * ch;
-    aoff[b] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + ch * 16 : kOob;
+    if (GATE_UP) {  // gathered x rows
+      const int t = r < valid_rows ? p.row_token[row0 + r] : -1;
+      aoff[b] = t >= 0 ? (uint32_t)t * (uint32_t)(p.lda * 2) + ch * 16 : kOob;
+    } else {
+      aoff[b] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + ch * 16 : kOob;
+    }
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int r = 8 * b + ir, n = n0 + 8 * (ip ^ km_b_swz(r));
-    boff[b] = n < N ? (uint32_t)r * (uint32_t)(N * 2) + n * 2 : kOob;
+    const int r = 8 * b + ir;
+    if (KMAJ) {
+      const int n = n0 + 8 * (ip ^ km_b_swz(r));
+      bkc[b] = 0;
+      boff[b] = n < N ? (uint32_t)r * (uint32_t)(N * 2) + n * 2 : kOob;
+    } else {  // weight row r of the tile: gate/up rows 0-31 gate, 32-63 up
+      const int ch = ip ^ km_a_swz(r);
+      const int f = GATE_UP ? n0 + (r & 31) : n0 + r;
+      const int brow = GATE_UP ? (r >> 5) * N + f : f;
+      bkc[b] = 8 * ch;
+      boff[b] = f < N ? (uint32_t)brow * (uint32_t)(K * 2) + ch * 16 : kOob;
+    }
   }
   // Reads.  MFMA step h of a chunk takes k = 32 h + 8 gq + (0 .. 7) in lane
   // (c, gq).  A: row 16 i + c, chunk 4 h + gq.  B: a transposing read gives
@@ -434,9 +467,13 @@ __device__ __forceinline__ void decode_tile_kmajor(const GroupedGemm& p, char* l
     for (int b = 0; b < NA; ++b)
       lds_dma16(rsA, st + b * 1024, k0 + akc[b] < K ? aoff[b] + 2 * k0 : kOob, 0);
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      lds_dma16(rsB, st + AB + b * 1024,
-                k0 + 8 * b + ir < K ? boff[b] + (uint32_t)k0 * (uint32_t)(N * 2) : kOob, 0);
+    for (int b = 0; b < NB; ++b) {
+      if (KMAJ)
+        lds_dma16(rsB, st + AB + b * 1024,
+                  k0 + 8 * b + ir < K ? boff[b] + (uint32_t)k0 * (uint32_t)(N * 2) : kOob, 0);
+      else
+        lds_dma16(rsB, st + AB + b * 1024, k0 + bkc[b] < K ? boff[b] + 2 * k0 : kOob, 0);
+    }
   };
   auto read_tr = [](const char* q) {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -469,7 +506,14 @@ __device__ __forceinline__ void decode_tile_kmajor(const GroupedGemm& p, char* l
 #pragma unroll
       for (int i = 0; i < MT; ++i) a[i] = *reinterpret_cast<const bf16x8*>(st + rdA[i][h]);
 #pragma unroll
-      for (int j = 0; j < NG; ++j) b[j] = read_tr(st + rdB[j] + h * 32 * 128);
+      for (int j = 0; j < NG; ++j) {
+        if (KMAJ) {
+          b[j] = read_tr(st + rdB[j] + h * 32 * 128);
+        } else {  // weight row 16 j + c, chunk 4 h + gq
+          const int r = 16 * j + c;
+          b[j] = *reinterpret_cast<const bf16x8*>(st + AB + r * 128 + 16 * ((4 * h + gq) ^ km_a_swz(r)));
+        }
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -501,19 +545,7 @@ __device__ __forceinline__ void decode_tile_kmajor(const GroupedGemm& p, char* l
 #pragma unroll
       for (int j = 0; j < NG; ++j) acc[i][j] += red[((w * MT + i) * NG + j) * 64 + lane];
 
-  // ---- epilogue: lane (c, gq) holds rows 4 gq + r, column c of each 16x16 tile
-  float* Y = reinterpret_cast<float*>(p.C);
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t grow = row0 + i * 16 + 4 * gq + r;
-#pragma unroll
-      for (int j = 0; j < NG; ++j) {
-        const int n = n0 + j * 16 + c;
-        if (n < N) Y[grow * p.ldc + n] = acc[i][j][r];
-      }
-    }
+  store_tile<GATE_UP, MT, NG>(p, acc, row0, n0, N, valid_rows, c, gq);
 }
 
 template <int MT, bool FP8, bool NARROW>
@@ -547,18 +579,59 @@ hipError_t launch_mt(bool gate_up, GroupedGemm g, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int MT>
+hipError_t launch_staged(bool gate_up, const GroupedGemm& g0, hipStream_t s);
+
 template <int MT, bool FP8>
 hipError_t launch_width(bool gate_up, const GroupedGemm& g, hipStream_t s) {
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
   const int nout = column_tile<FP8, false>(gate_up);
   const bool narrow = g.busy_tiles * ((nmax + nout - 1) / nout) < kFillBlocks;
-  return narrow ? launch_mt<MT, FP8, true>(gate_up, g, s) : launch_mt<MT, FP8, false>(gate_up, g, s);
+  if (narrow) return launch_mt<MT, FP8, true>(gate_up, g, s);
+  if (!FP8) return launch_staged<MT>(gate_up, g, s);
+  return launch_mt<MT, FP8, false>(gate_up, g, s);
 }
 
 template <int MT>
 __global__ __launch_bounds__(kKw * 64) void moe_gemm_rows_kmajor_decode_kernel(GroupedGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  decode_tile_kmajor<MT>(p, lds);
+  decode_tile_staged<MT, true, false>(p, lds);
+}
+
+template <int MT, bool GATE_UP>
+__global__ __launch_bounds__(kKw * 64) void moe_gemm_staged_decode_kernel(GroupedGemm p) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  decode_tile_staged<MT, false, GATE_UP>(p, lds);
+}
+
+// bf16 weights, wide column tiles: the weights stream through LDS
+template <int MT>
+hipError_t launch_staged(bool gate_up, const GroupedGemm& g0, hipStream_t s) {
+  static const hipError_t a0 =
+      hipFuncSetAttribute((const void*)moe_gemm_staged_decode_kernel<MT, true>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, km_lds_bytes<MT>());
+  static const hipError_t a1 =
+      hipFuncSetAttribute((const void*)moe_gemm_staged_decode_kernel<MT, false>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, km_lds_bytes<MT>());
+  if (a0 != hipSuccess) return a0;
+  if (a1 != hipSuccess) return a1;
+  const int64_t brows = gate_up ? 2 : 1;
+  if (brows * g0.K_routed * g0.N_routed * 2 >= (int64_t(1) << 31) ||
+      brows * g0.K_shared * g0.N_shared * 2 >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  GroupedGemm g = g0;
+  const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
+  const int nout = gate_up ? 32 : 64;
+  g.n_tiles_n = (nmax + nout - 1) / nout;
+  const int64_t blocks = g.max_tiles * g.n_tiles_n;
+  if (blocks == 0) return hipSuccess;
+  if (gate_up)
+    hipLaunchKernelGGL((moe_gemm_staged_decode_kernel<MT, true>), dim3((unsigned)blocks),
+                       dim3(kKw * 64), km_lds_bytes<MT>(), s, g);
+  else
+    hipLaunchKernelGGL((moe_gemm_staged_decode_kernel<MT, false>), dim3((unsigned)blocks),
+                       dim3(kKw * 64), km_lds_bytes<MT>(), s, g);
+  return hipGetLastError();
 }
 
 template <int MT>
