@@ -6,95 +6,163 @@
 // Mezcla de Expertos)", section 3 step 3 (a token's vector is duplicated to
 // each chosen expert).
 //
-// One workgroup per group g (E routed experts, plus the shared-expert group).
-// Every workgroup builds the full expert histogram in LDS (integer counts, so
-// the atomics' order does not matter) and derives offsets and padded offsets;
-// workgroup g then walks the assignments in ascending order and compacts the
-// ones routed to g with a ballot/popcount rank, so the output is the stable
-// order by assignment index and bitwise reproducible.
+// Output order: the assignments of group g in ascending assignment index
+// (stable), so the result is bitwise reproducible; no atomic decides a
+// position.  Two kernels compute it:
+//  - few assignments (A <= kSmallA, the decode sizes): one workgroup holds
+//    every id in LDS.  Each wave ranks its 64 lanes among the lanes of the
+//    same expert (one ballot per distinct expert), per-wave counts give each
+//    wave's base inside a group, and a wave-wide scan gives the offsets.
+//  - many assignments: one workgroup per group; each builds the full
+//    histogram in LDS (integer counts, so the atomics' order does not
+//    matter), scans it, and compacts the assignments of its own group with a
+//    ballot/popcount rank while walking them in ascending order.
 #include "device.hpp"
 #include "launch.hpp"
-#include "topk.hpp"  // ranks_before
 
 namespace moe {
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kMaxG = 257;        // 256 routed experts + the shared one
+constexpr int kSmallA = kThreads; // one assignment per thread of the one-workgroup path
+constexpr int kScanPer = 5;       // groups per lane of the wave-wide scan (64 * 5 >= kMaxG)
+
+// Exclusive prefix sums of v[0..n) (n <= 64 * kScanPer), each value first
+// rounded up to a multiple of bm (bm = 1: plain counts), into out[0..n];
+// out[n] is the total.  Called by all 64 lanes of one wave.
+__device__ __forceinline__ void wave_scan(const int* v, int n, int bm, int* out, int lane) {
+  int loc[kScanPer];
+  int s = 0;
+#pragma unroll
+  for (int q = 0; q < kScanPer; ++q) {
+    const int i = lane * kScanPer + q;
+    const int c = i < n ? (v[i] + bm - 1) / bm * bm : 0;
+    loc[q] = s;
+    s += c;
+  }
+  int inc = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  const int excl = inc - s;
+#pragma unroll
+  for (int q = 0; q < kScanPer; ++q) {
+    const int i = lane * kScanPer + q;
+    if (i < n) out[i] = excl + loc[q];
+  }
+  if (lane == 63) out[n] = inc;
+}
+
+// Rows that no assignment fills: padding rows read as token -1, the shared
+// expert's rows hold tokens 0 .. T-1 in order; and the group of every tile.
+// Row r belongs to the last group g with pad[g] <= r (empty groups have
+// pad[g] == pad[g + 1], so the search skips them).
+__device__ __forceinline__ void fill_rows(const int* hist, const int* pad, int G, int E, int BM,
+                                          int32_t* row_token, int32_t* tile_group, int tid) {
+  const int rows = pad[G];
+  for (int r = tid; r < rows; r += kThreads) {
+    int lo = 0, hi = G - 1;  // pad[lo] <= r < pad[hi + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pad[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    const int j = r - pad[lo];
+    if (j >= hist[lo]) row_token[r] = -1;
+    else if (lo == E) row_token[r] = j;
+    if (j % BM == 0) tile_group[r / BM] = lo;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void moe_align_small_kernel(
+    const int32_t* __restrict__ ids, int A, int k, int E, int id_base, int BM, int shared_rows,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ padded,
+    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ tile_group,
+    int32_t* __restrict__ n_tiles) {
+  __shared__ int s_ids[kSmallA];
+  __shared__ int wcnt[kWaves][kMaxG];  // per-wave counts, then each wave's base in a group
+  __shared__ int hist[kMaxG];
+  __shared__ int s_off[kMaxG + 1];
+  __shared__ int s_pad[kMaxG + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = E + (shared_rows > 0 ? 1 : 0);
+  for (int i = tid; i < kWaves * kMaxG; i += kThreads) (&wcnt[0][0])[i] = 0;
+
+  for (int a = tid; a < A; a += kThreads) s_ids[a] = ids[a];
+  __syncthreads();
+
+  // rank of assignment a = tid among the lanes of its wave routed to the same
+  // group (ascending lane order), and the wave's count of each group
+  const int a = tid;
+  const int e = a < A ? s_ids[a] - id_base : -1;
+  const bool valid = a < A && e >= 0 && e < E;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank = 0;
+  uint64_t pending = __ballot(valid);
+  while (pending) {
+    const int leader = (int)__builtin_ctzll(pending);
+    const int el = __builtin_amdgcn_readlane(e, leader);
+    const bool mine = valid && e == el;
+    const uint64_t m = __ballot(mine);
+    if (mine) rank = __popcll(m & below);
+    if (lane == 0) wcnt[wave][el] = __popcll(m);
+    pending &= ~m;
+  }
+  __syncthreads();
+  // group totals; wcnt becomes each wave's exclusive base inside the group
+  for (int i = tid; i < G; i += kThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = wcnt[w][i];
+      wcnt[w][i] = run;
+      run += c;
+    }
+    hist[i] = (i == E) ? shared_rows : run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    wave_scan(hist, G, 1, s_off, lane);
+    wave_scan(hist, G, BM, s_pad, lane);
+  }
+  __syncthreads();
+
+  if (valid) {
+    const int r = wcnt[wave][e] + rank;
+    sorted_assign[s_off[e] + r] = a;
+    row_of[a] = s_pad[e] + r;
+    row_token[s_pad[e] + r] = a / k;
+  } else if (a < A) {
+    row_of[a] = -1;  // an id outside the held experts gets no row
+  }
+  for (int i = tid; i < G; i += kThreads) counts[i] = hist[i];
+  for (int i = tid; i <= G; i += kThreads) {
+    offsets[i] = s_off[i];
+    padded[i] = s_pad[i];
+  }
+  if (tid == 0) n_tiles[0] = s_pad[G] / BM;
+  fill_rows(hist, s_pad, G, E, BM, row_token, tile_group, tid);
+}
 
 __global__ __launch_bounds__(kThreads) void moe_align_kernel(
     const int32_t* __restrict__ ids, int A, int k, int E, int id_base, int BM, int shared_rows,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ padded,
     int32_t* __restrict__ sorted_assign, int32_t* __restrict__ row_of,
     int32_t* __restrict__ row_token, int32_t* __restrict__ tile_group,
-    int32_t* __restrict__ n_tiles, RouteFinish fin) {
-  __shared__ int hist[258];
-  __shared__ int s_ids[kSmallRouteT * 8];
-  __shared__ int s_off[258];
-  __shared__ int s_pad[258];
+    int32_t* __restrict__ n_tiles) {
+  __shared__ int hist[kMaxG];
+  __shared__ int s_off[kMaxG + 1];
+  __shared__ int s_pad[kMaxG + 1];
   __shared__ int wave_tot[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = E + (shared_rows > 0 ? 1 : 0);
   const int g = blockIdx.x;
-
-  if (fin.partial) {
-    // Few tokens: finish the routing here.  Every workgroup adds the partial
-    // logits of all T <= kSmallRouteT tokens (part order, then the bias),
-    // picks each token's top-k (E <= kSmallRouteE) and keeps the ids in LDS;
-    // workgroup 0 also stores ids and weights.
-    // [T][EL + 1] logits, then (selection-only bias) [T][EL + 1] top-k keys
-    extern __shared__ float lg[];
-    const int T = A / k, EL = fin.E;
-    float* const key = fin.sel ? lg + T * (EL + 1) : lg;
-    for (int idx = tid; idx < T * EL; idx += kThreads) {
-      const int t = idx / EL, e = idx - t * EL;
-      const float* src = fin.partial + (int64_t)t * EL + e;
-      const int64_t stride = (int64_t)T * EL;
-      float v = 0.f;
-      for (int q0 = 0; q0 < fin.P; q0 += 16) {
-        float pv[16];  // every load of the group in flight before the in-order sum
-#pragma unroll
-        for (int q = 0; q < 16; ++q) pv[q] = q0 + q < fin.P ? src[(q0 + q) * stride] : 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (q0 + q < fin.P) v = (q0 + q == 0) ? pv[q] : v + pv[q];
-      }
-      if (fin.bias) v += fin.bias[e];
-      lg[t * (EL + 1) + e] = v;
-      if (fin.sel) key[t * (EL + 1) + e] = v + fin.sel[e];
-    }
-    __syncthreads();
-    // slot of every (token, expert): the number of the token's keys that
-    // rank before its own (value descending, ties to the lower index); one
-    // thread per pair, so all tokens are ranked at once
-    for (int idx = tid; idx < T * EL; idx += kThreads) {
-      const int t = idx / EL, e = idx - t * EL;
-      const float* row = key + t * (EL + 1);
-      const float v = row[e];
-      int rank = 0;
-      for (int j = 0; j < EL; ++j) rank += ranks_before(row[j], j, v, e) ? 1 : 0;
-      if (rank < k) s_ids[t * k + rank] = e;
-    }
-    __syncthreads();
-    if (g == 0) {  // softmax over the chosen logits, adding exp(l - l_max) in slot order
-      for (int idx = tid; idx < T * k; idx += kThreads) {
-        const int t = idx / k, q = idx - t * k;
-        const float* row = lg + t * (EL + 1);
-        float vmax = row[s_ids[t * k]];
-        for (int j = 1; j < k; ++j) vmax = fmaxf(vmax, row[s_ids[t * k + j]]);
-        float tot = 0.f, mine = 0.f;
-        for (int j = 0; j < k; ++j) {
-          const float ex = expf(row[s_ids[t * k + j]] - vmax);
-          tot += ex;
-          if (j == q) mine = ex;
-        }
-        fin.ids[idx] = s_ids[idx];
-        fin.wts[idx] = mine / tot;
-      }
-    }
-  }
   // group of assignment a (ids are global; this call holds experts id_base ..)
-  auto id_of = [&](int a) { return (fin.partial ? s_ids[a] : ids[a]) - id_base; };
+  auto id_of = [&](int a) { return ids[a] - id_base; };
 
   for (int i = tid; i < G; i += kThreads) hist[i] = (i == E) ? shared_rows : 0;
   __syncthreads();
@@ -103,16 +171,9 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
     if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0, p = 0;
-    for (int i = 0; i < G; ++i) {
-      s_off[i] = o;
-      s_pad[i] = p;
-      o += hist[i];
-      p += (hist[i] + BM - 1) / BM * BM;
-    }
-    s_off[G] = o;
-    s_pad[G] = p;
+  if (wave == 0) {
+    wave_scan(hist, G, 1, s_off, lane);
+    wave_scan(hist, G, BM, s_pad, lane);
   }
   __syncthreads();
   if (g == 0) {
@@ -168,23 +229,18 @@ __global__ __launch_bounds__(kThreads) void moe_align_kernel(
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int id_base, int BM, int shared_rows,
                         int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
                         int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
-                        const RouteFinish* fin, hipStream_t s) {
+                        hipStream_t s) {
   const int G = E + (shared_rows > 0 ? 1 : 0);
-  RouteFinish f{};
-  size_t lds = 0;
-  if (fin) {
-    if (T > kSmallRouteT || k > 8 || fin->E > kSmallRouteE) return hipErrorInvalidValue;
-    f = *fin;
-    lds = sizeof(float) * (size_t)T * (fin->E + 1) * (fin->sel ? 2 : 1);
-    // set once per process (a function-local static is initialised thread-safely)
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)moe_align_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)(sizeof(float) * 2 * kSmallRouteT * (kSmallRouteE + 1)));
-    if (attr != hipSuccess) return attr;
-  }
-  hipLaunchKernelGGL(moe_align_kernel, dim3(G), dim3(kThreads), lds, s, ids, T * k, k, E, id_base, BM,
-                     shared_rows, counts, offsets, padded, sorted_assign, row_of, row_token,
-                     tile_group, n_tiles, f);
+  if (G > kMaxG) return hipErrorInvalidValue;
+  const int64_t A = (int64_t)T * k;
+  if (A <= kSmallA)
+    hipLaunchKernelGGL(moe_align_small_kernel, dim3(1), dim3(kThreads), 0, s, ids, (int)A, k, E,
+                       id_base, BM, shared_rows, counts, offsets, padded, sorted_assign, row_of,
+                       row_token, tile_group, n_tiles);
+  else
+    hipLaunchKernelGGL(moe_align_kernel, dim3(G), dim3(kThreads), 0, s, ids, (int)A, k, E, id_base,
+                       BM, shared_rows, counts, offsets, padded, sorted_assign, row_of, row_token,
+                       tile_group, n_tiles);
   return hipGetLastError();
 }
 

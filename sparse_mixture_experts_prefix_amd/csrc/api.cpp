@@ -65,7 +65,7 @@ int64_t busy_tiles(const moe::Plan& P) {
 // gu_save (or NULL): keep g | u of every row, bf16 [cap][2 ldh] (training forward)
 int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, const float* wts,
                 float* y, void* ws, hipStream_t s, Marks mk = Marks{nullptr},
-                const moe::RouteFinish* fin = nullptr, uint16_t* gu_save = nullptr) {
+                uint16_t* gu_save = nullptr) {
   using namespace moe;
   int32_t* counts = at<int32_t>(ws, P.off_counts);
   int32_t* offsets = at<int32_t>(ws, P.off_offsets);
@@ -86,7 +86,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   }
 
   hipError_t e = launch_align(ids, (int)P.T, (int)P.k, (int)P.E_loc, (int)P.e0, P.BM, shared_rows, counts, offsets,
-                              padded, sorted, row_of, row_token, tile_group, n_tiles, fin, s);
+                              padded, sorted, row_of, row_token, tile_group, n_tiles, s);
   if (e == hipSuccess) e = mk.mark(2, s);
   if (e != hipSuccess) return hip_fail(e);
 
@@ -191,7 +191,7 @@ int run_backward(const moe::BwdPlan& B, const moe_shape* shape, const moe_weight
   hipError_t e = hipSuccess;
   if (!saved)
     e = launch_align(ids, T, k, E, 0, P.BM, Fs > 0 ? T : 0, counts, offsets, padded, sorted, row_of,
-                     row_token, tile_group, n_tiles, nullptr, s);
+                     row_token, tile_group, n_tiles, s);
   if (e == hipSuccess) e = launch_row_assign(row_of, (int)P.A, cap, row_assign, s);
   const int32_t* total = padded + G;  // rows in use
   if (e == hipSuccess) e = launch_gather_rows(w->x, false, row_token, total, cap, D, xr, s);
@@ -290,19 +290,36 @@ int moe_block_m(const moe_shape* shape) {
   return moe::choose_block_m(shape);
 }
 
-static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
-                        float* topk_w, void* workspace, size_t ws_bytes, void* stream,
-                        void* const* events, bool train = false) {
+}  // extern "C"
+
+// moe_forward's checks of everything but the workspace (MOE_OK: T == 0 or valid)
+int moe::check_forward_args(const moe_shape* shape, const moe_weights* w, const float* y,
+                            const int32_t* topk_ids, const float* topk_w) {
   moe::Plan P;
   int rc = moe::make_plan(shape, &P);
   if (rc) return rc;
   rc = moe::check_weights(shape, w, true);
   if (rc) return rc;
   if (P.T == 0) return MOE_OK;
-  if (!y || !workspace) return MOE_ERR_INVALID_ARG;
-  if (!moe::aligned16(y) || !moe::aligned16(workspace)) return MOE_ERR_ALIGNMENT;
+  if (!y) return MOE_ERR_INVALID_ARG;
+  if (!moe::aligned16(y)) return MOE_ERR_ALIGNMENT;
   if ((topk_ids && !moe::aligned16(topk_ids)) || (topk_w && !moe::aligned16(topk_w)))
     return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+extern "C" {
+
+static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
+                        float* topk_w, void* workspace, size_t ws_bytes, void* stream,
+                        void* const* events, bool train = false) {
+  int rc = moe::check_forward_args(shape, w, y, topk_ids, topk_w);
+  if (rc) return rc;
+  moe::Plan P;
+  moe::make_plan(shape, &P);
+  if (P.T == 0) return MOE_OK;
+  if (!workspace) return MOE_ERR_INVALID_ARG;
+  if (!moe::aligned16(workspace)) return MOE_ERR_ALIGNMENT;
   if (ws_bytes < (train ? P.total_train : P.total)) return MOE_ERR_WORKSPACE;
   uint16_t* gu_save = train ? at<uint16_t>(workspace, P.off_gusave) : nullptr;
   if (events)
@@ -316,23 +333,25 @@ static int forward_impl(const moe_shape* shape, const moe_weights* w, float* y, 
   const float* sel = shape->has_router_bias == MOE_ROUTER_BIAS_SELECT ? w->router_bias : nullptr;
   hipError_t e = mk.mark(0, s);
   if (P.T <= moe::kSmallRouteT && P.E <= moe::kSmallRouteE) {
-    // few tokens: partial logits over many workgroups, routing finished in align
+    // few tokens: partial logits over many workgroups, then one wave per token
     float* rpart = at<float>(workspace, P.off_rpart);
     if (e == hipSuccess)
       e = moe::launch_router_partial(static_cast<const uint16_t*>(w->x),
                                      static_cast<const uint16_t*>(w->w_g), (int)P.T, (int)P.D,
                                      (int)P.E, rpart, s);
+    if (e == hipSuccess)
+      e = moe::launch_route_finish(rpart, moe::router_parts(P.D), (int)P.T, (int)P.E, (int)P.k, bias,
+                                   sel, ids, wts, s);
     if (e == hipSuccess) e = mk.mark(1, s);
     if (e != hipSuccess) return hip_fail(e);
-    const moe::RouteFinish fin{rpart, moe::router_parts(P.D), (int)P.E, bias, sel, ids, wts};
-    return run_experts(P, w, ids, wts, y, workspace, s, mk, &fin, gu_save);
+    return run_experts(P, w, ids, wts, y, workspace, s, mk, gu_save);
   }
   if (e == hipSuccess)
     e = moe::launch_router(static_cast<const uint16_t*>(w->x), static_cast<const uint16_t*>(w->w_g),
                            bias, sel, (int)P.T, (int)P.D, (int)P.E, (int)P.k, ids, wts, s);
   if (e == hipSuccess) e = mk.mark(1, s);
   if (e != hipSuccess) return hip_fail(e);
-  return run_experts(P, w, ids, wts, y, workspace, s, mk, nullptr, gu_save);
+  return run_experts(P, w, ids, wts, y, workspace, s, mk, gu_save);
 }
 
 int moe_forward(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
@@ -382,7 +401,7 @@ int moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t 
   if (T > 0 && (!topk_ids || !sorted_assign || !row_of)) return MOE_ERR_INVALID_ARG;
   hipError_t e = moe::launch_align(topk_ids, T, k, E, 0, block_m, shared_rows, counts, offsets,
                                    padded_offsets, sorted_assign, row_of, row_token, tile_group,
-                                   n_tiles, nullptr, static_cast<hipStream_t>(stream));
+                                   n_tiles, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return MOE_OK;
 }

@@ -7,9 +7,10 @@
 // order.  The shared expert (glossary section 2, item 3) is added last with
 // weight 1.
 //
-// One workgroup per token gathers its k expert rows of Yp (fp32) and sums them
-// in slot order with float4 loads; no atomics, so the result is bitwise
-// reproducible.
+// A workgroup covers 1024 consecutive outputs of one token (one float4 per
+// thread): it reads the token's k row indices and weights once, then every
+// thread issues its k (+ shared) row loads together and sums them in slot
+// order.  No atomics, so the result is bitwise reproducible.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -18,35 +19,39 @@ namespace {
 
 constexpr int kMaxK = 8;
 
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ Yp,
-                                                      const int32_t* __restrict__ row_of,
-                                                      const float* __restrict__ wts,
-                                                      const int32_t* __restrict__ padded, int T,
-                                                      int D, int k, int E, int has_shared,
-                                                      float* __restrict__ y) {
-  const int t = blockIdx.x;
+constexpr int kCols4 = 256;  // float4 outputs per workgroup (one per thread)
+
+__global__ __launch_bounds__(kCols4) void moe_combine_kernel(const float* __restrict__ Yp,
+                                                         const int32_t* __restrict__ row_of,
+                                                         const float* __restrict__ wts,
+                                                         const int32_t* __restrict__ padded, int T,
+                                                         int D, int k, int E, int has_shared,
+                                                         float* __restrict__ y) {
+  const int D4 = D / 4;
+  const int chunks = (D4 + kCols4 - 1) / kCols4;
+  const int64_t t = blockIdx.x / chunks;
+  const int d = (int)(blockIdx.x - t * chunks) * kCols4 + threadIdx.x;
   int64_t rows[kMaxK];
   float w[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    const int r = (j < k) ? row_of[(int64_t)t * k + j] : -1;
+    const int r = (j < k) ? row_of[t * k + j] : -1;
     rows[j] = r;
-    w[j] = (r >= 0) ? wts[(int64_t)t * k + j] : 0.f;
+    w[j] = (r >= 0) ? wts[t * k + j] : 0.f;
   }
   const int64_t srow = has_shared ? (int64_t)padded[E] + t : -1;
-  const int D4 = D / 4;
-  for (int d = threadIdx.x; d < D4; d += blockDim.x) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if (d >= D4) return;
+  f32x4 v[kMaxK + 1];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (rows[j] >= 0) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(Yp + rows[j] * D + 4 * d);
-        s += w[j] * v;
-      }
-    }
-    if (srow >= 0) s += *reinterpret_cast<const f32x4*>(Yp + srow * D + 4 * d);
-    *reinterpret_cast<f32x4*>(y + (int64_t)t * D + 4 * d) = s;
-  }
+  for (int j = 0; j < kMaxK; ++j)
+    if (rows[j] >= 0) v[j] = *reinterpret_cast<const f32x4*>(Yp + rows[j] * D + 4 * d);
+  if (srow >= 0) v[kMaxK] = *reinterpret_cast<const f32x4*>(Yp + srow * D + 4 * d);
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (rows[j] >= 0) s += w[j] * v[j];
+  if (srow >= 0) s += v[kMaxK];
+  *reinterpret_cast<f32x4*>(y + t * D + 4 * d) = s;
 }
 
 }  // namespace
@@ -55,8 +60,9 @@ hipError_t launch_combine(const float* Yp, const int32_t* row_of, const float* w
                           const int32_t* padded, int T, int D, int k, int E, int has_shared,
                           float* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, s, Yp, row_of, wts, padded, T, D, k, E,
-                     has_shared, y);
+  const int64_t chunks = (D / 4 + kCols4 - 1) / kCols4;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)(T * chunks)), dim3(kCols4), 0, s, Yp, row_of,
+                     wts, padded, T, D, k, E, has_shared, y);
   return hipGetLastError();
 }
 

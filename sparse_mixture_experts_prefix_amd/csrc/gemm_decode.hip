@@ -466,13 +466,14 @@ __device__ __forceinline__ void decode_tile_staged(const GroupedGemm& p, char* l
 #pragma unroll
     for (int b = 0; b < NA; ++b)
       lds_dma16(rsA, st + b * 1024, k0 + akc[b] < K ? aoff[b] + 2 * k0 : kOob, 0);
+    // the weights are read once per call: non-temporal loads
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (KMAJ)
-        lds_dma16(rsB, st + AB + b * 1024,
-                  k0 + 8 * b + ir < K ? boff[b] + (uint32_t)k0 * (uint32_t)(N * 2) : kOob, 0);
+        lds_dma16<true>(rsB, st + AB + b * 1024,
+                        k0 + 8 * b + ir < K ? boff[b] + (uint32_t)k0 * (uint32_t)(N * 2) : kOob, 0);
       else
-        lds_dma16(rsB, st + AB + b * 1024, k0 + bkc[b] < K ? boff[b] + 2 * k0 : kOob, 0);
+        lds_dma16<true>(rsB, st + AB + b * 1024, k0 + bkc[b] < K ? boff[b] + 2 * k0 : kOob, 0);
     }
   };
   auto read_tr = [](const char* q) {
@@ -588,8 +589,12 @@ hipError_t launch_width(bool gate_up, const GroupedGemm& g, hipStream_t s) {
   const int nout = column_tile<FP8, false>(gate_up);
   const bool narrow = g.busy_tiles * ((nmax + nout - 1) / nout) < kFillBlocks;
   if (narrow) return launch_mt<MT, FP8, true>(gate_up, g, s);
-  if (!FP8) return launch_staged<MT>(gate_up, g, s);
-  return launch_mt<MT, FP8, false>(gate_up, g, s);
+  // wide tiles: bf16 weights stream through LDS, E4M3 codes into registers
+  // (so only those register-path kernels are instantiated)
+  if constexpr (!FP8)
+    return launch_staged<MT>(gate_up, g, s);
+  else
+    return launch_mt<MT, FP8, false>(gate_up, g, s);
 }
 
 template <int MT>

@@ -7,35 +7,32 @@
 
 namespace moe {
 
+// moe_forward's host checks of every argument but the workspace: an error
+// code, or MOE_OK (also for T == 0, where the call does nothing).
+int check_forward_args(const moe_shape* shape, const moe_weights* w, const float* y,
+                       const int32_t* topk_ids, const float* topk_w);
+
 // Router: logits = x W_g^T (+ bias) in fp32, top-k, softmax over the chosen.
 // sel (or NULL): selection-only bias, added to the keys of the top-k only.
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_g, const float* bias, const float* sel,
                          int T, int D, int E, int k, int32_t* ids, float* wts, hipStream_t s);
 
-// Few tokens: the router's K range is split over router_parts(D) workgroups
-// per 16 tokens, which write partial logits [P][T][E] (fp32); the align
-// kernel adds them (part order), adds the bias and picks top-k.
+// Few tokens: the router's work per 16 tokens is split over router_parts(D)
+// workgroups, which write partial logits [P][T][E] (fp32).
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w_g, int T, int D, int E,
                                  float* partial, hipStream_t s);
-
-// Routing finished inside the align kernel (NULL: the ids are given).
-struct RouteFinish {
-  const float* partial;  // [P][T][E]
-  int P;
-  int E;                 // experts the router scores (all of them, also for a shard)
-  const float* bias;     // fp32 [E] or NULL, added to the logits
-  const float* sel;      // fp32 [E] or NULL, added to the top-k keys only
-  int32_t* ids;          // top-k ids out [T, k]
-  float* wts;            // top-k weights out [T, k]
-};
+// ... and one wave per token adds them (part order) and the bias, and picks
+// the top-k and the softmax over the chosen: the same ids and weights as
+// launch_router, bitwise, for E <= kSmallRouteE.
+hipError_t launch_route_finish(const float* partial, int P, int T, int E, int k, const float* bias,
+                               const float* sel, int32_t* ids, float* wts, hipStream_t s);
 
 // Expert grouping of the assignments (see moe_align in moe.h).
 // E groups hold experts id_base .. id_base+E-1 (ids outside get no row).
-// With fin != NULL the ids come from fin (T <= kSmallRouteT) and `ids` is unused.
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int id_base, int BM, int shared_rows,
                         int32_t* counts, int32_t* offsets, int32_t* padded, int32_t* sorted_assign,
                         int32_t* row_of, int32_t* row_token, int32_t* tile_group, int32_t* n_tiles,
-                        const RouteFinish* fin, hipStream_t s);
+                        hipStream_t s);
 
 // out[0..n) = v (a kernel, not a memset, so it is safe in a captured graph).
 hipError_t launch_fill_i32(int32_t* out, int64_t n, int32_t v, hipStream_t s);

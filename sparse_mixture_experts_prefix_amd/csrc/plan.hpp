@@ -9,13 +9,13 @@
 
 namespace moe {
 
-// Few tokens (T <= kSmallRouteT, E <= kSmallRouteE): the router's K range is split over
-// router_parts(D) workgroups per 16 tokens (kRouterPartChunks 64-wide chunks
-// each), and the align kernel finishes the routing.
+// Few tokens (T <= kSmallRouteT, E <= kSmallRouteE): the router's 16 waves per
+// 16 tokens are split over kRouterGroups workgroups of four waves, each
+// writing its partial logits, and the align kernel finishes the routing.
 constexpr int kSmallRouteT = 64;
 constexpr int kSmallRouteE = 64;
-constexpr int kRouterPartChunks = 8;
-inline int router_parts(int64_t D) { return (int)(((D + 63) / 64 + kRouterPartChunks - 1) / kRouterPartChunks); }
+constexpr int kRouterGroups = 4;
+inline int router_parts(int64_t /*D*/) { return kRouterGroups; }
 
 // Workgroups the prefill GEMMs balance their last round over (one per CU,
 // at most this many), and so the number of partial tiles the workspace holds.

@@ -9,9 +9,10 @@
 // One workgroup of 16 wavefronts (8 when E > 128) owns 16 tokens.  Logits are an MFMA
 // 16x16x32 bf16 contraction with fp32 accumulation: wave w takes the 64-wide
 // slices w, w+16, w+32, ... of D (w, w+8, ... with 8 waves), and the partial
-// sums are added in LDS in wave order, so a token's logits are bitwise the
-// same for any T (one configuration for every batch size; 16 waves keep
-// enough loads in flight when T is a handful of tokens).  Each wave then
+// sums are added in LDS in groups of four waves, the groups in order.  So a
+// token's logits are bitwise the same for any T (one configuration for every
+// batch size), and with E <= 64 also on the few-token path, whose workgroups
+// each run one group of four waves.  Each wave then
 // ranks tokens in (value desc, index asc) order: with E <= 64 every lane
 // counts the logits that beat its own; with more experts, 4 logits per lane
 // and k rounds of a wave-wide arg-max pick them.
@@ -23,6 +24,10 @@ namespace moe {
 namespace {
 
 constexpr int kTok = 16;  // tokens per workgroup
+// The few-token router splits the full router's 16 waves over workgroups of
+// kPartWaves waves (see moe_router_partial_kernel).
+constexpr int kPartWaves = 4;
+static_assert(kRouterGroups * kPartWaves == 16, "one partial workgroup per group of four waves");
 
 // Waves per workgroup: 16, or 8 when E > 128 (64 accumulators per lane leave
 // no room for 16 waves' worth of registers).  Fixed per E, so logits do not
@@ -105,13 +110,15 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int u = 0; u < UNR; ++u)
+        for (int u = 0; u < UNR; ++u) {
+          if (ch0 + u * kWaves >= nchunks) break;  // past the end: nothing to add
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int c = 0; c < CG; ++c)
               acc[tt][c0 + c] =
                   mfma16(as_bf16x8(av[tt][u][h]), as_bf16x8(bv[u][c][h]), acc[tt][c0 + c]);
+        }
     }
   }
 
@@ -128,9 +135,17 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
     __syncthreads();
     for (int idx = tid; idx < kTok * EP; idx += kWaves * 64) {
       const int row = idx / EP, col = idx - row * EP;
-      float sum = slot(0, row, col);
+      // waves in groups of four, ((w0 + w1) + w2) + w3, then the groups in
+      // order: the association the few-token router (one workgroup per group
+      // of four waves) reproduces
+      float sum = 0.f;
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) sum += slot(w, row, col);
+      for (int g4 = 0; g4 < kWaves; g4 += kPartWaves) {
+        float gs = slot(g4, row, col);
+#pragma unroll
+        for (int w = 1; w < kPartWaves; ++w) gs += slot(g4 + w, row, col);
+        sum = g4 == 0 ? gs : sum + gs;
+      }
       if (bias && col < E) sum += bias[col];
       slot(0, row, col) = sum;  // only this thread reads or writes this element
     }
@@ -165,12 +180,13 @@ hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias,
 }
 
 
-// Partial logits for few tokens: workgroup (token tile, p) owns the 64-wide K
-// chunks p*8 .. p*8+7; wave w takes chunks w and w+4 of them, the four waves
-// are added in wave order, and the sum is stored as partial[p][t][e].  The
-// chunk of every product depends on D only, so the logits do not depend on T.
-constexpr int kPartWaves = 4;
-
+// Partial logits for few tokens (E <= 64, where the full router runs 16
+// waves): workgroup (token tile, p) runs the full router's waves 4p .. 4p + 3,
+// wave s walking the 64-wide K chunks 4p + s, 4p + s + 16, ... in ascending
+// order with the same MFMA sequence, adds its four waves in wave order and
+// stores the sum as partial[p][t][e].  The align kernel adds the four parts in
+// part order, which is the full router's grouped sum: a token's logits are
+// bitwise the same on either path and for every T.
 template <int NCT>
 __global__ __launch_bounds__(kPartWaves * 64) void moe_router_partial_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, int T, int D, int E,
@@ -184,6 +200,8 @@ __global__ __launch_bounds__(kPartWaves * 64) void moe_router_partial_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * kTok, p = blockIdx.y;
+  constexpr int kFullWaves = kRouterGroups * kPartWaves;  // the full router's waves
+  const int fw = p * kPartWaves + wave;                   // this wave's index there
   f32x4 acc[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -192,32 +210,38 @@ __global__ __launch_bounds__(kPartWaves * 64) void moe_router_partial_kernel(
   const bf16_t* xr = x + (int64_t)(tok < T ? tok : 0) * D;
   const int nchunks = (D + 63) / 64;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  constexpr int UNR = 4;  // chunks whose loads are in flight together
+  for (int ch0 = fw; ch0 < nchunks; ch0 += UNR * kFullWaves) {
 #pragma unroll
-  for (int c0 = 0; c0 < NCT; c0 += CG) {
-    u32x4 av[2][2], bv[2][CG][2];
+    for (int c0 = 0; c0 < NCT; c0 += CG) {
+      u32x4 av[UNR][2], bv[UNR][CG][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ch = p * kRouterPartChunks + wave + u * kPartWaves;
-      const int kk = ch * 64 + kb * 16;  // same K permutation as the full router
-      const bool in0 = ch < nchunks && kk < D, in1 = in0 && kk + 8 < D;
-      av[u][0] = (tok < T && in0) ? ld16(xr + kk) : zero;
-      av[u][1] = (tok < T && in1) ? ld16(xr + kk + 8) : zero;
+      for (int u = 0; u < UNR; ++u) {
+        const int ch = ch0 + u * kFullWaves;
+        const int kk = ch * 64 + kb * 16;  // same K permutation as the full router
+        const bool in0 = ch < nchunks && kk < D, in1 = in0 && kk + 8 < D;
+        av[u][0] = (tok < T && in0) ? ld16(xr + kk) : zero;
+        av[u][1] = (tok < T && in1) ? ld16(xr + kk + 8) : zero;
 #pragma unroll
-      for (int c = 0; c < CG; ++c) {
-        const int e = (c0 + c) * 16 + r16;
-        const bf16_t* wr = wg + (int64_t)(e < E ? e : 0) * D + kk;
-        bv[u][c][0] = (e < E && in0) ? ld16(wr) : zero;
-        bv[u][c][1] = (e < E && in1) ? ld16(wr + 8) : zero;
+        for (int c = 0; c < CG; ++c) {
+          const int e = (c0 + c) * 16 + r16;
+          const bf16_t* wr = wg + (int64_t)(e < E ? e : 0) * D + kk;
+          bv[u][c][0] = (e < E && in0) ? ld16(wr) : zero;
+          bv[u][c][1] = (e < E && in1) ? ld16(wr + 8) : zero;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // chunks past the end are not multiplied (as in the full router)
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (ch0 + u * kFullWaves >= nchunks) break;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+            acc[c0 + c] = mfma16(as_bf16x8(av[u][h]), as_bf16x8(bv[u][c][h]), acc[c0 + c]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int c = 0; c < CG; ++c)
-          acc[c0 + c] = mfma16(as_bf16x8(av[u][h]), as_bf16x8(bv[u][c][h]), acc[c0 + c]);
   }
 #pragma unroll
   for (int c = 0; c < NCT; ++c)
@@ -243,13 +267,54 @@ hipError_t launch_partial_nct(const uint16_t* x, const uint16_t* w_g, int T, int
       (const void*)moe_router_partial_kernel<NCT>, hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)lds);
   if (attr != hipSuccess) return attr;
-  const dim3 grid((T + kTok - 1) / kTok, router_parts(D));
+  const dim3 grid((T + kTok - 1) / kTok, kRouterGroups);
   hipLaunchKernelGGL(moe_router_partial_kernel<NCT>, grid, dim3(kPartWaves * 64), lds, s, x, w_g, T,
                      D, E, partial);
   return hipGetLastError();
 }
 
+// One wave per token: lane e < E adds the token's partial logits of the
+// router_parts groups in group order, then the bias, and the wave picks the
+// top-k and the softmax over the chosen (topk_softmax), as the full router
+// does with its grouped sum.
+__global__ __launch_bounds__(64) void moe_route_finish_kernel(const float* __restrict__ partial,
+                                                              int P, int T, int E, int k,
+                                                              const float* __restrict__ bias,
+                                                              const float* __restrict__ sel,
+                                                              int32_t* __restrict__ ids,
+                                                              float* __restrict__ wts) {
+  __shared__ float lg[64];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (lane < E) {
+    float pv[kRouterGroups];
+#pragma unroll
+    for (int q = 0; q < kRouterGroups; ++q)
+      pv[q] = q < P ? partial[((int64_t)q * T + t) * E + lane] : 0.f;
+    float v = pv[0];
+#pragma unroll
+    for (int q = 1; q < kRouterGroups; ++q)
+      if (q < P) v += pv[q];
+    if (bias) v += bias[lane];
+    lg[lane] = v;
+  }
+  __syncthreads();
+  topk_softmax(lg, sel, E, k, lane, [&](int q, int e, float p) {
+    ids[t * k + q] = e;
+    wts[t * k + q] = p;
+  });
+}
+
 }  // namespace
+
+hipError_t launch_route_finish(const float* partial, int P, int T, int E, int k, const float* bias,
+                               const float* sel, int32_t* ids, float* wts, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (E > 64 || P > kRouterGroups || k > 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_route_finish_kernel, dim3(T), dim3(64), 0, s, partial, P, T, E, k, bias, sel,
+                     ids, wts);
+  return hipGetLastError();
+}
 
 hipError_t launch_router_partial(const uint16_t* x, const uint16_t* w_g, int T, int D, int E,
                                  float* partial, hipStream_t s) {

@@ -72,6 +72,26 @@ def sample_tokens(T, n, extra=()):
     return np.array(sorted(s), np.int64)
 
 
+def tile_edge_tokens(ref, bm):
+    """Tokens owning the first and the last valid row of every m-tile of every
+    group, with the rows of an m-tile as the grouped GEMMs cut them: BM rows
+    each, except that with 256-row tiles a group of exactly two m-tiles shares
+    its rows out evenly (ceil(count / 2) rounded up to 32 rows per m-tile).
+    ``ref`` is an oracle.align result (row_token maps a padded row to its token)."""
+    toks = set()
+    counts, padded, row_token = ref["counts"], ref["padded"], ref["row_token"]
+    for g in range(counts.size):
+        cnt, p0 = int(counts[g]), int(padded[g])
+        if cnt == 0:
+            continue
+        mg = (int(padded[g + 1]) - p0) // bm
+        q = ((cnt + 1) // 2 + 31) // 32 * 32 if (bm == 256 and mg == 2) else bm
+        for j in range(-(-cnt // q)):
+            for r in (j * q, min((j + 1) * q, cnt) - 1):
+                toks.add(int(row_token[p0 + r]))
+    return sorted(toks)
+
+
 def align_equal(gpu, ref):
     """Bit-exact comparison of a GPU moe_align result with oracle.align."""
     G = ref["counts"].size

@@ -83,7 +83,17 @@ CASES = [
     (200, 200, 16, 2, 136, 64, False),   # 32-row tiles, ragged K and N, shared expert
     # T <= 64: the weight gradients' one-stage kernel, several tiles per workgroup
     (64, 2048, 16, 2, 1024, 0, False),
+    # weight-staging 16/32-row tiles on ragged shapes (N % 32 = 8, K % 64 = 40):
+    # the g | u recomputation (N = 2F = 2000) and the K-major products
+    (64, 1000, 32, 4, 1000, 0, False),
+    (256, 1000, 64, 8, 1000, 136, False),
 ]
+
+
+def test_backward_cases_reach_the_staged_tiles():
+    from tests.test_gpu_kernels import staged_decode_tiles
+    assert staged_decode_tiles(64, 1000, 32, 4, 1000, 0)
+    assert staged_decode_tiles(256, 1000, 64, 8, 1000, 136)
 
 
 @pytest.mark.parametrize("T,D,E,k,F,Fs,bias", CASES)

@@ -127,6 +127,35 @@ def test_router_batch_invariance(E, k):
         assert torch.equal(i1[0], ids[t]) and torch.equal(w1[0], w[t])
 
 
+@pytest.mark.parametrize("T,D,E,k", [(4096, 4096, 8, 2), (300, 2880, 32, 4), (200, 7168, 64, 6)])
+def test_routing_bitwise_the_same_on_every_path(T, D, E, k):
+    """A token's ids and weights are bitwise the same whether it is routed
+    alone or in a batch of up to 64 tokens (partial logits finished in the
+    align kernel) or in a larger batch (the full router kernel), through
+    moe_forward or moe_route."""
+    s = W.Shape(T=T, D=D, E=E, k=k, F=16)
+    inp = W.make_inputs(s, seed=E + k)
+    g = _gpu(inp)
+
+    def fwd(x):
+        n = x.shape[0]
+        ids = torch.empty((n, k), dtype=torch.int32, device=DEV)
+        w = torch.empty((n, k), dtype=torch.float32, device=DEV)
+        moe.moe_forward(x, g.w_g, g.w_gate_up, g.w_down, k, topk_ids=ids, topk_w=w)
+        return ids, w
+
+    ids_all, w_all = fwd(g.x)                    # T > 64: the full router
+    ids_r, w_r = moe.moe_route(g.x, g.w_g, k)
+    assert torch.equal(ids_all, ids_r) and torch.equal(w_all, w_r)
+    for n in (1, 5, 64):                         # few tokens: partial logits
+        for t0 in (0, 37, T - n):
+            xs = g.x[t0:t0 + n].contiguous()
+            ids_f, w_f = fwd(xs)
+            ids_q, w_q = moe.moe_route(xs, g.w_g, k)
+            assert torch.equal(ids_f, ids_all[t0:t0 + n]) and torch.equal(w_f, w_all[t0:t0 + n]), (n, t0)
+            assert torch.equal(ids_q, ids_f) and torch.equal(w_q, w_f), (n, t0)
+
+
 # ---------------------------------------------------------------------- align
 @pytest.mark.parametrize("T,k,E,shared", [(64, 2, 8, 0), (1000, 4, 32, 0), (513, 8, 256, 513),
                                           (1, 4, 32, 0), (4096, 2, 8, 4096), (3, 1, 1, 0)])
@@ -195,6 +224,34 @@ LAYER_CASES = [
 def test_layer_parity(T, D, E, k, F, Fs, bias):
     s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, router_bias=bias)
     _layer_parity(W.make_inputs(s, seed=T + E))
+
+
+def staged_decode_tiles(T, D, E, k, F, Fs):
+    """Whether both forward GEMMs of a bf16 layer run the weight-staging
+    16/32-row tiles: the decode tile family (BM < 256) with the wide column
+    tiles, which the launcher takes when the host's bound on occupied row
+    tiles times the column tiles (32 outputs for gate/up, 64 for down) is at
+    least 512 workgroups."""
+    bm = moe.moe_block_m(moe.make_shape(T, D, E, F, k, Fs))
+    A = T * k
+    busy = max(min(A, E), -(-A // bm)) + (-(-T // bm) if Fs else 0)
+    return bm < 256 and busy * -(-max(F, Fs) // 32) >= 512 and busy * -(-D // 64) >= 512
+
+
+STAGED_CASES = [
+    (256, 1000, 64, 8, 1000, 136),  # 32-row tiles; N % 32 = 8, K % 64 = 40; shared expert
+    (64, 1000, 32, 4, 1000, 0),     # 16-row tiles; the same ragged N and K
+    (1024, 192, 256, 8, 136, 0),    # 32-row tiles; K = 192 and 136 leave waves without a chunk
+]
+
+
+@pytest.mark.parametrize("T,D,E,k,F,Fs", STAGED_CASES)
+def test_layer_staged_decode_tiles_ragged(T, D, E, k, F, Fs):
+    """The LDS-staged decode tiles on ragged shapes: weight rows past N
+    masked, 8-wide K pieces past K masked, and waves with no K chunk."""
+    assert staged_decode_tiles(T, D, E, k, F, Fs)
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs)
+    _layer_parity(W.make_inputs(s, seed=T + F))
 
 
 @pytest.mark.parametrize("T,D,E,k,F,Fs", [
@@ -390,8 +447,9 @@ def test_layer_split_last_round(T, D, E, k, F, Fs):
     shape = moe.make_shape(T, D, E, F, k, Fs)
     assert moe.moe_block_m(shape) == 256
     y1, ids, _ = _layer_parity(inp)
-    # again with a workspace full of 0xFF bytes: the arrival counters start at -1
-    # unless the call clears them, and the partial tiles hold NaNs
+    # again with a workspace full of 0xFF bytes: the fp32 partial tiles then
+    # hold NaNs, so y is only equal if every piece writes its partial tile
+    # before the fixup kernel reads it
     g = _gpu(inp)
     ws = moe.alloc_workspace(shape, DEV)
     ws.view(torch.uint8).fill_(0xFF)

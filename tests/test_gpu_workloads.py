@@ -1,10 +1,13 @@
 """GPU parity at the full sizes of the five named workloads, in the launch
 configuration the benchmark times.
 
-Routing and grouping are checked on every token; the layer output on a
-deterministic sample of tokens (every (T/n)-th token, every near-tie token and
-the tokens owning the first and last row of every expert group), which the
-oracle computes one by one.
+Routing and grouping are checked on every token.  The layer output is
+checked on every token of the tiny, gpt-oss-shaped and Mixtral-shaped
+workloads, and elsewhere on a deterministic sample the oracle computes one by
+one: every (T/n)-th token, every near-tie token, and the tokens owning the
+first and the last valid row of every m-tile of every expert group (so every
+row tile of both GEMMs, the split pieces of a last round included, holds a
+compared row).
 """
 import dataclasses
 import time
@@ -15,7 +18,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import align_equal, check_routing, reference_y, sample_tokens, y_error
+from tests.parity import (align_equal, check_routing, reference_y, sample_tokens,
+                          tile_edge_tokens, y_error)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,17 +54,13 @@ def _run(name, T=None, n_sample=48, fp8=False):
     out = moe.moe_align(torch.from_numpy(ids_g).to(DEV), s.E, bm, s.T if s.Fs else 0)
     ref = oracle.align(ids_g, s.E, bm, shared=bool(s.Fs))
     align_equal({k_: v.cpu().numpy() for k_, v in out.items()}, ref)
-    # tokens owning the first and last row of every expert
-    edges = []
-    for e in range(s.E):
-        a0, a1 = ref["offsets"][e], ref["offsets"][e + 1]
-        if a1 > a0:
-            edges += [ref["sorted_assign"][a0] // s.k, ref["sorted_assign"][a1 - 1] // s.k]
+    # tokens owning the first and last valid row of every m-tile of every group
+    edges = tile_edge_tokens(ref, bm)
     tok = sample_tokens(s.T, n_sample, list(flipped) + edges)
     y_ref = reference_y(inp, ids_or, p_or, ids_g, w_g, flipped, tok)
     rel, err, rms = y_error(y_g[tok], y_ref)
     loads = np.bincount(ids_g.ravel(), minlength=s.E)
-    print("%s T=%d: gen %.1fs oracle %.1fs, sampled %d tokens, max|err|/RMS=%.4g (err %.3g, rms %.3g), "
+    print("%s T=%d: gen %.1fs oracle %.1fs, compared %d tokens, max|err|/RMS=%.4g (err %.3g, rms %.3g), "
           "near-tie flips %d, max load %d, empty experts %d" % (
               name, s.T, t_gen, time.time() - t1, tok.size, rel, err, rms, len(flipped),
               loads.max(), int((loads == 0).sum())))
@@ -84,7 +84,7 @@ def test_gptoss_decode_fp8_weights(T):
 
 
 def test_mixtral_prefill():
-    _run("mixtral_prefill")
+    _run("mixtral_prefill", n_sample=4096)  # every token
 
 
 def test_mixtral_prefill_fp8_weights():
