@@ -79,7 +79,8 @@ enum {
   MOE_ERR_UNSUPPORTED = -2, /* E > 256, k > 8, or sizes overflowing 32-bit row indices */
   MOE_ERR_WORKSPACE = -3,   /* workspace smaller than the call's *_workspace_size() */
   MOE_ERR_ALIGNMENT = -4,   /* a pointer not 16-byte aligned */
-  MOE_ERR_HIP = -5          /* a HIP launch failed; moe_strerror gives HIP's text */
+  MOE_ERR_HIP = -5,         /* a HIP launch failed; moe_strerror gives HIP's text */
+  MOE_ERR_SCRATCH = -6      /* moe_forward_noalloc: the shape needs more than the static array */
 };
 
 /* moe_shape.weight_format (any other value: MOE_ERR_INVALID_ARG).
@@ -164,6 +165,30 @@ int moe_block_m(const moe_shape* shape);
  */
 int moe_forward(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
                 float* topk_w, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  There
+ * is no workspace argument: the workspace is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends (the first call on a device looks up its address,
+ * with hipGetSymbolAddress, while that device is current).  No call
+ * allocates or frees memory or calls a routine that does.
+ *   shape, w, y, topk_ids, topk_w, stream: as for moe_forward (the caller
+ *             still owns and passes the inputs and outputs)
+ * Limit: shapes whose moe_workspace_size exceeds MOE_STATIC_SCRATCH_BYTES
+ * (decode-sized calls fit: e.g. T <= 64 at D = F = 2880, E = 32, k = 4 needs
+ * about 13 MB) return MOE_ERR_SCRATCH and launch nothing; use moe_forward.
+ * All calls on one GPU share its array, which keeps the last call's contents
+ * (nothing in it needs clearing: every byte a kernel reads is written first
+ * in the same call).  Calls that overlap on one GPU -- on different streams,
+ * or from host threads without an order between them -- race on the array
+ * and give wrong results: keep them on one stream.
+ * Same results as moe_forward, bitwise; otherwise the same errors.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_shape* shape, const moe_weights* w, float* y, int32_t* topk_ids,
+                        float* topk_w, void* stream);
 
 /*
  * Router only: fp32 logits x . W_g^T (+ bias), top-k, softmax over the k

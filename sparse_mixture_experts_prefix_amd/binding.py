@@ -22,11 +22,13 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_ALIGNMENT = -4
 MOE_ERR_HIP = -5
+MOE_ERR_SCRATCH = -6
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES: moe_forward_noalloc's array per GPU
 
 EXPORTS = ("moe_workspace_size", "moe_block_m", "moe_forward", "moe_route", "moe_align",
            "moe_forward_routed", "moe_forward_timed", "moe_expert_load",
            "moe_backward_workspace_size", "moe_backward", "moe_train_workspace_size",
-           "moe_forward_train", "moe_backward_saved", "moe_strerror")
+           "moe_forward_train", "moe_backward_saved", "moe_forward_noalloc", "moe_strerror")
 
 
 class MoEError(RuntimeError):
@@ -92,6 +94,8 @@ def load_library(path: str = LIB_PATH):
             lib.moe_backward_saved.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P,
                                                P, ctypes.POINTER(Grads), P, ctypes.c_size_t, P,
                                                ctypes.c_size_t, P]
+            lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Weights), P, P,
+                                                P, P]
             lib.moe_strerror.argtypes = [ctypes.c_int]
             lib.moe_strerror.restype = ctypes.c_char_p
             for name in EXPORTS[:-1]:
@@ -281,6 +285,36 @@ def moe_forward(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None,
     _check(load_library().moe_forward(ctypes.byref(shape), ctypes.byref(w), _ptr(y), _ptr(topk_ids),
                                       _ptr(topk_w), _ptr(workspace), workspace.numel(),
                                       _stream(x.device)))
+    return y
+
+
+def moe_forward_noalloc(x, w_g, w_gate_up, w_down, k, router_bias=None, ws_gate_up=None,
+                        ws_down=None, *, y, topk_ids=None, topk_w=None, expert_begin=None,
+                        bias_select=False, scales=None):
+    """moe_forward whose workspace is the library's static per-GPU array
+    (moe_forward_noalloc in moe.h): nothing is allocated, here or in the
+    library, so the outputs are preallocated (y fp32 [T, D]; topk_ids int32
+    [T, k] and topk_w fp32 [T, k], or None).  Calls that overlap on one GPU
+    race on that array.  Raises MoEError(MOE_ERR_SCRATCH) for shapes whose
+    workspace exceeds it.  Returns y."""
+    T, D, E_loc, F = _check_layer(x, w_gate_up, w_down, ws_gate_up, ws_down, scales)
+    _dev(w_g, "w_g", torch.bfloat16)
+    E = w_g.shape[0]
+    _dev(w_g, "w_g", torch.bfloat16, (E, D))
+    if E_loc != E and expert_begin is None:
+        raise ValueError("w_gate_up holds %d of %d experts: pass expert_begin" % (E_loc, E))
+    if router_bias is not None:
+        _dev(router_bias, "router_bias", torch.float32, (E,))
+    shape = _layer_shape(x, w_gate_up, w_down, k, ws_gate_up, bias_mode(router_bias, bias_select), E,
+                         expert_begin)
+    _dev(y, "y", torch.float32, (T, D))
+    if topk_ids is not None:
+        _dev(topk_ids, "topk_ids", torch.int32, (T, k))
+    if topk_w is not None:
+        _dev(topk_w, "topk_w", torch.float32, (T, k))
+    w = _weights(x, w_g, router_bias, w_gate_up, w_down, ws_gate_up, ws_down, scales)
+    _check(load_library().moe_forward_noalloc(ctypes.byref(shape), ctypes.byref(w), _ptr(y),
+                                              _ptr(topk_ids), _ptr(topk_w), _stream(x.device)))
     return y
 
 

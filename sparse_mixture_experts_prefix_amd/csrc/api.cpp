@@ -17,6 +17,12 @@ int hip_fail(hipError_t e) {
   return MOE_ERR_HIP;
 }
 
+}  // namespace
+
+int moe::record_hip_error(hipError_t e) { return hip_fail(e); }
+
+namespace {
+
 template <class T>
 T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
@@ -533,6 +539,9 @@ const char* moe_strerror(int code) {
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_size()";
     case MOE_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
     case MOE_ERR_HIP: return g_hip_msg;
+    case MOE_ERR_SCRATCH:
+      return "moe_forward_noalloc: the shape's workspace exceeds MOE_STATIC_SCRATCH_BYTES (64 MiB); "
+             "call moe_forward with a workspace";
     default: return "unknown error code";
   }
 }

@@ -7,6 +7,10 @@
 
 namespace moe {
 
+// Records a HIP error as the text moe_strerror(MOE_ERR_HIP) returns on this
+// thread and returns MOE_ERR_HIP.
+int record_hip_error(hipError_t e);
+
 // moe_forward's host checks of every argument but the workspace: an error
 // code, or MOE_OK (also for T == 0, where the call does nothing).
 int check_forward_args(const moe_shape* shape, const moe_weights* w, const float* y,

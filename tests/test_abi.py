@@ -174,8 +174,27 @@ def test_shard_workspace_is_smaller(lib):
     assert B.workspace_size(_shape(T=4096, E=64, k=2, expert_begin=0, num_local_experts=64)) == full
 
 
+def test_noalloc_rejects_shapes_beyond_its_array(lib):
+    """moe_forward_noalloc refuses, before touching any device, a shape whose
+    workspace exceeds the static array (the Mixtral-shaped prefill layer needs
+    about 0.5 GB), and checks its arguments as moe_forward does."""
+    big = _shape(T=4096, D=4096, E=8, F=14336, k=2)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value > B.STATIC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(big), ctypes.byref(_weights()), FAKE, None, None,
+                                   None) == B.MOE_ERR_SCRATCH
+    small = _shape()
+    assert lib.moe_forward_noalloc(ctypes.byref(small), ctypes.byref(_weights(x=None)), FAKE, None,
+                                   None, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_noalloc(ctypes.byref(small), ctypes.byref(_weights()), FAKE + 4, None,
+                                   None, None) == B.MOE_ERR_ALIGNMENT
+    assert lib.moe_forward_noalloc(ctypes.byref(_shape(T=0)), ctypes.byref(_weights(x=None)), None,
+                                   None, None, None) == 0
+
+
 def test_strerror(lib):
-    for code in (0, -1, -2, -3, -4, -5, 99):
+    for code in (0, -1, -2, -3, -4, -5, -6, 99):
         assert isinstance(B.strerror(code), str) and B.strerror(code)
 
 
