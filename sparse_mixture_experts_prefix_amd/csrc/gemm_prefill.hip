@@ -42,10 +42,6 @@ constexpr int kBBytes = BN * BK * 2;             // 32 KB: one K-stage of B
 constexpr int kLdsBytes = 2 * kABytes + 3 * kBBytes;  // A double-, B triple-buffered: 160 KB
 constexpr int kB8Bytes = BN * BK;                // 16 KB: one K-stage of E4M3 B
 template <bool FP8> constexpr int b_stage_bytes() { return FP8 ? kB8Bytes : kBBytes; }
-// The gate/up epilogue stages a 256 x (128 + 8) fp32 tile through LDS (139 KB),
-// so every variant gets the whole 160 KB (one workgroup per CU either way).
-constexpr int kEpilogueBytes = BM * (BN / 2 + 8) * 4;
-static_assert(kEpilogueBytes <= kLdsBytes, "gate/up epilogue must fit in the LDS allocation");
 static_assert(2 * kABytes + 3 * kB8Bytes <= kLdsBytes, "E4M3 K stages must fit");
 template <bool FP8> constexpr int lds_bytes() { return kLdsBytes; }
 constexpr int MS = 4, NS = 8;                    // tile blocks: up to MS m-tiles x NS n-tiles
@@ -112,12 +108,15 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 //    whole stage ahead of their use.
 // The barrier before substep 3 of stage i+1 waits for A(i+2) and B(i+2)
 // only (vmcnt(8): the eight B(i+3) loads issued after them may still fly).
-// Stages s0 .. s0+n-1 (n >= 1); ACT = active 32-row A sub-tiles of this wave.
+// Stages s0 .. s0+n-1 (n >= 1); ACT = active 32-row A sub-tiles of this wave;
+// NA = A loads per wave and stage (8; fewer when the tile has few rows: the
+// rows a load slot j of any wave carries start at 32 j, so 2 tier slots cover
+// the first 64 tier rows).
 // E4M3 B: four loads per wave and stage instead of eight, so B(i+3) takes
 // two per substep and the barrier waits with vmcnt(4).
 // KMAJ: B is K-major (see kmaj_chunk); KA: A is too.
 template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB, bool KMAJ = false,
-          bool KA = false, bool PRE = false>
+          bool KA = false, bool PRE = false, int NA = 8>
 __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, bool il,
                                        int lane, IssueA& issue_a, IssueB& issue_b,
                                        f32x16 (&acc)[4][4]) {
@@ -247,18 +246,18 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
 
   if constexpr (!PRE) {  // PRE: the caller has issued stage s0's loads
     issue_b(s0, 0, 0, NBL);
-    issue_a(s0, 0, 0, 8);
+    issue_a(s0, 0, 0, NA);
   }
   if (n > 1) issue_b(s0 + 1, 1, 0, NBL);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  if (n > 1) issue_a(s0 + 1, 1, 0, 4);
+  if (n > 1) issue_a(s0 + 1, 1, 0, NA / 2);
   read(0, 0, 0, 0);
   int bcur = 0, b2 = 2;  // B buffers of stages i and i+2
   for (int i = 0; i + 1 < n; ++i) {
     const int a2 = i + 2 < n ? i + 2 : n - 1;  // past the end: harmless reloads
     read(i, bcur, 1, 1);
-    issue_a(s0 + i + 1, (i + 1) & 1, 4, 8);
+    issue_a(s0 + i + 1, (i + 1) & 1, NA / 2, NA);
     mma(0);
     pattern();
     read(i, bcur, 2, 0);
@@ -280,7 +279,7 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     bcur = bcur == 2 ? 0 : bcur + 1;
     b2 = b2 == 2 ? 0 : b2 + 1;
     read(i + 1, bcur, 0, 0);
-    issue_a(s0 + a2, i & 1, 0, 4);
+    issue_a(s0 + a2, i & 1, 0, NA / 2);
     mma(1);
     pattern();
   }
@@ -415,8 +414,10 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int wm = wave >> 1, wn = wave & 1;
 
   // ------------------------------------------------------ operand sources
-  // Wave `wave`, load j (0..7) writes LDS rows (wave*8 + j)*8 .. +7 of a
-  // region; lane i of it carries row +i/8 and K-chunk (i%8) ^ swz(row).
+  // B: wave `wave`, load j (0..7) writes LDS rows (wave*8 + j)*8 .. +7 of a
+  // stage; A: load j of wave w writes rows (4 j + w)*8 .. +7, so a tile with
+  // few rows needs only the first loads of each wave (see k_loop's NA).  Lane
+  // i of a load carries row +i/8 and K-chunk (i%8) ^ swz(row).
   const __amdgpu_buffer_rsrc_t rsA =
       GATE_UP ? make_rsrc(p.A, (uint32_t)p.a_bytes)
               : make_rsrc(p.A + row0 * p.lda, (uint32_t)(BM * p.lda * 2));
@@ -437,14 +438,20 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int sub = lane >> 3;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = (wave * 8 + j) * 8 + sub;  // 0..255
+    const int r = (wave * 8 + j) * 8 + sub;  // 0..255 (B rows)
     const int kc = (lane & 7) ^ swz(r);
     const uint32_t kb = kc * 16;
-    if (GATE_UP) {
-      const int t = r < valid_rows ? p.row_token[row0 + r] : -1;
-      offA[j] = t >= 0 ? (uint32_t)t * (uint32_t)(p.lda * 2) + kb : kOob;
-    } else {
-      offA[j] = r < valid_rows ? (uint32_t)r * (uint32_t)(p.lda * 2) + kb : kOob;
+    {
+      // A: slot j of wave w loads 8-row block 4 j + w, so a tile with few
+      // rows needs only its first slots in every wave
+      const int ra = (j * 4 + wave) * 8 + sub;
+      const uint32_t kba = ((lane & 7) ^ swz(ra)) * 16;
+      if (GATE_UP) {
+        const int t = ra < valid_rows ? p.row_token[row0 + ra] : -1;
+        offA[j] = t >= 0 ? (uint32_t)t * (uint32_t)(p.lda * 2) + kba : kOob;
+      } else {
+        offA[j] = ra < valid_rows ? (uint32_t)ra * (uint32_t)(p.lda * 2) + kba : kOob;
+      }
     }
     if constexpr (KMAJ) {
       // K-major B: load j writes k-rows 2 (wave*8 + j) and + 1 of a stage;
@@ -486,12 +493,12 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
           const int r8 = (wave * 4 + j) * 16 + (lane >> 2);
           if (k0 + ((lane & 3) ^ swz4(r8)) * 16 >= K) o = kOob;
         } else {
-          const int r = (wave * 8 + j) * 8 + sub;
+          const int r = isB ? (wave * 8 + j) * 8 + sub : (j * 4 + wave) * 8 + sub;
           const int kc = kcl ^ swz(r);
           if (k0 + kc * 8 >= K) o = kOob;
         }
       }
-      const int blk = b8 ? wave * 4 + j : wave * 8 + j;  // 1-KB block of the stage
+      const int blk = b8 ? wave * 4 + j : isB ? wave * 8 + j : j * 4 + wave;  // 1-KB block of the stage
       // stage offset: k0 elements along each row, or (K-major B) k0 rows of N
       const uint32_t soff = isB ? (KMAJ ? (uint32_t)k0 * (uint32_t)(N * 2) : (uint32_t)(k0 * EB))
                                 : (uint32_t)(k0 * 2);
@@ -522,13 +529,23 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int nk = (K + BK - 1) / BK;
   const int s0 = piece ? (int)((int64_t)part * nk / S) : 0;
   const int s1 = piece ? (int)((int64_t)(part + 1) * nk / S) : nk;
-  switch (act) {
-    case 4: k_loop<GATE_UP, 4, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
-    case 3: k_loop<GATE_UP, 3, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
-    case 2: k_loop<GATE_UP, 2, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
-    case 1: k_loop<GATE_UP, 1, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
-    default: k_loop<GATE_UP, 0, FP8, decltype(issue_a), decltype(issue_b), KMAJ>(lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc); break;
+  // row tier of the tile (64-row steps): its A loads per wave per stage are
+  // 2 tier, and a wave's active sub-tiles are tier or tier - 1
+  const int tier = min(4, max(1, (valid_rows + 63) / 64));
+#define MOE_KL(A_, N_)                                                                            \
+  k_loop<GATE_UP, A_, FP8, decltype(issue_a), decltype(issue_b), KMAJ, false, false, N_>(         \
+      lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc)
+  switch (tier * 8 + act) {
+    case 4 * 8 + 4: MOE_KL(4, 8); break;
+    case 4 * 8 + 3: MOE_KL(3, 8); break;
+    case 3 * 8 + 3: MOE_KL(3, 6); break;
+    case 3 * 8 + 2: MOE_KL(2, 6); break;
+    case 2 * 8 + 2: MOE_KL(2, 4); break;
+    case 2 * 8 + 1: MOE_KL(1, 4); break;
+    case 1 * 8 + 1: MOE_KL(1, 2); break;
+    default: MOE_KL(0, 2); break;
   }
+#undef MOE_KL
   auto a_row = [&](int i) { return a_row_of(wm, i, il); };
 
   // E4M3: every output column times the scale of its weight row
@@ -592,37 +609,38 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     }
   }
   if (GATE_UP) {
-    // SwiGLU in registers; the 256 x 128 fp32 result goes through the (now
-    // idle) LDS so that each lane writes 16 bytes of H at a time, and padding
-    // rows are not written.  Rows are padded to 136 floats so the two row
-    // groups of a 64-lane write land on different banks.
-    constexpr int kHs = BN / 2 + 8;  // kEpilogueBytes = BM * kHs * 4
-    float* hs = reinterpret_cast<float*>(lds);
-    __syncthreads();  // every wave is done reading the K stages
+    // SwiGLU in registers, h stored from registers as bf16 pairs (measured
+    // 1.5-2% faster for the whole gate/up kernel than staging the fp32 tile
+    // through LDS for 16-byte stores).  Register r of lane l holds row
+    // 8 (r / 4) + 4 kh + r % 4, column l % 32 of its 32 x 32 block; for the
+    // register pair (2q, 2q + 1) (rows R, R + 1) the even lane stores row R,
+    // columns c, c + 1 and the odd lane row R + 1, columns c - 1, c, after
+    // swapping one value (DPP quad permutation 1 0 3 2).  Rows past the tile's
+    // count (padding, or the next m-tile's) are not stored.
+    const __amdgpu_buffer_rsrc_t rsH = make_rsrc(reinterpret_cast<bf16_t*>(p.C) + row0 * p.ldc,
+                                                (uint32_t)(BM * p.ldc * 2));
+    const bool odd = lane & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= act) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int q = 0; q < 8; ++q) {
+        const int r = 2 * q + (odd ? 1 : 0);
         const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          hs[row * kHs + wn * 64 + j * 32 + lr] = silu(acc[i][j][r]) * acc[i][j + 2][r];
+        for (int j = 0; j < 2; ++j) {
+          const float h0 = silu(acc[i][j][2 * q]) * acc[i][j + 2][2 * q];
+          const float h1 = silu(acc[i][j][2 * q + 1]) * acc[i][j + 2][2 * q + 1];
+          const float send = odd ? h0 : h1;
+          const float got = __builtin_bit_cast(
+              float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+          const float lo = odd ? got : h0, hi = odd ? h1 : got;
+          const int col = n0 + wn * 64 + j * 32 + (lr & ~1);
+          const uint32_t v = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+          const uint32_t off = (row < valid_rows && col < N) ? (uint32_t)((row * p.ldc + col) * 2) : kOob;
+          __builtin_amdgcn_raw_buffer_store_b32(v, rsH, off, 0, 0);
+        }
       }
-    }
-    __syncthreads();
-    bf16_t* H = reinterpret_cast<bf16_t*>(p.C);
-    const int ncol = min(BN / 2, N - n0);  // a multiple of 8 (N % 8 == 0)
-    for (int e = tid; e < valid_rows * (BN / 16); e += 256) {
-      const int row = e / (BN / 16), c8 = (e % (BN / 16)) * 8;
-      if (c8 >= ncol) continue;
-      const float4 v0 = *reinterpret_cast<const float4*>(hs + row * kHs + c8);
-      const float4 v1 = *reinterpret_cast<const float4*>(hs + row * kHs + c8 + 4);
-      auto pack = [](float a, float b) {
-        return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-      };
-      const u32x4 w = {pack(v0.x, v0.y), pack(v0.z, v0.w), pack(v1.x, v1.y), pack(v1.z, v1.w)};
-      st16(H + (row0 + row) * p.ldc + n0 + c8, w);
     }
     return;
   }

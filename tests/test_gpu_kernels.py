@@ -226,6 +226,23 @@ def test_layer_parity(T, D, E, k, F, Fs, bias):
     _layer_parity(W.make_inputs(s, seed=T + E))
 
 
+@pytest.mark.parametrize("T,D,E,k,F,Fs", [
+    (4096, 256, 8, 2, 4096, 0),      # every expert over several m-tiles, a ragged last one
+    (3000, 320, 8, 2, 4000, 1000),   # ragged N and K; the shared expert's narrower N
+])
+def test_layer_many_gate_up_rounds(T, D, E, k, F, Fs):
+    """Shapes with at least four rounds of 256 x 256 gate/up tiles (no tile cut
+    over K), experts over several m-tiles with ragged last ones, ragged N and K
+    and a shared expert narrower than the routed ones: every token against
+    the oracle."""
+    bm = moe.moe_block_m(moe.make_shape(T, D, E, F, k, Fs))
+    assert bm == 256
+    m_tiles_min = -(-T * k // 256) + (-(-T // 256) if Fs else 0)
+    assert m_tiles_min * -(-max(F, Fs) // 128) >= 4 * 256
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs)
+    _layer_parity(W.make_inputs(s, seed=T + F))
+
+
 def staged_decode_tiles(T, D, E, k, F, Fs):
     """Whether both forward GEMMs of a bf16 layer run the weight-staging
     16/32-row tiles: the decode tile family (BM < 256) with the wide column
