@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.parity import align_equal, check_routing, reference_y, sample_tokens, y_error
+from tests import tolerances as TL
+from tests.parity import Y_TOL, align_equal, check_routing, reference_y, sample_tokens, y_error
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,7 @@ def _layer_parity(inp, tokens=None):
     rel, err, rms = y_error(y[tok], y_ref)
     print("T=%d D=%d E=%d k=%d F=%d Fs=%d: max|err|/RMS=%.4g flips=%d" % (
         T, s.D, s.E, s.k, s.F, s.Fs, rel, len(flipped)))
-    assert rel <= 2e-2
+    assert rel <= Y_TOL
     return y, ids_g, w_g
 
 
@@ -203,7 +204,7 @@ def test_forward_routed_parity(T, D, E, k, F, Fs):
     torch.cuda.synchronize()
     y_ref = oracle.experts(inp, ids_or, p_or.astype(np.float32).astype(np.float64))
     rel, _, _ = y_error(y.cpu().numpy(), y_ref)
-    assert rel <= 2e-2
+    assert rel <= Y_TOL
 
 
 # --------------------------------------------------------------- whole layer
@@ -386,8 +387,9 @@ def test_layer_fp8_power_of_two_scales_match_bf16(T, D, E, k, F, Fs):
     K differently (128- vs 64-wide chunks), so y may differ by fp32 summation
     order and the rare bf16 rounding of an h element that lands on the other
     side.  With scales up to 2^-7 a weight reaches 3.5, so one such h moves a
-    y element by up to ~0.4% of RMS: bounded at 1e-2 RMS, and the routing
-    must agree bit for bit."""
+    y element by a fraction of a percent of RMS (emulated in
+    tests/test_tolerances.py): bounded at KSPLIT_TOL, and the routing must
+    agree bit for bit."""
     s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs, fp8=True)
     inp = W.make_inputs(s, seed=T + 1)
     rng = np.random.default_rng(T)
@@ -414,7 +416,7 @@ def test_layer_fp8_power_of_two_scales_match_bf16(T, D, E, k, F, Fs):
     assert np.array_equal(ids8, idsb) and np.array_equal(w8, wb)
     rel, _, _ = y_error(y8, yb.astype(np.float64))
     print("E4M3 vs bf16 kernels: max|dy|/RMS = %.3g" % rel)
-    assert rel <= 1e-2
+    assert rel <= TL.KSPLIT_TOL
 
 
 def test_layer_fp8_shard_and_routed():
@@ -437,7 +439,7 @@ def test_layer_fp8_shard_and_routed():
     y_ref = oracle.experts(sh, ids_or, p_or.astype(np.float32).astype(np.float64), expert_begin=a,
                            n_local=b - a)
     rel, _, _ = y_error(y.cpu().numpy(), y_ref)
-    assert rel <= 2e-2
+    assert rel <= Y_TOL
 
 
 def _split(V, ctas, kmin):
@@ -526,11 +528,12 @@ def test_layer_expert_shards(T, D, E, k, F, Fs, bounds):
                              expert_begin=a, n_local=b - a)
         err = float(np.max(np.abs(y.cpu().numpy().astype(np.float64) - ref)))
         print("shard %d [%d, %d): max|err|/RMS(layer) = %.4g" % (r, a, b, err / rms))
-        assert err <= 2e-2 * rms
+        assert err <= Y_TOL * rms
         total += y.cpu().numpy()
     # not bitwise: a shard's tile count changes the K-split of its GEMMs, and a
-    # different fp32 summation order can move H by one bf16 ulp (2^-8)
-    assert float(np.max(np.abs(total - y_full))) <= 1e-2 * rms
+    # different fp32 summation order can move h by one bf16 ulp; the bar is
+    # derived from the count of such flips in tests/test_tolerances.py
+    assert float(np.max(np.abs(total - y_full))) <= TL.SHARD_SUM_TOL * rms
 
 
 def test_layer_E1_k1_dense_ffn():
@@ -622,4 +625,4 @@ def test_forward_routed_tile_boundaries():
     torch.cuda.synchronize()
     y_ref = oracle.experts(inp, ids, p.astype(np.float64))
     rel, _, _ = y_error(y.cpu().numpy(), y_ref)
-    assert rel <= 2e-2
+    assert rel <= Y_TOL
