@@ -644,21 +644,43 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     }
     return;
   }
+  // fp32 rows of the tile through buffer stores: the row of register r is
+  // wave-uniform and goes in the scalar offset, the lane's column (and its
+  // 4-row half) in the vector offset, so no store needs a 64-bit address.
+  // The scalar offset is outside the hardware's range check, so a tile with
+  // rows past its count (the group's last) drops those rows through the
+  // vector offset; full tiles take the same loop with the check folded away.
+  {
+    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(reinterpret_cast<float*>(p.C) + row0 * p.ldc,
+                                                (uint32_t)((int64_t)valid_rows * p.ldc * 4));
+    uint32_t voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i >= act) continue;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (row >= valid_rows) continue;  // past the tile's rows: the next m-tile's or padding
-      const int64_t grow = row0 + row;
-      float* Y = reinterpret_cast<float*>(p.C);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 128 + j * 32 + lr;
-        if (n < N) Y[grow * p.ldc + n] = acc[i][j][r];
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn * 128 + j * 32 + lr;
+      voff[j] = n < N ? (uint32_t)((4 * kh * p.ldc + n) * 4) : kOob;
     }
+    auto store_rows = [&](const bool check) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= act) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rb = a_row(i) + 8 * (r >> 2) + (r & 3);
+          const uint32_t soff = (uint32_t)(rb * p.ldc * 4);
+          const bool ok = !check || rb + 4 * kh < valid_rows;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float v = acc[i][j][r];  // a scalar first (see the pieces' stores)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsY,
+                                                  ok ? voff[j] : kOob, soff, 0);
+          }
+        }
+      }
+    };
+    if (valid_rows >= BM)
+      store_rows(false);
+    else
+      store_rows(true);
   }
 }
 
