@@ -11,7 +11,7 @@ namespace moe {
 
 // Few tokens (T <= kSmallRouteT, E <= kSmallRouteE): the router's 16 waves per
 // 16 tokens are split over kRouterGroups workgroups of four waves, each
-// writing its partial logits, and the align kernel finishes the routing.
+// writing its partial logits, and a per-token kernel finishes the routing.
 constexpr int kSmallRouteT = 64;
 constexpr int kSmallRouteE = 64;
 constexpr int kRouterGroups = 4;

@@ -184,7 +184,7 @@ hipError_t launch_nct(const uint16_t* x, const uint16_t* w_g, const float* bias,
 // waves): workgroup (token tile, p) runs the full router's waves 4p .. 4p + 3,
 // wave s walking the 64-wide K chunks 4p + s, 4p + s + 16, ... in ascending
 // order with the same MFMA sequence, adds its four waves in wave order and
-// stores the sum as partial[p][t][e].  The align kernel adds the four parts in
+// stores the sum as partial[p][t][e].  moe_route_finish_kernel adds the four parts in
 // part order, which is the full router's grouped sum: a token's logits are
 // bitwise the same on either path and for every T.
 template <int NCT>

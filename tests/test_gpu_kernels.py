@@ -132,7 +132,7 @@ def test_router_batch_invariance(E, k):
 def test_routing_bitwise_the_same_on_every_path(T, D, E, k):
     """A token's ids and weights are bitwise the same whether it is routed
     alone or in a batch of up to 64 tokens (partial logits finished in the
-    align kernel) or in a larger batch (the full router kernel), through
+    route-finish kernel) or in a larger batch (the full router kernel), through
     moe_forward or moe_route."""
     s = W.Shape(T=T, D=D, E=E, k=k, F=16)
     inp = W.make_inputs(s, seed=E + k)
@@ -273,7 +273,7 @@ def test_layer_staged_decode_tiles_ragged(T, D, E, k, F, Fs):
 
 
 @pytest.mark.parametrize("T,D,E,k,F,Fs", [
-    (64, 2880, 32, 4, 512, 0),     # few tokens: routing finished in the align kernel
+    (64, 2880, 32, 4, 512, 0),     # few tokens: partial logits, routing finished per token
     (7, 512, 64, 6, 256, 256),     # few tokens, 64 experts, shared expert
     (300, 1024, 8, 2, 512, 0),     # full router, E <= 64 top-k
     (40, 1024, 256, 8, 256, 256),  # full router, E > 64 top-k
