@@ -159,7 +159,10 @@ def test_routing_bitwise_the_same_on_every_path(T, D, E, k):
 
 # ---------------------------------------------------------------------- align
 @pytest.mark.parametrize("T,k,E,shared", [(64, 2, 8, 0), (1000, 4, 32, 0), (513, 8, 256, 513),
-                                          (1, 4, 32, 0), (4096, 2, 8, 4096), (3, 1, 1, 0)])
+                                          (1, 4, 32, 0), (4096, 2, 8, 4096), (3, 1, 1, 0),
+                                          # T*k = 1024, the last size of the one-workgroup
+                                          # kernel, and 1025, the first of the per-group one
+                                          (128, 8, 64, 0), (205, 5, 64, 0), (205, 5, 64, 205)])
 def test_align_parity_random_ids(T, k, E, shared):
     rng = np.random.default_rng(T * 7 + E)
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
@@ -606,12 +609,18 @@ def test_errors_are_raised_before_launch():
     assert ei.value.code in (moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED)
 
 
-def test_forward_routed_tile_boundaries():
+@pytest.mark.parametrize("counts", [
+    [257, 300, 511, 512, 256, 1, 0, 700],
+    # one-tile groups at the row tiers' edges (64-row steps pick the A loads per
+    # stage) and at 32-row sub-tile edges
+    [64, 65, 192, 193, 33, 32, 128, 129],
+])
+def test_forward_routed_tile_boundaries(counts):
     """256-row tiles at group sizes around tile boundaries (k = 1, so the counts are
     exact): 257, 300, 511 and 700 rows (two- and three-m-tile groups, the two-tile ones
-    split evenly), 512 and 256 (full tiles), 1 row and an empty expert; tokens in
-    shuffled order so every tile gathers scattered rows."""
-    counts = [257, 300, 511, 512, 256, 1, 0, 700]
+    split evenly), 512 and 256 (full tiles), 1 row and an empty expert; one-tile groups
+    on both sides of 32, 64, 128 and 192 rows; tokens in shuffled order so every tile
+    gathers scattered rows."""
     T, D, F = sum(counts), 256, 320
     assert moe.moe_block_m(moe.make_shape(T, D, len(counts), F, 1)) == 256
     s = W.Shape(T=T, D=D, E=len(counts), k=1, F=F, Fs=64)
