@@ -10,7 +10,9 @@
 // A workgroup covers 1024 consecutive outputs of one token (one float4 per
 // thread): it reads the token's k row indices and weights once, then every
 // thread issues its k (+ shared) row loads together and sums them in slot
-// order.  No atomics, so the result is bitwise reproducible.
+// order.  No atomics, so the result is bitwise reproducible.  Every Yp element
+// is read once, so the loads are non-temporal (DeepSeek-shaped layer, 1.9 GB
+// of Yp: 463 -> 402 us; no change where Yp is small).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -44,8 +46,10 @@ __global__ __launch_bounds__(kCols4) void moe_combine_kernel(const float* __rest
   f32x4 v[kMaxK + 1];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
-    if (rows[j] >= 0) v[j] = *reinterpret_cast<const f32x4*>(Yp + rows[j] * D + 4 * d);
-  if (srow >= 0) v[kMaxK] = *reinterpret_cast<const f32x4*>(Yp + srow * D + 4 * d);
+    if (rows[j] >= 0)
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Yp + rows[j] * D + 4 * d));
+  if (srow >= 0)
+    v[kMaxK] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Yp + srow * D + 4 * d));
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)

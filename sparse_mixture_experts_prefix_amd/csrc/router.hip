@@ -85,40 +85,97 @@ __global__ __launch_bounds__(waves_for<NCT>() * 64) void moe_router_kernel(const
   // tiles, for their accumulators' registers)
   constexpr int CG = TT > 1 ? 4 : (NCT < 8 ? NCT : 8);
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int ch0 = wave; ch0 < nchunks; ch0 += UNR * kWaves) {
+  if constexpr (TT > 1) {
+    // E > 128: a chunk's x fragments are loaded once and its W_g column tiles
+    // in groups of GP, each group's loads issued before the MFMAs of the one
+    // before (the next chunk's first group before the last group's MFMAs, its
+    // x right after them), so loads are in flight while the MFMAs run.  Every
+    // accumulator still takes its MFMAs in chunk order.
+    static_assert(UNR == 1, "one chunk at a time");
+    constexpr int GP = 2;  // column tiles per group (registers: 128 accumulators beside them)
+    constexpr int NG = NCT / GP;
+    u32x4 xa[TT][2], wb[2][GP][2];
+    auto load_x = [&](int ch) {
+      const int kk = ch * 64 + kb * 16;
+      const bool in0 = ch < nchunks && kk < D, in1 = in0 && kk + 8 < D;
 #pragma unroll
-    for (int c0 = 0; c0 < NCT; c0 += CG) {
-      u32x4 av[TT][UNR][2], bv[UNR][CG][2];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int kk = (ch0 + u * kWaves) * 64 + kb * 16;  // D % 8 == 0: 8-runs are all in or out
-        const bool in0 = ch0 + u * kWaves < nchunks && kk < D, in1 = in0 && kk + 8 < D;
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-          av[tt][u][0] = (tin[tt] && in0) ? ld16(xr[tt] + kk) : zero;
-          av[tt][u][1] = (tin[tt] && in1) ? ld16(xr[tt] + kk + 8) : zero;
-        }
-#pragma unroll
-        for (int c = 0; c < CG; ++c) {
-          const int e = (c0 + c) * 16 + r16;
-          const bf16_t* wr = wg + (int64_t)(e < E ? e : 0) * D + kk;
-          bv[u][c][0] = (e < E && in0) ? ld16(wr) : zero;
-          bv[u][c][1] = (e < E && in1) ? ld16(wr + 8) : zero;
-        }
+      for (int tt = 0; tt < TT; ++tt) {
+        xa[tt][0] = (tin[tt] && in0) ? ld16(xr[tt] + kk) : zero;
+        xa[tt][1] = (tin[tt] && in1) ? ld16(xr[tt] + kk + 8) : zero;
       }
-      __builtin_amdgcn_sched_barrier(0);  // all loads of the trip before the MFMAs
+    };
+    auto load_w = [&](int ch, int grp, int wbuf) {
+      const int kk = ch * 64 + kb * 16;
+      const bool in0 = ch < nchunks && kk < D, in1 = in0 && kk + 8 < D;
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+      for (int c = 0; c < GP; ++c) {
+        const int e = (grp * GP + c) * 16 + r16;
+        const bf16_t* wr = wg + (int64_t)(e < E ? e : 0) * D + kk;
+        wb[wbuf][c][0] = (e < E && in0) ? ld16(wr) : zero;
+        wb[wbuf][c][1] = (e < E && in1) ? ld16(wr + 8) : zero;
+      }
+    };
+    if (wave < nchunks) {
+      load_x(wave);
+      load_w(wave, 0, 0);
+    }
+    for (int ch = wave; ch < nchunks; ch += kWaves) {
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-          if (ch0 + u * kWaves >= nchunks) break;  // past the end: nothing to add
+      for (int grp = 0; grp < NG; ++grp) {
+        const int wbuf = grp & 1;  // NG is even: group 0 of every chunk is buffer 0
+        if (grp + 1 < NG)
+          load_w(ch, grp + 1, wbuf ^ 1);
+        else if (ch + kWaves < nchunks)
+          load_w(ch + kWaves, 0, wbuf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);  // the next loads before these MFMAs
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int c = 0; c < CG; ++c)
-              acc[tt][c0 + c] =
-                  mfma16(as_bf16x8(av[tt][u][h]), as_bf16x8(bv[u][c][h]), acc[tt][c0 + c]);
+            for (int c = 0; c < GP; ++c)
+              acc[tt][grp * GP + c] = mfma16(as_bf16x8(xa[tt][h]), as_bf16x8(wb[wbuf][c][h]),
+                                             acc[tt][grp * GP + c]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ch + kWaves < nchunks) load_x(ch + kWaves);
+    }
+  } else {
+    for (int ch0 = wave; ch0 < nchunks; ch0 += UNR * kWaves) {
+#pragma unroll
+      for (int c0 = 0; c0 < NCT; c0 += CG) {
+        u32x4 av[TT][UNR][2], bv[UNR][CG][2];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int kk = (ch0 + u * kWaves) * 64 + kb * 16;  // D % 8 == 0: 8-runs are all in or out
+          const bool in0 = ch0 + u * kWaves < nchunks && kk < D, in1 = in0 && kk + 8 < D;
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+            av[tt][u][0] = (tin[tt] && in0) ? ld16(xr[tt] + kk) : zero;
+            av[tt][u][1] = (tin[tt] && in1) ? ld16(xr[tt] + kk + 8) : zero;
+          }
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            const int e = (c0 + c) * 16 + r16;
+            const bf16_t* wr = wg + (int64_t)(e < E ? e : 0) * D + kk;
+            bv[u][c][0] = (e < E && in0) ? ld16(wr) : zero;
+            bv[u][c][1] = (e < E && in1) ? ld16(wr + 8) : zero;
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);  // all loads of the trip before the MFMAs
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int u = 0; u < UNR; ++u) {
+            if (ch0 + u * kWaves >= nchunks) break;  // past the end: nothing to add
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int c = 0; c < CG; ++c)
+                acc[tt][c0 + c] =
+                    mfma16(as_bf16x8(av[tt][u][h]), as_bf16x8(bv[u][c][h]), acc[tt][c0 + c]);
+          }
+      }
     }
   }
 
