@@ -77,7 +77,10 @@ def _layer_parity(inp, tokens=None):
 # --------------------------------------------------------------------- router
 @pytest.mark.parametrize("T,D,E,k,bias", [
     (64, 128, 8, 2, False), (300, 2880, 32, 4, False), (97, 7168, 256, 8, False),
-    (1, 64, 3, 3, False), (50, 4096, 8, 2, True), (33, 136, 17, 5, False)])
+    (1, 64, 3, 3, False), (50, 4096, 8, 2, True), (33, 136, 17, 5, False),
+    # E > 128 (two token tiles per workgroup, W_g column tiles loaded in pairs):
+    # ragged expert count, and fewer K chunks than the workgroup has waves
+    (300, 512, 129, 4, True), (40, 136, 200, 8, False)])
 def test_router_parity(T, D, E, k, bias):
     s = W.Shape(T=T, D=D, E=E, k=k, F=8, router_bias=bias)
     inp = W.make_inputs(s, seed=T + D)
