@@ -885,21 +885,42 @@ __device__ __forceinline__ void wgrad_issue(const WgradGemm& p, const WgradTile&
   }
 }
 
+// The tile's fp32 rows through buffer stores, as the down GEMM's epilogue:
+// the wave-uniform row offset in the scalar offset, the lane's column (and
+// 4-row half) in the vector offset, and rows past the matrix dropped through
+// an out-of-range vector offset (the scalar offset is not range-checked).
 __device__ __forceinline__ void wgrad_store(const WgradTile& w, int wm, int wn, int lane,
                                             const f32x16 (&acc)[4][4]) {
   const int lr = lane & 31, kh = lane >> 5;
+  const int rows = w.M - w.m0 < BM ? w.M - w.m0 : BM;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(w.C + (int64_t)w.m0 * w.N, (uint32_t)((int64_t)rows * w.N * 4));
+  uint32_t voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int n = w.n0 + b_row_of<false>(wn, j) + lr;
+    voff[j] = n < w.N ? (uint32_t)((4 * kh * w.N + n) * 4) : kOob;
+  }
+  auto store_rows = [&](const bool check) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = w.m0 + a_row_of(wm, i, false) + 8 * (r >> 2) + 4 * kh + (r & 3);
-      if (m >= w.M) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = w.n0 + b_row_of<false>(wn, j) + lr;
-        if (n < w.N) w.C[(int64_t)m * w.N + n] = acc[i][j][r];
+      for (int r = 0; r < 16; ++r) {
+        const int rb = a_row_of(wm, i, false) + 8 * (r >> 2) + (r & 3);
+        const uint32_t soff = (uint32_t)(rb * w.N * 4);
+        const bool ok = !check || rb + 4 * kh < rows;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = acc[i][j][r];  // a scalar first (see the pieces' stores)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs,
+                                                ok ? voff[j] : kOob, soff, 0);
+        }
       }
-    }
+  };
+  if (rows >= BM)
+    store_rows(false);
+  else
+    store_rows(true);
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
