@@ -50,7 +50,9 @@
  *    nonzero) positive multiples of 8, T*k + E*BM + T < 2^31.
  *  - Ownership: the caller owns every buffer.  The library allocates no device
  *    memory and keeps no state between calls except a cached device-property
- *    lookup.  The workspace is caller-provided, sized by moe_workspace_size
+ *    lookup (and, for moe_forward_noalloc only, its static per-GPU workspace
+ *    array and that array's cached address).  The workspace is
+ *    caller-provided, sized by moe_workspace_size
  *    (moe_backward_workspace_size for the backward pass,
  *    moe_train_workspace_size for the training forward), and its contents
  *    need not be initialised.
