@@ -338,12 +338,16 @@ template <bool FP8> constexpr int unroll() { return FP8 ? kUnrFp8 : kUnr; }
 // decode_tile_staged.
 constexpr int kKmBBytes = 64 * 128;  // a stage's B: 64 k-rows x 64 columns, bf16
 template <int MT> constexpr int km_a_bytes() { return 16 * MT * 128; }
-template <int MT> constexpr int km_stage_bytes() { return km_a_bytes<MT>() + kKmBBytes; }
+// NG column groups of 16 weight rows (row-major weights; K-major stages are
+// always 64 columns): a stage's B is NG * 2 KB
+template <int MT, int NG = 4> constexpr int km_stage_bytes() { return km_a_bytes<MT>() + NG * 2048; }
 // stages per wave: 16-row tiles take two, so two workgroups share a CU (80 KB
 // each) and one's start and end overlap the other's streaming; 32-row tiles
 // take three (144 KB, one workgroup per CU)
 template <int MT> constexpr int km_stages() { return MT == 1 ? 2 : 3; }
-template <int MT> constexpr int km_lds_bytes() { return kKw * km_stages<MT>() * km_stage_bytes<MT>(); }
+template <int MT, int NG = 4> constexpr int km_lds_bytes() {
+  return kKw * km_stages<MT>() * km_stage_bytes<MT, NG>();
+}
 
 // 16-byte chunk c (columns 8c .. 8c + 7) of k-row r of a B stage sits at
 // chunk position c ^ km_b_swz(r) of the row's 128 bytes.  A 32-lane half of a
@@ -362,15 +366,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // KMAJ = false: the forward's products with row-major weights ([N][K] per
-// group; gate/up: 32 gate rows and the matching 32 up rows), staged the same
-// way: a stage's B is 64 weight rows x 64 k, laid out like A, read with plain
-// 16-byte LDS reads.
-template <int MT, bool KMAJ, bool GATE_UP>
+// group; gate/up: 8 NG gate rows and the matching 8 NG up rows), staged the
+// same way: a stage's B is 16 NG weight rows x 64 k, laid out like A, read
+// with plain 16-byte LDS reads.  NG = 4 (64 weight rows) for most shapes; 2
+// (gate/up) and 1 (down) when a handful of tokens occupy few row tiles, so
+// the grid still fills the chip.
+template <int MT, bool KMAJ, bool GATE_UP, int NG = 4>
 __device__ __forceinline__ void decode_tile_staged(const GroupedGemm& p, char* lds) {
   static_assert(!(KMAJ && GATE_UP), "K-major weights: rows x weight products only");
-  constexpr int NG = 4, BMD = 16 * MT, NOUT = GATE_UP ? 16 * NG / 2 : 16 * NG;
-  constexpr int SB = km_stage_bytes<MT>(), AB = km_a_bytes<MT>(), S = km_stages<MT>();
-  constexpr int NA = AB / 1024, NB = kKmBBytes / 1024, V = NA + NB;  // 1-KB loads per chunk
+  static_assert(!KMAJ || NG == 4, "K-major stages hold 64 columns");
+  static_assert(!GATE_UP || NG % 2 == 0, "gate/up tiles pair gate and up groups");
+  constexpr int BMD = 16 * MT, NOUT = GATE_UP ? 16 * NG / 2 : 16 * NG;
+  constexpr int SB = km_stage_bytes<MT, NG>(), AB = km_a_bytes<MT>(), S = km_stages<MT>();
+  constexpr int NA = AB / 1024, NB = NG * 2, V = NA + NB;  // 1-KB loads per chunk
+  constexpr int HR = 8 * NG;  // gate/up: weight rows of each half of the tile
 
   const int64_t bid = blockIdx.x;
   const int64_t n_tile = bid % p.n_tiles_n;
@@ -420,10 +429,10 @@ __device__ __forceinline__ void decode_tile_staged(const GroupedGemm& p, char* l
       const int n = n0 + 8 * (ip ^ km_b_swz(r));
       bkc[b] = 0;
       boff[b] = n < N ? (uint32_t)r * (uint32_t)(N * 2) + n * 2 : kOob;
-    } else {  // weight row r of the tile: gate/up rows 0-31 gate, 32-63 up
+    } else {  // weight row r of the tile: gate/up rows 0 .. HR - 1 gate, HR .. 2 HR - 1 up
       const int ch = ip ^ km_a_swz(r);
-      const int f = GATE_UP ? n0 + (r & 31) : n0 + r;
-      const int brow = GATE_UP ? (r >> 5) * N + f : f;
+      const int f = GATE_UP ? n0 + r % HR : n0 + r;
+      const int brow = GATE_UP ? (r / HR) * N + f : f;
       bkc[b] = 8 * ch;
       boff[b] = f < N ? (uint32_t)brow * (uint32_t)(K * 2) + ch * 16 : kOob;
     }
@@ -580,21 +589,25 @@ hipError_t launch_mt(bool gate_up, GroupedGemm g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int MT>
-hipError_t launch_staged(bool gate_up, const GroupedGemm& g0, hipStream_t s);
+template <int MT, bool GATE_UP, int NG>
+hipError_t launch_staged(const GroupedGemm& g0, hipStream_t s);
 
 template <int MT, bool FP8>
 hipError_t launch_width(bool gate_up, const GroupedGemm& g, hipStream_t s) {
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
   const int nout = column_tile<FP8, false>(gate_up);
   const bool narrow = g.busy_tiles * ((nmax + nout - 1) / nout) < kFillBlocks;
-  if (narrow) return launch_mt<MT, FP8, true>(gate_up, g, s);
-  // wide tiles: bf16 weights stream through LDS, E4M3 codes into registers
-  // (so only those register-path kernels are instantiated)
-  if constexpr (!FP8)
-    return launch_staged<MT>(gate_up, g, s);
-  else
+  // bf16 weights stream through LDS (narrow tiles: the register path's
+  // column groups), E4M3 codes into registers
+  if constexpr (!FP8) {
+    if (narrow)
+      return gate_up ? launch_staged<MT, true, kNgGateUpNarrow>(g, s)
+                     : launch_staged<MT, false, kNgDownNarrow>(g, s);
+    return gate_up ? launch_staged<MT, true, 4>(g, s) : launch_staged<MT, false, 4>(g, s);
+  } else {
+    if (narrow) return launch_mt<MT, FP8, true>(gate_up, g, s);
     return launch_mt<MT, FP8, false>(gate_up, g, s);
+  }
 }
 
 template <int MT>
@@ -603,39 +616,32 @@ __global__ __launch_bounds__(kKw * 64) void moe_gemm_rows_kmajor_decode_kernel(G
   decode_tile_staged<MT, true, false>(p, lds);
 }
 
-template <int MT, bool GATE_UP>
+template <int MT, bool GATE_UP, int NG>
 __global__ __launch_bounds__(kKw * 64) void moe_gemm_staged_decode_kernel(GroupedGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  decode_tile_staged<MT, false, GATE_UP>(p, lds);
+  decode_tile_staged<MT, false, GATE_UP, NG>(p, lds);
 }
 
-// bf16 weights, wide column tiles: the weights stream through LDS
-template <int MT>
-hipError_t launch_staged(bool gate_up, const GroupedGemm& g0, hipStream_t s) {
-  static const hipError_t a0 =
-      hipFuncSetAttribute((const void*)moe_gemm_staged_decode_kernel<MT, true>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, km_lds_bytes<MT>());
-  static const hipError_t a1 =
-      hipFuncSetAttribute((const void*)moe_gemm_staged_decode_kernel<MT, false>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, km_lds_bytes<MT>());
-  if (a0 != hipSuccess) return a0;
-  if (a1 != hipSuccess) return a1;
-  const int64_t brows = gate_up ? 2 : 1;
+// bf16 weights: the weights stream through LDS, NG column groups per tile
+template <int MT, bool GATE_UP, int NG>
+hipError_t launch_staged(const GroupedGemm& g0, hipStream_t s) {
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)moe_gemm_staged_decode_kernel<MT, GATE_UP, NG>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, km_lds_bytes<MT, NG>());
+  if (attr != hipSuccess) return attr;
+  const int64_t brows = GATE_UP ? 2 : 1;
   if (brows * g0.K_routed * g0.N_routed * 2 >= (int64_t(1) << 31) ||
       brows * g0.K_shared * g0.N_shared * 2 >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
   GroupedGemm g = g0;
   const int nmax = g.N_routed > g.N_shared ? g.N_routed : g.N_shared;
-  const int nout = gate_up ? 32 : 64;
+  const int nout = GATE_UP ? 8 * NG : 16 * NG;
   g.n_tiles_n = (nmax + nout - 1) / nout;
   const int64_t blocks = g.max_tiles * g.n_tiles_n;
   if (blocks == 0) return hipSuccess;
-  if (gate_up)
-    hipLaunchKernelGGL((moe_gemm_staged_decode_kernel<MT, true>), dim3((unsigned)blocks),
-                       dim3(kKw * 64), km_lds_bytes<MT>(), s, g);
-  else
-    hipLaunchKernelGGL((moe_gemm_staged_decode_kernel<MT, false>), dim3((unsigned)blocks),
-                       dim3(kKw * 64), km_lds_bytes<MT>(), s, g);
+  constexpr int lds = km_lds_bytes<MT, NG>();
+  hipLaunchKernelGGL((moe_gemm_staged_decode_kernel<MT, GATE_UP, NG>), dim3((unsigned)blocks),
+                     dim3(kKw * 64), lds, s, g);
   return hipGetLastError();
 }
 
