@@ -262,11 +262,36 @@ def staged_decode_tiles(T, D, E, k, F, Fs):
     return bm < 256 and busy * -(-max(F, Fs) // 32) >= 512 and busy * -(-D // 64) >= 512
 
 
+def narrow_decode_tiles(T, D, E, k, F, Fs):
+    """Whether both forward GEMMs take the narrow column tiles (16 outputs per
+    workgroup, still staged through LDS for bf16): fewer than 512 workgroups
+    with the wide ones."""
+    bm = moe.moe_block_m(moe.make_shape(T, D, E, F, k, Fs))
+    A = T * k
+    busy = max(min(A, E), -(-A // bm)) + (-(-T // bm) if Fs else 0)
+    return bm < 256 and busy * -(-max(F, Fs) // 32) < 512 and busy * -(-D // 64) < 512
+
+
 STAGED_CASES = [
     (256, 1000, 64, 8, 1000, 136),  # 32-row tiles; N % 32 = 8, K % 64 = 40; shared expert
     (64, 1000, 32, 4, 1000, 0),     # 16-row tiles; the same ragged N and K
     (1024, 192, 256, 8, 136, 0),    # 32-row tiles; K = 192 and 136 leave waves without a chunk
 ]
+NARROW_CASES = [
+    (1, 1000, 32, 4, 1000, 0),      # one token: N % 16 = 8, K % 64 = 40
+    (3, 200, 8, 2, 136, 64),        # shared expert; K = 200 and 136, N = 136 and 64
+    (1, 2880, 32, 4, 2880, 0),      # the gpt-oss shape at one token
+    (2, 512, 64, 8, 384, 0),        # top-8 of 64 experts
+]
+
+
+@pytest.mark.parametrize("T,D,E,k,F,Fs", NARROW_CASES)
+def test_layer_narrow_decode_tiles_ragged(T, D, E, k, F, Fs):
+    """The narrow staged decode tiles (32 and 16 weight rows per stage) on
+    ragged shapes and a few tokens."""
+    assert narrow_decode_tiles(T, D, E, k, F, Fs)
+    s = W.Shape(T=T, D=D, E=E, k=k, F=F, Fs=Fs)
+    _layer_parity(W.make_inputs(s, seed=T + F))
 
 
 @pytest.mark.parametrize("T,D,E,k,F,Fs", STAGED_CASES)
