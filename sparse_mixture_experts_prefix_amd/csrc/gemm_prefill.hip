@@ -24,12 +24,17 @@
 //    than another.
 //  - MFMA work of 32-row sub-tiles that hold only padding rows is skipped.
 //  - A short, partial last round of tiles is cut along K (see split_of).
+//  - A group's last m-tile of at most 32 rows is not a tile of its own: the
+//    m-tile before it computes those rows too, with their A fragments loaded
+//    straight into registers (see tile_rows and k_loop's XR).
 //  - E4M3 weights (one fp32 scale per weight row): a B stage holds the codes,
 //    64-byte rows of four 16-byte chunks swizzled by (r >> 1) & 3; a lane's
 //    16-byte read carries its weights of two k-substeps (K is permuted the
 //    same way for A), widened to bf16 exactly in registers, and each output
 //    column is multiplied by its row's scale before the epilogue.  Half the
 //    weight bytes and half the B loads of bf16, for the same MFMAs.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -45,6 +50,9 @@ template <bool FP8> constexpr int b_stage_bytes() { return FP8 ? kB8Bytes : kBBy
 static_assert(2 * kABytes + 3 * kB8Bytes <= kLdsBytes, "E4M3 K stages must fit");
 template <bool FP8> constexpr int lds_bytes() { return kLdsBytes; }
 constexpr int MS = 4, NS = 8;                    // tile blocks: up to MS m-tiles x NS n-tiles
+constexpr int kExtraRows = 32;                   // rows a full m-tile takes on from the next
+constexpr int kTileRows = BM + kExtraRows;        // rows of the largest tile
+static_assert(kTileRows * BN == kPartialTileFloats, "a partial tile holds the largest tile");
 constexpr int kMaxSplit = 8;                     // pieces per tile of the last round
 constexpr int kMinPieceStages = 4;               // K-stages per piece, at least
 constexpr int kSplitRounds = 4;                  // cut only when V < kSplitRounds * ctas
@@ -115,13 +123,54 @@ __device__ __forceinline__ int b_row_of(int wn, int j) {
 // E4M3 B: four loads per wave and stage instead of eight, so B(i+3) takes
 // two per substep and the barrier waits with vmcnt(4).
 // KMAJ: B is K-major (see kmaj_chunk); KA: A is too.
+// XR: the tile also computes its folded rows (see tile_rows).  Their A
+// fragments come from memory straight into registers, one 16-byte load per
+// lane and k-substep (every wave loads the same 32 rows), issued a stage
+// ahead together with the A rows of that stage, so that B's loads keep their
+// lead; each wave takes two 32 x 32 output blocks of them with the B
+// fragments it already holds: gate/up the gate and up blocks of column block
+// wm of its half, down column blocks 2 wm and 2 wm + 1 of its half.
+struct ExtraRows {
+  __amdgpu_buffer_rsrc_t rs;  // A's buffer
+  uint32_t off;               // this lane's row (lane % 32) at k = 0 (kOob past the rows)
+  int K;
+  f32x16 acc[2];
+};
+// column block (j of b_row_of) of folded-row output block h of wave row w
+template <bool GATE_UP>
+__device__ __forceinline__ constexpr int xblock(int w, int h) {
+  return GATE_UP ? w + 2 * h : 2 * w + h;
+}
+// The folded rows' two MFMAs with their accumulators in VGPRs: the tile's
+// 256 accumulators fill the AGPRs, and the compiler would put these in AGPRs
+// too (and spill).  Written out, so the hazards the compiler handles for its
+// own MFMAs are handled here: two wait states before (an E4M3 B fragment is
+// written by VALU just before), and xr_settle after the K loop, before any
+// other instruction reads the accumulators.
+__device__ __forceinline__ void mfma32_x2(f32x16& c0, f32x16& c1, const bf16x8& a, const bf16x8& b0,
+                                          const bf16x8& b1) {
+  asm("s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
+      : "+v"(c0), "+v"(c1)
+      : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b0)),
+        "v"(__builtin_bit_cast(u32x4, b1)));
+}
+// wait states after the last of them (a 32x32x16 MFMA's result is read by
+// VALU or memory instructions only 18 or more wait states later); the
+// accumulators pass through, so nothing that reads them can move above it
+__device__ __forceinline__ void xr_settle(f32x16& c0, f32x16& c1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
+}
+
 template <bool GATE_UP, int ACT, bool FP8, class IssueA, class IssueB, bool KMAJ = false,
-          bool KA = false, bool PRE = false, int NA = 8>
+          bool KA = false, bool PRE = false, int NA = 8, bool XR = false, int XW = 0>
 __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, int wn, bool il,
                                        int lane, IssueA& issue_a, IssueB& issue_b,
-                                       f32x16 (&acc)[4][4]) {
+                                       f32x16 (&acc)[4][4], ExtraRows* xr = nullptr) {
   static_assert(!KMAJ || (!GATE_UP && !FP8), "K-major B: bf16 rows x weight products only");
   static_assert(!KA || KMAJ, "K-major A comes with K-major B");
+  static_assert(!XR || (ACT == 4 && NA == 8 && !KMAJ), "folded rows: full tiles of the forward kernels");
   constexpr int NBL = FP8 ? 4 : 8;  // B loads per wave and stage
   const int lr = lane & 31, kh = lane >> 5;
   // LDS byte offset of this lane's A chunk inside a 32-row block, per k-substep.
@@ -202,6 +251,27 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[slot][i], fb[slot][j], acc[i][j]);
   };
+  // folded rows: fragments of the current and the next stage
+  u32x4 xcur[4], xnext[4];
+  auto issue_x = [&](int stage, u32x4(&dst)[4]) {
+    if constexpr (XR) {
+      const int k0 = stage * BK;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = FP8 ? 4 * (ks >> 1) + 2 * kh + (ks & 1) : 2 * ks + kh;  // as rd[ks]
+        const uint32_t o = k0 + 8 * c < xr->K ? xr->off + 16 * c : kOob;
+        dst[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr->rs, o, 2 * k0, 0));
+      }
+    }
+  };
+  auto mma_x = [&](int slot, int ks) {
+    if constexpr (XR) {
+      // XW = wm, a compile-time copy of the loop per wave row
+      const bf16x8 a = __builtin_bit_cast(bf16x8, xcur[ks]);
+      mfma32_x2(xr->acc[0], xr->acc[1], a, fb[slot][xblock<GATE_UP>(XW, 0)],
+                fb[slot][xblock<GATE_UP>(XW, 1)]);
+    }
+  };
   // instruction order of one substep (16 MFMAs): one MFMA, then the 8
   // fragment reads of the next substep each behind one MFMA (a burst of reads
   // queues behind the other waves' reads and the loads' LDS writes), then the
@@ -243,11 +313,38 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     if constexpr (15 - RD - 3 * GAP > 0) __builtin_amdgcn_sched_group_barrier(0x008, 15 - RD - 3 * GAP, 0);
   };
+  // XR: nl (4, or 8 with the folded rows' loads) loads spread over the 16
+  // MFMAs after the reads (the folded rows' two MFMAs are written out, which
+  // the scheduler does not count)
+  auto pattern_x = [&](auto nl) {
+    constexpr int NL = decltype(nl)::value, GAP = NL > 4 ? 1 : 2, REST = 16 - 9 - GAP * (NL - 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < NL; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (q + 1 < NL) __builtin_amdgcn_sched_group_barrier(0x008, GAP, 0);
+    }
+    if constexpr (REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);
+  };
+  auto block_pattern = [&](auto nl) {
+    if constexpr (XR)
+      pattern_x(nl);
+    else
+      pattern();
+  };
+  using L4 = std::integral_constant<int, 4>;
+  using L8 = std::integral_constant<int, 8>;
 
   if constexpr (!PRE) {  // PRE: the caller has issued stage s0's loads
     issue_b(s0, 0, 0, NBL);
     issue_a(s0, 0, 0, NA);
   }
+  issue_x(s0, xcur);
   if (n > 1) issue_b(s0 + 1, 1, 0, NBL);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
@@ -258,16 +355,20 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     const int a2 = i + 2 < n ? i + 2 : n - 1;  // past the end: harmless reloads
     read(i, bcur, 1, 1);
     issue_a(s0 + i + 1, (i + 1) & 1, NA / 2, NA);
+    issue_x(s0 + i + 1, xnext);  // before B(i+2), whose loads may still fly at the barrier
     mma(0);
-    pattern();
+    mma_x(0, 0);
+    block_pattern(L8{});
     read(i, bcur, 2, 0);
     issue_b(s0 + a2, b2, 0, NBL / 2);
     mma(1);
-    pattern();
+    mma_x(1, 1);
+    block_pattern(L4{});
     read(i, bcur, 3, 1);
     issue_b(s0 + a2, b2, NBL / 2, NBL);
     mma(0);
-    pattern();
+    mma_x(0, 2);
+    block_pattern(L4{});
     // vmcnt(NBL): A(i+1) and B(i+1) landed, B(i+2) may still fly; lgkmcnt(0):
     // this wave's reads of stage i are done.  A plain s_barrier, since the
     // fence of __syncthreads would wait for every load.
@@ -281,16 +382,26 @@ __device__ __forceinline__ void k_loop(const char* lds, int s0, int n, int wm, i
     read(i + 1, bcur, 0, 0);
     issue_a(s0 + a2, i & 1, 0, NA / 2);
     mma(1);
-    pattern();
+    mma_x(1, 3);
+    block_pattern(L4{});
+    if constexpr (XR) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) xcur[ks] = xnext[ks];
+    }
   }
   // last stage: no loads, no barrier
   read(n - 1, bcur, 1, 1);
   mma(0);
+  mma_x(0, 0);
   read(n - 1, bcur, 2, 0);
   mma(1);
+  mma_x(1, 1);
   read(n - 1, bcur, 3, 1);
   mma(0);
+  mma_x(0, 2);
   mma(1);
+  mma_x(1, 3);
+  if constexpr (XR) xr_settle(xr->acc[0], xr->acc[1]);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no load may still be writing LDS at exit
 }
 
@@ -308,9 +419,9 @@ struct Split {
   int S;               // pieces per cut tile (1: no cut)
 };
 
-__device__ __forceinline__ Split split_of(const GroupedGemm& p) {
+__device__ __forceinline__ Split split_of(const GroupedGemm& p, int64_t mt) {
   Split sp;
-  sp.V = (int64_t)p.n_tiles[0] * p.n_tiles_n;
+  sp.V = mt * p.n_tiles_n;
   sp.R = 0;
   sp.S = 1;
   if (p.ctas > 0 && sp.V % p.ctas && sp.V < (int64_t)kSplitRounds * p.ctas) {
@@ -327,33 +438,10 @@ __device__ __forceinline__ Split split_of(const GroupedGemm& p) {
   return sp;
 }
 
-// Logical tile L -> (m_tile, n_tile): columns of NS n-tiles; inside a column
-// the groups in order, each cut into blocks of up to MS of its m-tiles x the
-// column's n-tiles, m-tile fastest.  Consecutive tiles (the workgroups an XCD
-// runs together) then share their A and B tiles, and a block never straddles
-// two experts' weights.
-__device__ __forceinline__ void tile_coords(const GroupedGemm& p, int64_t L, int64_t& m_tile,
-                                            int64_t& n_tile) {
-  const int64_t mt = p.n_tiles[0];
-  const int64_t colsz = mt * NS;
-  const int64_t sn = L / colsz;
-  const int64_t cw = min((int64_t)NS, p.n_tiles_n - sn * NS);  // n-tiles in this column
-  const int64_t u = L - sn * colsz;                               // < mt * cw
-  const int g = p.tile_group[u / cw];
-  const int64_t t0 = p.group_padded[g] / p.BM;                   // the group's first m-tile
-  const int64_t mg = p.group_padded[g + 1] / p.BM - t0;          // and its m-tiles
-  const int64_t v = u - t0 * cw;                                  // < mg * cw
-  const int64_t mb = v / (MS * cw);                               // block of the group
-  const int64_t mh = min((int64_t)MS, mg - mb * MS);              // its m-tiles
-  const int64_t inner = v - mb * MS * cw;
-  m_tile = t0 + mb * MS + inner % mh;
-  n_tile = sn * NS + inner / mh;
-}
-
-// Rows of m-tile `m_tile` (of group g).  A group of two m-tiles (a few hundred
-// rows: many experts, few rows each) shares its rows out evenly, q = ceil(count
-// / 2) rounded up to whole 32-row sub-tiles: otherwise its second m-tile holds
-// a few rows, runs ahead of the first (it is load-bound, with almost no MFMA
+// Rows of a group's m-tiles.  A group of two m-tiles (a few hundred rows:
+// many experts, few rows each) shares its rows out evenly, q = ceil(count / 2)
+// rounded up to whole 32-row sub-tiles: otherwise its second m-tile holds a
+// few rows, runs ahead of the first (it is load-bound, with almost no MFMA
 // work) and reads the expert's weights from HBM a second time instead of from
 // L2 together with the first.  Larger groups keep full 256-row m-tiles (q =
 // 256): there the light last m-tile costs a smaller share of the weight
@@ -362,14 +450,136 @@ __device__ __forceinline__ void tile_coords(const GroupedGemm& p, int64_t L, int
 // m-tile j covers the group's rows j q .. j q + valid - 1, stored from padded
 // row row0 = group_padded[g] + j q (its 256-row window may reach into the next
 // m-tile's rows, which it neither reads nor writes).
-__device__ __forceinline__ void tile_rows(const GroupedGemm& p, int64_t m_tile, int g, int64_t& row0,
-                                          int& valid) {
-  const int64_t first = p.group_padded[g] / BM;
-  const int64_t mg = p.group_padded[g + 1] / BM - first;
-  const int cnt = p.group_count[g];
+// In the forward kernels (not K-major B) a group of two or more m-tiles whose
+// last one would hold at most kExtraRows rows folds those rows into the m-tile
+// before it, which then has valid = 256 rows through LDS plus `extra` rows
+// 256 .. 256 + extra - 1; the last m-tile does not run.  It would stream the
+// expert's whole weight tile for a few rows, at over half a full tile's time
+// (and a group of 257-288 rows would be two half-empty tiles).  m-tiles of a
+// group of c rows that run:
+__device__ __forceinline__ int run_mtiles(int c) {
+  const int mg = (c + BM - 1) / BM;
+  return mg - (mg >= 2 && c - (mg - 1) * BM <= kExtraRows ? 1 : 0);
+}
+
+// A group's m-tiles as the kernel numbers them: the group, its row count, its
+// first m-tile and its m-tiles.  FOLD: the m-tiles that run, numbered group by
+// group in row order; else every BM-row m-tile of the padded layout (the
+// align kernel's tile_group and n_tiles).
+struct RunGroup {
+  int g, cnt, mg;
+  int64_t first;
+};
+
+// FOLD numbering: every wave derives it from the group counts, five groups per
+// lane (one round of loads and a wave-wide prefix sum), so no workgroup is
+// launched for a folded m-tile.  (Such workgroups, returning at once, left CUs
+// idle behind longer tiles: the hardware hands workgroups out to the XCDs in
+// order.  The same numbering read from tables the align kernel wrote measured
+// slower: the down GEMM on the Mixtral shape took 0.96 ms instead of 0.82.)
+constexpr int kGroupsPerLane = 5;  // 64 x 5 >= 257 groups
+struct GroupScan {
+  int cnt[kGroupsPerLane];  // counts of this lane's groups 5 l .. 5 l + 4 (0 past the last)
+  int excl;                 // m-tiles that run in the groups before them
+  int64_t mt;               // m-tiles that run in all groups
+};
+
+__device__ __forceinline__ GroupScan scan_groups(const GroupedGemm& p) {
+  const int lane = threadIdx.x & 63;
+  const int G = p.E + (p.B_shared ? 1 : 0);
+  GroupScan sc;
+  int tot = 0;
+#pragma unroll
+  for (int q = 0; q < kGroupsPerLane; ++q) {
+    const int g = lane * kGroupsPerLane + q;
+    sc.cnt[q] = g < G ? p.group_count[g] : 0;
+    tot += run_mtiles(sc.cnt[q]);
+  }
+  int incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  sc.excl = incl - tot;
+  sc.mt = __builtin_amdgcn_readlane(incl, 63);
+  return sc;
+}
+
+template <bool FOLD>
+__device__ __forceinline__ int64_t mtiles_of(const GroupedGemm& p) {
+  if constexpr (FOLD) return scan_groups(p).mt;
+  return p.n_tiles[0];
+}
+
+// the group of m-tile m (< mtiles_of), as wave-uniform (scalar) values
+template <bool FOLD>
+__device__ __forceinline__ RunGroup group_of_mtile(const GroupedGemm& p, int64_t m) {
+  RunGroup rg;
+  if constexpr (FOLD) {
+    const GroupScan sc = scan_groups(p);
+    const int lane = threadIdx.x & 63;
+    int run = sc.excl, hit = -1, hfirst = 0, hmg = 0;
+#pragma unroll
+    for (int q = 0; q < kGroupsPerLane; ++q) {
+      const int mm = run_mtiles(sc.cnt[q]);
+      if (m >= run && m < run + mm) {
+        hit = lane * kGroupsPerLane + q;
+        hfirst = run;
+        hmg = mm;
+      }
+      run += mm;
+    }
+    const int src = (int)__builtin_ctzll(__ballot(hit >= 0));  // the one lane that holds it
+    rg.g = __builtin_amdgcn_readlane(hit, src);
+    rg.first = __builtin_amdgcn_readlane(hfirst, src);
+    rg.mg = __builtin_amdgcn_readlane(hmg, src);
+  } else {
+    rg.g = p.tile_group[m];
+    rg.first = p.group_padded[rg.g] / p.BM;
+    rg.mg = (int)(p.group_padded[rg.g + 1] / p.BM - rg.first);
+  }
+  rg.cnt = p.group_count[rg.g];
+  return rg;
+}
+
+// Logical tile L -> (m-tile, n_tile) and its group: columns of NS n-tiles;
+// inside a column the groups in order, each cut into blocks of up to MS of its
+// m-tiles x the column's n-tiles, m-tile fastest.  Consecutive tiles (the
+// workgroups an XCD runs together) then share their A and B tiles, and a
+// block never straddles two experts' weights.
+template <bool FOLD>
+__device__ __forceinline__ void tile_coords(const GroupedGemm& p, int64_t mt, int64_t L,
+                                            int64_t& m_tile, int64_t& n_tile, RunGroup& rg) {
+  const int64_t colsz = mt * NS;
+  const int64_t sn = L / colsz;
+  const int64_t cw = min((int64_t)NS, p.n_tiles_n - sn * NS);  // n-tiles in this column
+  const int64_t u = L - sn * colsz;                               // < mt * cw
+  rg = group_of_mtile<FOLD>(p, u / cw);
+  const int64_t v = u - rg.first * cw;                            // < mg * cw
+  const int64_t mb = v / (MS * cw);                               // block of the group
+  const int64_t mh = min((int64_t)MS, rg.mg - mb * MS);           // its m-tiles
+  const int64_t inner = v - mb * MS * cw;
+  m_tile = rg.first + mb * MS + inner % mh;
+  n_tile = sn * NS + inner / mh;
+}
+
+// Rows of the group's j-th m-tile (in row order; see above).
+template <bool FOLD>
+__device__ __forceinline__ void tile_rows(const GroupedGemm& p, const RunGroup& rg, int64_t j,
+                                          int64_t& row0, int& valid, int& extra) {
+  const int cnt = rg.cnt;
+  const int64_t pad0 = p.group_padded[rg.g];
+  const int mg = (cnt + BM - 1) / BM;  // m-tiles of the padded layout
+  extra = 0;
+  if (FOLD && rg.mg < mg) {  // the last m-tile's rows fold into m-tile mg - 2
+    row0 = pad0 + j * BM;
+    valid = BM;
+    if (j == rg.mg - 1) extra = cnt - (int)(j + 1) * BM;
+    return;
+  }
   const int q = mg == 2 ? ((cnt + 1) / 2 + 31) / 32 * 32 : BM;
-  const int64_t j = m_tile - first;
-  row0 = p.group_padded[g] + j * q;
+  row0 = pad0 + j * q;
   valid = max(0, min(q, cnt - (int)(j * q)));
 }
 
@@ -379,7 +589,8 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   // hardware deals workgroup b to XCD b % 8, so XCD x executes run x in
   // order and the workgroups an XCD runs together share A and B tiles in its
   // L2.  The R*S pieces come after all of them.
-  const Split sp = split_of(p);
+  const int64_t mt = mtiles_of<!KMAJ>(p);
+  const Split sp = split_of(p, mt);
   const int64_t run = (sp.n_dp + 7) / 8;
   const int64_t b = blockIdx.x;
   int64_t L;
@@ -397,8 +608,9 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const bool piece = L >= sp.n_dp;
   const int S = sp.S;
   int64_t m_tile, n_tile;
-  tile_coords(p, L, m_tile, n_tile);
-  const int g = p.tile_group[m_tile];
+  RunGroup rg;
+  tile_coords<!KMAJ>(p, mt, L, m_tile, n_tile, rg);
+  const int g = rg.g;
   const bool shared = g >= p.E;
   const int N = shared ? p.N_shared : p.N_routed;
   const int K = shared ? p.K_shared : p.K_routed;
@@ -407,7 +619,8 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   if (n0 >= N) return;
   int64_t row0;
   int valid_rows;
-  tile_rows(p, m_tile, g, row0, valid_rows);
+  int extra;  // folded rows 256 .. 256 + extra - 1 (see tile_rows)
+  tile_rows<!KMAJ>(p, rg, m_tile - rg.first, row0, valid_rows, extra);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -420,7 +633,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   // i of a load carries row +i/8 and K-chunk (i%8) ^ swz(row).
   const __amdgpu_buffer_rsrc_t rsA =
       GATE_UP ? make_rsrc(p.A, (uint32_t)p.a_bytes)
-              : make_rsrc(p.A + row0 * p.lda, (uint32_t)(BM * p.lda * 2));
+              : make_rsrc(p.A + row0 * p.lda, (uint32_t)((BM + extra) * p.lda * 2));
   constexpr int EB = FP8 ? 1 : 2;  // bytes per weight
   const int64_t brows = (int64_t)(GATE_UP ? 2 : 1) * N;  // weight rows of this group
   const char* Bg = shared ? static_cast<const char*>(p.B_shared)
@@ -532,6 +745,232 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   // row tier of the tile (64-row steps): its A loads per wave per stage are
   // 2 tier, and a wave's active sub-tiles are tier or tier - 1
   const int tier = min(4, max(1, (valid_rows + 63) / 64));
+  auto a_row = [&](int i) { return a_row_of(wm, i, il); };
+
+  // ---------------------------------------------------------- after K loop
+  // XRT: the tile holds folded rows (xr); the other tiles' code does not
+  // carry them, so their registers and schedule stay as they were.
+  auto finish = [&](auto xrt, ExtraRows* xr) {
+    constexpr bool XRT = decltype(xrt)::value;
+    // E4M3: every output column times the scale of its weight row
+    if constexpr (FP8) {
+      const float* Sg = shared ? p.S_shared : p.S_routed + (int64_t)g * brows;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int wr = b_weight_row(b_row_of<GATE_UP>(wn, j) + lr);
+        const float sc = wr >= 0 ? Sg[wr] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i >= act) continue;
+          acc[i][j] *= sc;
+        }
+      }
+      if constexpr (XRT) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int wr = b_weight_row(b_row_of<GATE_UP>(wn, xblock<GATE_UP>(wm, h)) + lr);
+          xr->acc[h] *= wr >= 0 ? Sg[wr] : 0.f;
+        }
+      }
+    }
+
+    // ---------------------------------------------- pieces of a split tile
+    if (piece) {  // row-major fp32 partial tile, columns in LDS B-row order
+      // one per-lane base offset; every store adds a compile-time byte offset,
+      // so the 256 stores need no address registers
+      const __amdgpu_buffer_rsrc_t rsP = make_rsrc(
+          p.partial + (int64_t)(piece_tile * S + part) * (kTileRows * BN), kTileRows * BN * 4);
+      const uint32_t vbase = (uint32_t)(((a_row(0) + 4 * kh) * BN + b_row_of<GATE_UP>(wn, 0) + lr) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= act) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int off = ((a_row(i) - a_row(0) + 8 * (r >> 2) + (r & 3)) * BN +
+                             (b_row_of<GATE_UP>(0, j) - b_row_of<GATE_UP>(0, 0))) * 4;
+            const float v = acc[i][j][r];  // a scalar first: bit_cast of a vector element
+                                           // reinterprets the vector's first lane
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsP, vbase, off, 0);
+          }
+      }
+      if constexpr (XRT) {  // folded rows: partial rows 256 .. 287
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t vx =
+              (uint32_t)(((BM + 4 * kh) * BN + b_row_of<GATE_UP>(wn, xblock<GATE_UP>(wm, h)) + lr) * 4);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float v = xr->acc[h][r];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsP, vx,
+                                                  (8 * (r >> 2) + (r & 3)) * BN * 4, 0);
+          }
+        }
+      }
+      return;
+    }
+
+    // ------------------------------------------------------------ epilogue
+    if (GATE_UP && p.gu_out) {  // keep g and u (bf16) of the valid rows for the backward pass
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= act) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
+          if (row >= valid_rows) continue;
+          bf16_t* gr = reinterpret_cast<bf16_t*>(p.gu_out) + (row0 + row) * p.ld_gu;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int f = n0 + wn * 64 + j * 32 + lr;
+            if (f < N) {
+              gr[f] = f32_to_bf16(acc[i][j][r]);
+              gr[N + f] = f32_to_bf16(acc[i][j + 2][r]);
+            }
+          }
+        }
+      }
+      if constexpr (XRT) {  // folded rows: gate and up of column block wm of this wave's half
+        const int f = n0 + wn * 64 + wm * 32 + lr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = BM + 8 * (r >> 2) + 4 * kh + (r & 3);
+          if (row >= BM + extra || f >= N) continue;
+          bf16_t* gr = reinterpret_cast<bf16_t*>(p.gu_out) + (row0 + row) * p.ld_gu;
+          gr[f] = f32_to_bf16(xr->acc[0][r]);
+          gr[N + f] = f32_to_bf16(xr->acc[1][r]);
+        }
+      }
+    }
+    if (GATE_UP) {
+      // SwiGLU in registers, h stored from registers as bf16 pairs (measured
+      // 1.5-2% faster for the whole gate/up kernel than staging the fp32 tile
+      // through LDS for 16-byte stores).  Register r of lane l holds row
+      // 8 (r / 4) + 4 kh + r % 4, column l % 32 of its 32 x 32 block; for the
+      // register pair (2q, 2q + 1) (rows R, R + 1) the even lane stores row R,
+      // columns c, c + 1 and the odd lane row R + 1, columns c - 1, c, after
+      // swapping one value (DPP quad permutation 1 0 3 2).  Rows past the
+      // tile's count (padding, or the next m-tile's) are not stored; the
+      // folded rows (gate and up of column block wm of the wave's half) alike.
+      const int rows = XRT ? BM + extra : valid_rows;
+      const __amdgpu_buffer_rsrc_t rsH = make_rsrc(reinterpret_cast<bf16_t*>(p.C) + row0 * p.ldc,
+                                                  (uint32_t)((XRT ? BM + extra : BM) * p.ldc * 2));
+      const bool odd = lane & 1;
+      auto store_pair = [&](float g0, float u0, float g1, float u1, int row, int col) {
+        const float h0 = silu(g0) * u0;
+        const float h1 = silu(g1) * u1;
+        const float send = odd ? h0 : h1;
+        const float got = __builtin_bit_cast(
+            float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+        const float lo = odd ? got : h0, hi = odd ? h1 : got;
+        const uint32_t v = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+        const uint32_t off = (row < rows && col < N) ? (uint32_t)((row * p.ldc + col) * 2) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b32(v, rsH, off, 0, 0);
+      };
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= act) continue;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = 2 * q + (odd ? 1 : 0);
+          const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            store_pair(acc[i][j][2 * q], acc[i][j + 2][2 * q], acc[i][j][2 * q + 1],
+                       acc[i][j + 2][2 * q + 1], row, n0 + wn * 64 + j * 32 + (lr & ~1));
+        }
+      }
+      if constexpr (XRT) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = 2 * q + (odd ? 1 : 0);
+          store_pair(xr->acc[0][2 * q], xr->acc[1][2 * q], xr->acc[0][2 * q + 1], xr->acc[1][2 * q + 1],
+                     BM + 8 * (r >> 2) + 4 * kh + (r & 3), n0 + wn * 64 + wm * 32 + (lr & ~1));
+        }
+      }
+      return;
+    }
+    // fp32 rows of the tile through buffer stores: the row of register r is
+    // wave-uniform and goes in the scalar offset, the lane's column (and its
+    // 4-row half) in the vector offset, so no store needs a 64-bit address.
+    // The scalar offset is outside the hardware's range check, so a tile with
+    // rows past its count (the group's last) drops those rows through the
+    // vector offset; full tiles take the same loop with the check folded away.
+    {
+      const __amdgpu_buffer_rsrc_t rsY =
+          make_rsrc(reinterpret_cast<float*>(p.C) + row0 * p.ldc,
+                    (uint32_t)((int64_t)(XRT ? valid_rows + extra : valid_rows) * p.ldc * 4));
+      uint32_t voff[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wn * 128 + j * 32 + lr;
+        voff[j] = n < N ? (uint32_t)((4 * kh * p.ldc + n) * 4) : kOob;
+      }
+      auto store_rows = [&](const bool check) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i >= act) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rb = a_row(i) + 8 * (r >> 2) + (r & 3);
+            const uint32_t soff = (uint32_t)(rb * p.ldc * 4);
+            const bool ok = !check || rb + 4 * kh < valid_rows;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float v = acc[i][j][r];  // a scalar first (see the pieces' stores)
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsY,
+                                                    ok ? voff[j] : kOob, soff, 0);
+            }
+          }
+        }
+      };
+      if (valid_rows >= BM)
+        store_rows(false);
+      else
+        store_rows(true);
+      if constexpr (XRT) {  // folded rows: column blocks 2 wm, 2 wm + 1 of this wave's half
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t vo = wm ? voff[xblock<GATE_UP>(1, h)] : voff[xblock<GATE_UP>(0, h)];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rb = BM + 8 * (r >> 2) + (r & 3);
+            const float v = xr->acc[h][r];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsY,
+                                                  rb + 4 * kh < BM + extra ? vo : kOob,
+                                                  (uint32_t)(rb * p.ldc * 4), 0);
+          }
+        }
+      }
+    }
+  };
+  if constexpr (!KMAJ) {
+    if (extra > 0) {  // a full tile with folded rows (see tile_rows); this lane's is row 256 + lane % 32
+      ExtraRows xr;
+      xr.rs = rsA;
+      xr.K = K;
+      if (GATE_UP) {
+        const int t = lr < extra ? p.row_token[row0 + BM + lr] : -1;
+        xr.off = t >= 0 ? (uint32_t)t * (uint32_t)(p.lda * 2) : kOob;
+      } else {
+        xr.off = lr < extra ? (uint32_t)(BM + lr) * (uint32_t)(p.lda * 2) : kOob;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xr.acc[h][r] = 0.f;
+      // one copy of the loop per wave row (a wave-uniform branch)
+      if (wm == 0)
+        k_loop<GATE_UP, 4, FP8, decltype(issue_a), decltype(issue_b), false, false, false, 8, true, 0>(
+            lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc, &xr);
+      else
+        k_loop<GATE_UP, 4, FP8, decltype(issue_a), decltype(issue_b), false, false, false, 8, true, 1>(
+            lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc, &xr);
+      finish(std::true_type{}, &xr);
+      return;
+    }
+  }
 #define MOE_KL(A_, N_)                                                                            \
   k_loop<GATE_UP, A_, FP8, decltype(issue_a), decltype(issue_b), KMAJ, false, false, N_>(         \
       lds, s0, s1 - s0, wm, wn, il, lane, issue_a, issue_b, acc)
@@ -546,142 +985,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     default: MOE_KL(0, 2); break;
   }
 #undef MOE_KL
-  auto a_row = [&](int i) { return a_row_of(wm, i, il); };
-
-  // E4M3: every output column times the scale of its weight row
-  if constexpr (FP8) {
-    const float* Sg = shared ? p.S_shared : p.S_routed + (int64_t)g * brows;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int wr = b_weight_row(b_row_of<GATE_UP>(wn, j) + lr);
-      const float sc = wr >= 0 ? Sg[wr] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i >= act) continue;
-        acc[i][j] *= sc;
-      }
-    }
-  }
-
-  // ------------------------------------------------ pieces of a split tile
-  if (piece) {  // row-major fp32 partial tile, columns in LDS B-row order
-    // one per-lane base offset; every store adds a compile-time byte offset,
-    // so the 256 stores need no address registers
-    const __amdgpu_buffer_rsrc_t rsP = make_rsrc(
-        p.partial + (int64_t)(piece_tile * S + part) * (BM * BN), BM * BN * 4);
-    const uint32_t vbase = (uint32_t)(((a_row(0) + 4 * kh) * BN + b_row_of<GATE_UP>(wn, 0) + lr) * 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= act) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int off = ((a_row(i) - a_row(0) + 8 * (r >> 2) + (r & 3)) * BN +
-                           (b_row_of<GATE_UP>(0, j) - b_row_of<GATE_UP>(0, 0))) * 4;
-          const float v = acc[i][j][r];  // a scalar first: bit_cast of a vector element
-                                         // reinterprets the vector's first lane
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsP, vbase, off, 0);
-        }
-    }
-    return;
-  }
-
-  // -------------------------------------------------------------- epilogue
-  if (GATE_UP && p.gu_out) {  // keep g and u (bf16) of the valid rows for the backward pass
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= act) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
-        if (row >= valid_rows) continue;
-        bf16_t* gr = reinterpret_cast<bf16_t*>(p.gu_out) + (row0 + row) * p.ld_gu;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int f = n0 + wn * 64 + j * 32 + lr;
-          if (f < N) {
-            gr[f] = f32_to_bf16(acc[i][j][r]);
-            gr[N + f] = f32_to_bf16(acc[i][j + 2][r]);
-          }
-        }
-      }
-    }
-  }
-  if (GATE_UP) {
-    // SwiGLU in registers, h stored from registers as bf16 pairs (measured
-    // 1.5-2% faster for the whole gate/up kernel than staging the fp32 tile
-    // through LDS for 16-byte stores).  Register r of lane l holds row
-    // 8 (r / 4) + 4 kh + r % 4, column l % 32 of its 32 x 32 block; for the
-    // register pair (2q, 2q + 1) (rows R, R + 1) the even lane stores row R,
-    // columns c, c + 1 and the odd lane row R + 1, columns c - 1, c, after
-    // swapping one value (DPP quad permutation 1 0 3 2).  Rows past the tile's
-    // count (padding, or the next m-tile's) are not stored.
-    const __amdgpu_buffer_rsrc_t rsH = make_rsrc(reinterpret_cast<bf16_t*>(p.C) + row0 * p.ldc,
-                                                (uint32_t)(BM * p.ldc * 2));
-    const bool odd = lane & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= act) continue;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int r = 2 * q + (odd ? 1 : 0);
-        const int row = a_row(i) + 8 * (r >> 2) + 4 * kh + (r & 3);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float h0 = silu(acc[i][j][2 * q]) * acc[i][j + 2][2 * q];
-          const float h1 = silu(acc[i][j][2 * q + 1]) * acc[i][j + 2][2 * q + 1];
-          const float send = odd ? h0 : h1;
-          const float got = __builtin_bit_cast(
-              float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
-          const float lo = odd ? got : h0, hi = odd ? h1 : got;
-          const int col = n0 + wn * 64 + j * 32 + (lr & ~1);
-          const uint32_t v = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-          const uint32_t off = (row < valid_rows && col < N) ? (uint32_t)((row * p.ldc + col) * 2) : kOob;
-          __builtin_amdgcn_raw_buffer_store_b32(v, rsH, off, 0, 0);
-        }
-      }
-    }
-    return;
-  }
-  // fp32 rows of the tile through buffer stores: the row of register r is
-  // wave-uniform and goes in the scalar offset, the lane's column (and its
-  // 4-row half) in the vector offset, so no store needs a 64-bit address.
-  // The scalar offset is outside the hardware's range check, so a tile with
-  // rows past its count (the group's last) drops those rows through the
-  // vector offset; full tiles take the same loop with the check folded away.
-  {
-    const __amdgpu_buffer_rsrc_t rsY = make_rsrc(reinterpret_cast<float*>(p.C) + row0 * p.ldc,
-                                                (uint32_t)((int64_t)valid_rows * p.ldc * 4));
-    uint32_t voff[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 128 + j * 32 + lr;
-      voff[j] = n < N ? (uint32_t)((4 * kh * p.ldc + n) * 4) : kOob;
-    }
-    auto store_rows = [&](const bool check) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i >= act) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rb = a_row(i) + 8 * (r >> 2) + (r & 3);
-          const uint32_t soff = (uint32_t)(rb * p.ldc * 4);
-          const bool ok = !check || rb + 4 * kh < valid_rows;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float v = acc[i][j][r];  // a scalar first (see the pieces' stores)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsY,
-                                                  ok ? voff[j] : kOob, soff, 0);
-          }
-        }
-      }
-    };
-    if (valid_rows >= BM)
-      store_rows(false);
-    else
-      store_rows(true);
-  }
+  finish(std::false_type{}, nullptr);
 }
 
 template <bool FP8>
@@ -709,33 +1013,36 @@ __global__ __launch_bounds__(256) void moe_gemm_rows_kmajor_prefill_kernel(Group
 // (gate/up: SwiGLU into H; down: rows of Yp).  All S loads of an output are
 // issued before the sum, so the kernel streams instead of waiting on each.
 constexpr int kFixRows = 16;
-constexpr int kFixBlocksPerTile = BM / kFixRows;
+constexpr int kFixBlocksPerTile = kTileRows / kFixRows;
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p) {
-  const Split sp = split_of(p);
+template <bool GATE_UP, bool FOLD>
+__device__ __forceinline__ void fixup_tiles(const GroupedGemm& p) {
+  const int64_t mt = mtiles_of<FOLD>(p);
+  const Split sp = split_of(p, mt);
   const int64_t t = blockIdx.x / kFixBlocksPerTile;
   if (t >= sp.R) return;
   int64_t m_tile, n_tile;
-  tile_coords(p, sp.n_dp + t, m_tile, n_tile);
-  const int g = p.tile_group[m_tile];
+  RunGroup rg;
+  tile_coords<FOLD>(p, mt, sp.n_dp + t, m_tile, n_tile, rg);
+  const int g = rg.g;
   const int N = g >= p.E ? p.N_shared : p.N_routed;
   constexpr int NB = GATE_UP ? BN / 2 : BN;  // output columns of a tile
   const int n0 = (int)n_tile * NB;
   if (n0 >= N) return;
   int64_t row0;
-  int valid_rows;
-  tile_rows(p, m_tile, g, row0, valid_rows);
+  int valid_rows, extra;
+  tile_rows<FOLD>(p, rg, m_tile - rg.first, row0, valid_rows, extra);
   const int r0 = (blockIdx.x % kFixBlocksPerTile) * kFixRows;
-  const int r1 = min(r0 + kFixRows, valid_rows);
-  const float* P = p.partial + t * sp.S * (BM * BN);
+  const int r1 = min(r0 + kFixRows, valid_rows + extra);  // folded rows included
+  const float* P = p.partial + t * sp.S * (kTileRows * BN);
   constexpr int Q = NB / 4;  // float4 outputs per row
   // sum of the S partials of the float4 at (row, col), in piece order
   auto sum4 = [&](int row, int col) {
     float4 v[kMaxSplit];
 #pragma unroll
     for (int q = 0; q < kMaxSplit; ++q)
-      if (q < sp.S) v[q] = *reinterpret_cast<const float4*>(P + (int64_t)q * (BM * BN) + row * BN + col);
+      if (q < sp.S)
+        v[q] = *reinterpret_cast<const float4*>(P + (int64_t)q * (kTileRows * BN) + row * BN + col);
     float4 a = v[0];
 #pragma unroll
     for (int q = 1; q < kMaxSplit; ++q)
@@ -776,6 +1083,14 @@ __global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p
         if (n0 + c + u < N) Y[u] = y[u];
     }
   }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p) {
+  if (p.b_kmajor)
+    fixup_tiles<GATE_UP, false>(p);  // the K-major kernel's m-tiles do not fold
+  else
+    fixup_tiles<GATE_UP, true>(p);
 }
 
 template <bool FP8>

@@ -20,7 +20,9 @@ inline int router_parts(int64_t /*D*/) { return kRouterGroups; }
 // Workgroups the prefill GEMMs balance their last round over (one per CU,
 // at most this many), and so the number of partial tiles the workspace holds.
 constexpr int kSplitCtas = 256;
-constexpr int64_t kPartialTileFloats = 256 * 256;
+// A partial tile: up to 256 + 32 rows (a 256-row tile with the next m-tile's
+// few rows folded in) x 256 columns.
+constexpr int64_t kPartialTileFloats = (256 + 32) * 256;
 
 // Row-tile height of the grouped GEMMs and the per-call workspace layout.
 struct Plan {

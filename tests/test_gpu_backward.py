@@ -145,6 +145,7 @@ TRAIN_CASES = [
     (1500, 320, 8, 2, 200, 0, True),     # 256-row tiles, ragged M, N and K, bias in the logits
     (700, 512, 16, 4, 256, 256, False),  # 256-row tiles with the shared expert
     (4096, 512, 8, 2, 384, 0, False),    # 256-row tiles, more tiles than run at once
+    (270, 256, 2, 2, 320, 64, False),    # every group 270 rows: 14 folded into the first tile
 ]
 
 
@@ -206,6 +207,9 @@ def test_backward_saved_twice_is_deterministic():
 
 @pytest.mark.parametrize("counts,D,F", [
     ([257, 300, 511, 512, 256, 1, 0, 700], 256, 320),  # 256-row tiles
+    # 256-row tiles whose groups' last few rows fold into the tile before (270,
+    # 288, 513, 1030 rows; the shared expert's 2456 = 9 * 256 + 152 do not)
+    ([270, 288, 289, 513, 1030, 0, 40, 26], 136, 200),
     ([16, 17, 1, 0, 15, 32, 8, 3], 256, 320),          # 16-row tiles
     ([33, 32, 64, 1, 0, 40, 31, 47], 256, 320),        # 32-row tiles
     # T = 64: the one-stage weight gradients, 576 tiles over 256 workgroups, with

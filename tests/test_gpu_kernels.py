@@ -473,6 +473,16 @@ def test_layer_fp8_shard_and_routed():
     assert rel <= Y_TOL
 
 
+def _run_mtiles(counts):
+    """256-row m-tiles that run: a group of two or more m-tiles whose last one
+    would hold at most 32 rows folds them into the m-tile before it."""
+    n = 0
+    for c in counts:
+        mg = (int(c) + 255) // 256
+        n += mg - (1 if mg >= 2 and c - (mg - 1) * 256 <= 32 else 0)
+    return n
+
+
 def _split(V, ctas, kmin):
     """(R, S) of the prefill GEMMs' last-round split: R tiles cut in S pieces."""
     if V % ctas == 0 or V >= 4 * ctas:
@@ -508,7 +518,7 @@ def test_layer_split_last_round(T, D, E, k, F, Fs):
     torch.cuda.synchronize()
     assert np.array_equal(y1, y2.cpu().numpy())
     counts = np.bincount(ids.ravel(), minlength=E)
-    mt = int(sum((c + 255) // 256 for c in counts)) + ((T + 255) // 256 if Fs else 0)
+    mt = _run_mtiles(list(counts) + ([T] if Fs else []))
     ctas = min(256, torch.cuda.get_device_properties(0).multi_processor_count)
     fmax = max(F, Fs)
     _, s_gu = _split(mt * ((fmax + 127) // 128), ctas, D)
@@ -637,29 +647,110 @@ def test_errors_are_raised_before_launch():
     assert ei.value.code in (moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED)
 
 
-@pytest.mark.parametrize("counts", [
-    [257, 300, 511, 512, 256, 1, 0, 700],
+# Group sizes whose last 256-row m-tile would hold at most 32 rows fold those
+# rows into the m-tile before it: 270 and 288 (two m-tiles, 14 and 32 rows
+# folded), 513, 1030 and 1056 (three to five m-tiles, 1, 6 and 32 folded);
+# 289 and 650 do not fold (33 and 138 rows left), 20 is one tile.  Their sum,
+# 4116 = 16 * 256 + 20, makes the shared expert's last 20 rows fold too.
+FOLDED = [270, 288, 289, 513, 1030, 1056, 650, 20]
+
+
+@pytest.mark.parametrize("counts,D,F,fp8", [
+    ([257, 300, 511, 512, 256, 1, 0, 700], 256, 320, False),
     # one-tile groups at the row tiers' edges (64-row steps pick the A loads per
     # stage) and at 32-row sub-tile edges
-    [64, 65, 192, 193, 33, 32, 128, 129],
+    ([64, 65, 192, 193, 33, 32, 128, 129], 256, 320, False),
+    # folded rows, with K and N tails in both GEMMs (136 = 2 * 64 + 8, 200 = 3 * 64 + 8)
+    (FOLDED, 136, 200, False),
+    (FOLDED, 256, 320, False),
+    (FOLDED, 256, 320, True),
 ])
-def test_forward_routed_tile_boundaries(counts):
+def test_forward_routed_tile_boundaries(counts, D, F, fp8):
     """256-row tiles at group sizes around tile boundaries (k = 1, so the counts are
-    exact): 257, 300, 511 and 700 rows (two- and three-m-tile groups, the two-tile ones
-    split evenly), 512 and 256 (full tiles), 1 row and an empty expert; one-tile groups
-    on both sides of 32, 64, 128 and 192 rows; tokens in shuffled order so every tile
-    gathers scattered rows."""
-    T, D, F = sum(counts), 256, 320
-    assert moe.moe_block_m(moe.make_shape(T, D, len(counts), F, 1)) == 256
-    s = W.Shape(T=T, D=D, E=len(counts), k=1, F=F, Fs=64)
+    exact): 257, 300, 511 and 700 rows (two- and three-m-tile groups; 257 folds its
+    last row into the first m-tile, the other two-tile ones split evenly), 512 and 256
+    (full tiles), 1 row and an empty expert; one-tile groups on both sides of 32, 64,
+    128 and 192 rows; the folded-row sizes above, with bf16 and E4M3 weights; tokens
+    in shuffled order so every tile gathers scattered rows."""
+    T = sum(counts)
+    assert moe.moe_block_m(moe.make_shape(T, D, len(counts), F, 1, weight_format=int(fp8))) == 256
+    s = W.Shape(T=T, D=D, E=len(counts), k=1, F=F, Fs=64, fp8=fp8)
     inp = W.make_inputs(s, seed=11)
     order = np.random.default_rng(5).permutation(T)
     ids = np.repeat(np.arange(len(counts)), counts)[order].astype(np.int32).reshape(T, 1)
     p = np.ones((T, 1), np.float32)
     g = _gpu(inp)
     y = moe.moe_forward_routed(g.x, g.w_gate_up, g.w_down, torch.from_numpy(ids).to(DEV),
-                               torch.from_numpy(p).to(DEV), g.ws_gate_up, g.ws_down)
+                               torch.from_numpy(p).to(DEV), g.ws_gate_up, g.ws_down,
+                               scales=_scales(g))
     torch.cuda.synchronize()
     y_ref = oracle.experts(inp, ids, p.astype(np.float64))
     rel, _, _ = y_error(y.cpu().numpy(), y_ref)
+    print("counts %s D=%d F=%d fp8=%s: max|err|/RMS=%.4g" % (counts, D, F, fp8, rel))
+    assert rel <= Y_TOL
+
+
+def test_folded_rows_are_bitwise_the_rows_of_a_tile():
+    """A row's arithmetic does not depend on which tile computes it: with 1030
+    and 270 rows (6 and 14 rows folded into the tile before, computed by the
+    written-out MFMAs) every token's y is bitwise the y of a call that holds
+    only the unfolded tokens (groups of 1024 and 256 rows, no folding) or the
+    folded ones with 100 others of each expert (one-tile groups of 106 and 114
+    rows, still 256-row tiles: T k > 48 E)."""
+    counts = [1030, 270]
+    T, D, F = sum(counts), 256, 320
+    s = W.Shape(T=T, D=D, E=2, k=1, F=F, Fs=0)
+    inp = W.make_inputs(s, seed=21)
+    ids = np.repeat(np.arange(2), counts).astype(np.int32).reshape(T, 1)
+    p = np.ones((T, 1), np.float32)
+    g = _gpu(inp)
+
+    def run(tok):
+        return moe.moe_forward_routed(g.x[tok].contiguous(), g.w_gate_up, g.w_down,
+                                      torch.from_numpy(ids[tok]).to(DEV),
+                                      torch.from_numpy(p[tok]).to(DEV))
+
+    y = run(np.arange(T))
+    keep = np.r_[0:1024, 1030:1030 + 256]       # rows of the 256-row tiles
+    folded = np.r_[1024:1030, 1030 + 256:T]     # the folded rows
+    mixed = np.r_[0:100, 1024:1030, 1030:1130, 1030 + 256:T]
+    assert moe.moe_block_m(moe.make_shape(mixed.size, D, 2, F, 1)) == 256
+    y_keep, y_mixed = run(keep), run(mixed)
+    torch.cuda.synchronize()
+    assert torch.equal(y[keep], y_keep)
+    assert torch.equal(y[folded], y_mixed[torch.from_numpy(np.isin(mixed, folded)).to(DEV)])
+    y_ref = oracle.experts(inp, ids, p.astype(np.float64))
+    rel, _, _ = y_error(y.cpu().numpy(), y_ref)
+    assert rel <= Y_TOL
+
+
+def test_folded_rows_in_split_tiles():
+    """Folded rows in tiles cut along K (a short last round: every tile is cut
+    into two pieces here, K = 520 is nine stages): parity, and bitwise the same
+    y from a workspace full of NaN bytes."""
+    counts = [270, 1030, 20, 513]
+    T, D, F = sum(counts), 520, 520
+    s = W.Shape(T=T, D=D, E=len(counts), k=1, F=F, Fs=0)
+    inp = W.make_inputs(s, seed=23)
+    order = np.random.default_rng(7).permutation(T)
+    ids = np.repeat(np.arange(len(counts)), counts)[order].astype(np.int32).reshape(T, 1)
+    p = np.ones((T, 1), np.float32)
+    g = _gpu(inp)
+    ctas = min(256, torch.cuda.get_device_properties(0).multi_processor_count)
+    mt = _run_mtiles(counts)
+    assert _split(mt * ((F + 127) // 128), ctas, D)[1] >= 2
+    assert _split(mt * ((D + 255) // 256), ctas, F)[1] >= 2
+    shape = moe.make_shape(T, D, len(counts), F, 1)
+    outs = []
+    for fill in (None, 0xFF):
+        ws = moe.alloc_workspace(shape, DEV)
+        if fill is not None:
+            ws.view(torch.uint8).fill_(fill)
+        outs.append(moe.moe_forward_routed(g.x, g.w_gate_up, g.w_down, torch.from_numpy(ids).to(DEV),
+                                           torch.from_numpy(p).to(DEV), workspace=ws))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    y_ref = oracle.experts(inp, ids, p.astype(np.float64))
+    rel, _, _ = y_error(outs[0].cpu().numpy(), y_ref)
+    print("folded rows in split tiles: max|err|/RMS=%.4g" % rel)
     assert rel <= Y_TOL
