@@ -583,13 +583,19 @@ __device__ __forceinline__ void tile_rows(const GroupedGemm& p, const RunGroup& 
   valid = max(0, min(q, cnt - (int)(j * q)));
 }
 
-template <bool GATE_UP, bool FP8, bool KMAJ = false>
+// KT: K may end inside a K-stage (K % 64 != 0), so loads of the last stage
+// mask the chunks past K; with KT false the K loop carries no such selects.
+// FOLD (see tile_rows): bf16 row-major weights only; the E4M3 kernels keep
+// their registers for widening the codes (the folded rows' fragments and
+// accumulators made them spill in the K loop).
+template <bool GATE_UP, bool FP8, bool KMAJ = false, bool KT = true>
 __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
+  constexpr bool FOLD = !KMAJ && !FP8;
   // The V - R whole tiles are cut into 8 equal runs, one per XCD: the
   // hardware deals workgroup b to XCD b % 8, so XCD x executes run x in
   // order and the workgroups an XCD runs together share A and B tiles in its
   // L2.  The R*S pieces come after all of them.
-  const int64_t mt = mtiles_of<!KMAJ>(p);
+  const int64_t mt = mtiles_of<FOLD>(p);
   const Split sp = split_of(p, mt);
   const int64_t run = (sp.n_dp + 7) / 8;
   const int64_t b = blockIdx.x;
@@ -609,7 +615,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   const int S = sp.S;
   int64_t m_tile, n_tile;
   RunGroup rg;
-  tile_coords<!KMAJ>(p, mt, L, m_tile, n_tile, rg);
+  tile_coords<FOLD>(p, mt, L, m_tile, n_tile, rg);
   const int g = rg.g;
   const bool shared = g >= p.E;
   const int N = shared ? p.N_shared : p.N_routed;
@@ -620,7 +626,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   int64_t row0;
   int valid_rows;
   int extra;  // folded rows 256 .. 256 + extra - 1 (see tile_rows)
-  tile_rows<!KMAJ>(p, rg, m_tile - rg.first, row0, valid_rows, extra);
+  tile_rows<FOLD>(p, rg, m_tile - rg.first, row0, valid_rows, extra);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -694,7 +700,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
     const int k0 = stage * BK;
     const bool b8 = FP8 && isB;
     char* base = isB ? lds + 2 * kABytes + buf * b_stage_bytes<FP8>() : lds + buf * kABytes;
-    const bool tail = k0 + BK > K;
+    const bool tail = KT && k0 + BK > K;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < j0 || j >= j1) continue;
@@ -945,7 +951,7 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
       }
     }
   };
-  if constexpr (!KMAJ) {
+  if constexpr (FOLD) {
     if (extra > 0) {  // a full tile with folded rows (see tile_rows); this lane's is row 256 + lane % 32
       ExtraRows xr;
       xr.rs = rsA;
@@ -988,16 +994,16 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   finish(std::false_type{}, nullptr);
 }
 
-template <bool FP8>
+template <bool FP8, bool KT>
 __global__ __launch_bounds__(256) void moe_gemm_gate_up_prefill_kernel(GroupedGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  prefill_tile<true, FP8>(p, lds);
+  prefill_tile<true, FP8, false, KT>(p, lds);
 }
 
-template <bool FP8>
+template <bool FP8, bool KT>
 __global__ __launch_bounds__(256) void moe_gemm_down_prefill_kernel(GroupedGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  prefill_tile<false, FP8>(p, lds);
+  prefill_tile<false, FP8, false, KT>(p, lds);
 }
 
 // rows x weight with the weight stored K-major ([K][N] per group): the
@@ -1087,21 +1093,21 @@ __device__ __forceinline__ void fixup_tiles(const GroupedGemm& p) {
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void moe_gemm_split_fixup_kernel(GroupedGemm p) {
-  if (p.b_kmajor)
-    fixup_tiles<GATE_UP, false>(p);  // the K-major kernel's m-tiles do not fold
+  if (p.b_kmajor || p.fp8)
+    fixup_tiles<GATE_UP, false>(p);  // the K-major and E4M3 kernels' m-tiles do not fold
   else
     fixup_tiles<GATE_UP, true>(p);
 }
 
-template <bool FP8>
+template <bool FP8, bool KT>
 hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
   constexpr int lds = lds_bytes<FP8>();
   // set once per process (a function-local static is initialised thread-safely)
   static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8>,
+    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8, KT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel<FP8>,
+      e = hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel<FP8, KT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e == hipSuccess && !FP8)
       e = hipFuncSetAttribute((const void*)moe_gemm_rows_kmajor_prefill_kernel,
@@ -1125,14 +1131,14 @@ hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
   const int64_t blocks = (g.max_tiles * g.n_tiles_n + 7) / 8 * 8 + (g.ctas > 0 ? g.ctas : 0);
   if (blocks == 0) return hipSuccess;
   if (gate_up)
-    hipLaunchKernelGGL(moe_gemm_gate_up_prefill_kernel<FP8>, dim3((unsigned)blocks), dim3(256), lds,
-                       s, g);
+    hipLaunchKernelGGL((moe_gemm_gate_up_prefill_kernel<FP8, KT>), dim3((unsigned)blocks), dim3(256),
+                       lds, s, g);
   else if (g.b_kmajor)
     hipLaunchKernelGGL(moe_gemm_rows_kmajor_prefill_kernel, dim3((unsigned)blocks), dim3(256), lds,
                        s, g);
   else
-    hipLaunchKernelGGL(moe_gemm_down_prefill_kernel<FP8>, dim3((unsigned)blocks), dim3(256), lds, s,
-                       g);
+    hipLaunchKernelGGL((moe_gemm_down_prefill_kernel<FP8, KT>), dim3((unsigned)blocks), dim3(256), lds,
+                       s, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.ctas <= 0) return e;
   const unsigned fix_blocks = (unsigned)g.ctas * kFixBlocksPerTile;
@@ -1145,7 +1151,11 @@ hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
 
 hipError_t launch(bool gate_up, const GroupedGemm& g, hipStream_t s) {
   if (g.b_kmajor && (gate_up || g.fp8)) return hipErrorInvalidValue;  // no such variant
-  return g.fp8 ? launch_fmt<true>(gate_up, g, s) : launch_fmt<false>(gate_up, g, s);
+  // a K of some group that ends inside a 64-wide K-stage needs the masked loads
+  const bool kt = g.K_routed % BK != 0 || (g.B_shared && g.K_shared % BK != 0);
+  if (g.fp8)
+    return kt ? launch_fmt<true, true>(gate_up, g, s) : launch_fmt<true, false>(gate_up, g, s);
+  return kt ? launch_fmt<false, true>(gate_up, g, s) : launch_fmt<false, false>(gate_up, g, s);
 }
 
 // One tile of a weight gradient: its group, corner and row count.
