@@ -117,6 +117,41 @@ def _cpu_baseline(inp, target_s, y_gpu, ids_gpu):
     return base, parity
 
 
+def _dense_context(torch, s, dev, reps=20):
+    """Context, not this path: the vendor library's dense bf16 GEMM (hipBLASLt
+    through torch's linear) on one matrix of the expert GEMMs' sizes each
+    (all T*k rows against one [2F, D] and one [D, F] weight), timed with
+    events on torch's stream.  It shows what a tuned library reaches on the
+    same box and clock under the same power limit."""
+    M = s.T * s.k
+    gen = torch.Generator(device=dev).manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    res = {}
+    for name, K, N in (("gate_up", s.D, 2 * s.F), ("down", s.F, s.D)):
+        a, w = rnd(M, K), rnd(N, K)
+        for _ in range(3):
+            torch.nn.functional.linear(a, w)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            torch.nn.functional.linear(a, w)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
+        res[name] = {"m_n_k": [M, N, K], "ms": round(ms, 4), "tflops": round(tf, 1),
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del a, w
+    torch.cuda.empty_cache()
+    res["what"] = ("hipBLASLt dense bf16 GEMM via torch.nn.functional.linear, same FLOPs as each "
+                   "expert GEMM as one dense product; context only, not part of the timed path")
+    return res
+
+
 def _bench_backward(args, s, wl, g, moe, torch, W, dev):
     """Backward pass timing: gradients of sum <dy, y> for the routing of one
     forward call, on the same inputs; dy ~ N(0, 1) fp32.  --saved: that call is
@@ -421,6 +456,8 @@ def main():
                          "call instead of the forward pass")
     ap.add_argument("--saved", action="store_true",
                     help="with --backward: take the routing and g | u from moe_forward_train")
+    ap.add_argument("--no-dense-context", action="store_true",
+                    help="skip the library dense-GEMM context figures of a prefill workload")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="run one plain device copy of this many GiB first (a known-size kernel "
                          "for calibrating rocprofv3 byte counters)")
@@ -518,6 +555,13 @@ def main():
         out["parity"] = parity
     else:
         out["cpu_baseline"] = None
+    if (not args.no_dense_context and args.ep == 1 and not args.fp8 and not args.graph
+            and out["config"]["T"] * out["config"]["k"] >= 1024):
+        _log("timing the library dense GEMMs (context)")
+        out["context_dense_gemm"] = _dense_context(torch, W.WORKLOADS[args.workload].shape
+                                                   if args.T is None else
+                                                   W.WORKLOADS[args.workload].shape.with_T(args.T),
+                                                   dev)
     print(json.dumps(out), flush=True)
 
 
