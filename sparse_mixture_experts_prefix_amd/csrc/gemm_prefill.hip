@@ -548,6 +548,13 @@ __device__ __forceinline__ RunGroup group_of_mtile(const GroupedGemm& p, int64_t
 // m-tiles x the column's n-tiles, m-tile fastest.  Consecutive tiles (the
 // workgroups an XCD runs together) then share their A and B tiles, and a
 // block never straddles two experts' weights.
+// A block that holds its group's folded m-tile (see tile_rows), whose tiles
+// take longer than the others, lists that m-tile's tiles first (n fastest):
+// workgroups are handed out in order to the CUs that free up first, so the
+// heavy tiles of the next block go to CUs that just ran light ones.  In the
+// m-tile order the CUs that finished a heavy tile last also took the next
+// block's heavy tiles, and with two rounds of tiles (the down GEMM at the
+// Mixtral shape) those CUs set the kernel's end.
 template <bool FOLD>
 __device__ __forceinline__ void tile_coords(const GroupedGemm& p, int64_t mt, int64_t L,
                                             int64_t& m_tile, int64_t& n_tile, RunGroup& rg) {
@@ -560,6 +567,18 @@ __device__ __forceinline__ void tile_coords(const GroupedGemm& p, int64_t mt, in
   const int64_t mb = v / (MS * cw);                               // block of the group
   const int64_t mh = min((int64_t)MS, rg.mg - mb * MS);           // its m-tiles
   const int64_t inner = v - mb * MS * cw;
+  if (FOLD && mh > 1 && mb * MS + mh == rg.mg && rg.mg < (rg.cnt + BM - 1) / BM) {
+    // the block's last m-tile holds the folded rows
+    if (inner < cw) {
+      m_tile = rg.first + mb * MS + mh - 1;
+      n_tile = sn * NS + inner;
+    } else {
+      const int64_t j = inner - cw;
+      m_tile = rg.first + mb * MS + j % (mh - 1);
+      n_tile = sn * NS + j / (mh - 1);
+    }
+    return;
+  }
   m_tile = rg.first + mb * MS + inner % mh;
   n_tile = sn * NS + inner / mh;
 }
