@@ -121,6 +121,11 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
   gu.group_count = counts;
   gu.group_padded = padded;
   gu.a_bytes = P.T * P.D * 2;
+  // expert groups of at most one m-tile and its folded rows on average: each
+  // weight tile is read by one workgroup (measured on the DeepSeek shape:
+  // gate/up 3.96 -> 3.82 ms; with four m-tiles per group, Mixtral shape,
+  // the plain policy is 2.5% faster, and the down GEMM is too)
+  gu.stream_b = P.A <= (int64_t)(P.BM + 32) * P.E;
   gu.ctas = ctas;
   gu.partial = prefill ? at<float>(ws, P.off_partial) : nullptr;
   gu.gu_out = gu_save;
@@ -131,6 +136,7 @@ int run_experts(const moe::Plan& P, const moe_weights* w, const int32_t* ids, co
 
   GroupedGemm dn = gu;
   dn.gu_out = nullptr;
+  dn.stream_b = 0;
   dn.A = H;
   dn.row_token = nullptr;
   dn.lda = P.ldh;

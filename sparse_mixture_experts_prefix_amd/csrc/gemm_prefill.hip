@@ -607,7 +607,10 @@ __device__ __forceinline__ void tile_rows(const GroupedGemm& p, const RunGroup& 
 // FOLD (see tile_rows): bf16 row-major weights only; the E4M3 kernels keep
 // their registers for widening the codes (the folded rows' fragments and
 // accumulators made them spill in the K loop).
-template <bool GATE_UP, bool FP8, bool KMAJ = false, bool KT = true>
+// NTB: the weight loads take the non-temporal cache policy, for launches
+// whose expert groups are about one m-tile each (every weight tile is then
+// read by one workgroup, and keeping it in L2 only evicts the shared rows).
+template <bool GATE_UP, bool FP8, bool KMAJ = false, bool KT = true, bool NTB = false>
 __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   constexpr bool FOLD = !KMAJ && !FP8;
   // The V - R whole tiles are cut into 8 equal runs, one per XCD: the
@@ -742,6 +745,9 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
                                 : (uint32_t)(k0 * 2);
       if constexpr (KMAJ)
         lds_dma16(isB ? rsB : rsA, base + blk * 1024, o, soff);
+      else if (NTB && isB)  // cache policy 2: non-temporal
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(base + blk * 1024), 16, o,
+                                                 (int)soff, 0, 2);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(isB ? rsB : rsA, (lds_void*)(base + blk * 1024), 16,
                                                  o, (int)soff, 0, 0);
@@ -1013,10 +1019,10 @@ __device__ __forceinline__ void prefill_tile(const GroupedGemm& p, char* lds) {
   finish(std::false_type{}, nullptr);
 }
 
-template <bool FP8, bool KT>
+template <bool FP8, bool KT, bool NTB>
 __global__ __launch_bounds__(256) void moe_gemm_gate_up_prefill_kernel(GroupedGemm p) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  prefill_tile<true, FP8, false, KT>(p, lds);
+  prefill_tile<true, FP8, false, KT, NTB>(p, lds);
 }
 
 template <bool FP8, bool KT>
@@ -1123,8 +1129,11 @@ hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
   constexpr int lds = lds_bytes<FP8>();
   // set once per process (a function-local static is initialised thread-safely)
   static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8, KT>,
+    hipError_t e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8, KT, false>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)moe_gemm_gate_up_prefill_kernel<FP8, KT, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)moe_gemm_down_prefill_kernel<FP8, KT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1149,9 +1158,12 @@ hipError_t launch_fmt(bool gate_up, GroupedGemm g, hipStream_t s) {
   // round (at most ctas of them; see prefill_tile)
   const int64_t blocks = (g.max_tiles * g.n_tiles_n + 7) / 8 * 8 + (g.ctas > 0 ? g.ctas : 0);
   if (blocks == 0) return hipSuccess;
-  if (gate_up)
-    hipLaunchKernelGGL((moe_gemm_gate_up_prefill_kernel<FP8, KT>), dim3((unsigned)blocks), dim3(256),
-                       lds, s, g);
+  if (gate_up && g.stream_b)
+    hipLaunchKernelGGL((moe_gemm_gate_up_prefill_kernel<FP8, KT, true>), dim3((unsigned)blocks),
+                       dim3(256), lds, s, g);
+  else if (gate_up)
+    hipLaunchKernelGGL((moe_gemm_gate_up_prefill_kernel<FP8, KT, false>), dim3((unsigned)blocks),
+                       dim3(256), lds, s, g);
   else if (g.b_kmajor)
     hipLaunchKernelGGL(moe_gemm_rows_kmajor_prefill_kernel, dim3((unsigned)blocks), dim3(256), lds,
                        s, g);

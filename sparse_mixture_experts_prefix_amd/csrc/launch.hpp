@@ -64,6 +64,7 @@ struct GroupedGemm {
   const int32_t* group_count;   // rows of each group
   const int32_t* group_padded;  // first padded row of each group
   int64_t a_bytes;              // bytes addressable through A (gate/up: all of x)
+  int stream_b;                 // prefill gate/up: weight loads non-temporal (groups of ~1 m-tile)
   int64_t n_tiles_n;            // set by the launcher
   // Prefill only: workgroups that run at once (0: never split a tile over K)
   // and room for that many fp32 partial tiles of BM x BN (row-major)
